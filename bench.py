@@ -1,0 +1,204 @@
+"""Benchmark of the MoE layer forward on one MI355X.
+
+A step is one whole layer forward (router GEMM, scoring + top-K, sort by
+expert, grouped gate/up + SwiGLU, grouped down, unpermute-reduce and blends)
+over one batch of seeded synthetic tokens, with every input resident in HBM.
+Prints one JSON line.  The default workload is the decode layer (4 tokens,
+H 2048, 128 experts, top-8, I 768); --workload picks another.
+
+The dominant kernel (the routed gate/up grouped GEMM) is timed with HIP events
+recorded on the stream the library launches on, over the same kind of steps,
+and reported against the binding roofline.  The oracle (float64 numpy on the
+host cores) is timed on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}  # dense MFMA peaks
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="decode", choices=["tiny", "decode", "prefill_zipf", "fp8_sigmoid",
+                                                              "zero_experts"])
+    ap.add_argument("--layers", type=int, default=0,
+                    help="distinct weight copies cycled through (0: enough to exceed the 256 MB MALL)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle leg")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); every box here has a single MI355X "
+              f"and the multi-GPU expert-parallel path is design only.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_bias_amd as moe
+    import moe_inputs as mi
+    import moe_inputs.device as mid
+
+    wl = mi.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    N, H, E, R, K, I, Is = (wl.num_tokens, wl.hidden, wl.num_experts, wl.router_width, wl.top_k, wl.inter,
+                            wl.shared_inter)
+    fp8 = wl.weight_dtype == "fp8"
+    wbytes = 1 if fp8 else 2
+    layer_bytes = 3 * E * I * H * wbytes
+    n_layers = args.layers or max(1, min(8, int(np.ceil(1.0e9 / layer_bytes)) + 1))
+    if layer_bytes * n_layers > 150e9:
+        n_layers = max(1, int(150e9 // layer_bytes))
+
+    cfg = moe.make_config(N, H, E, R, K, I, Is, wl.scoring, wl.renormalize, wl.routed_scale, wl.weight_dtype)
+    layers = []
+    for l in range(n_layers):
+        dl = mid.device_layer(wl, layer=l, device="cuda:0")
+        w = moe.weights_from_stacked(dl.router, dl.bias, dl.gate, dl.up, dl.down, dl.gate_s, dl.up_s, dl.down_s,
+                                     dl.sh_gate, dl.sh_up, dl.sh_down, dl.sh_gate_s, dl.sh_up_s, dl.sh_down_s)
+        layers.append((dl, w))
+    ws = torch.empty(moe.moe_workspace_size(cfg), dtype=torch.uint8, device=dev)
+    out = torch.empty((N, H), dtype=torch.bfloat16, device=dev)
+    L = moe.moe_workspace_layout(cfg)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    def step(i):
+        dl, w = layers[i % n_layers]
+        moe.moe_forward(cfg, w, dl.x, out, ws, stream)
+
+    # ---- whole-layer timing
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+
+    # ---- realised routing per layer (for the algorithmic bytes / flops)
+    touched, rows_real = [], []
+    for l in range(n_layers):
+        step(l)
+        torch.cuda.synchronize()
+        counts = ws[L["counts"]:L["counts"] + 4 * R].view(torch.int32).cpu().numpy()
+        touched.append(int((counts[:E] > 0).sum()))
+        rows_real.append(int(counts[:E].sum()))
+    e_t = float(np.mean(touched))
+    p_r = float(np.mean(rows_real))
+
+    # ---- dominant kernel: the routed gate/up grouped GEMM, timed with events on the launch stream.
+    # The stage calls below reuse moe_forward's own intermediates in the workspace.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    a_off = L["xq"] if fp8 else None
+    for i in range(args.warmup + args.steps):
+        dl, w = layers[i % n_layers]
+        moe.moe_forward(cfg, w, dl.x, out, ws, stream)  # refreshes ids / offsets / quantised x for this batch
+        sid = ws.data_ptr() + L["sorted_ids"]
+        offs = L["offsets"] + ws.data_ptr()
+        a = dl.x if not fp8 else ws.data_ptr() + a_off
+        a_sc = None if not fp8 else ws.data_ptr() + L["x_scales"]
+        h = ws.data_ptr() + L["h"]
+        hs = None if not fp8 else ws.data_ptr() + L["h_scales"]
+        if i >= args.warmup:
+            ev[i - args.warmup][0].record(stream)
+        moe.moe_grouped_gemm(cfg, moe.MOE_STAGE_GATE_UP, moe.MOE_GROUP_ROUTED, w, a, a_sc, sid, offs, h, hs, ws,
+                             stream)
+        if i >= args.warmup:
+            ev[i - args.warmup][1].record(stream)
+    torch.cuda.synchronize()
+    k_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    # algorithmic bytes / flops of one gate/up launch
+    gu_weight_bytes = e_t * 2 * I * H * wbytes + (e_t * 2 * (I // 128) * (H // 128) * 4 if fp8 else 0)
+    gu_bytes = gu_weight_bytes + N * H * wbytes + p_r * I * wbytes
+    gu_flops = 4.0 * p_r * H * I
+    # whole layer
+    layer_flops = 2.0 * N * H * R + 6.0 * p_r * H * I + 6.0 * N * H * Is
+    layer_bytes_alg = (e_t * 3 * I * H * wbytes + R * H * 2 + 2 * N * H * 2 + 3 * Is * H * wbytes)
+    ai = gu_flops / gu_bytes
+    ridge = MFMA_PEAK_TFLOPS[wl.weight_dtype] * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if ai < ridge:
+        roof = {"bound": "hbm", "achieved": gu_bytes / (k_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": gu_flops / (k_ms * 1e-3) / 1e12,
+                "peak": MFMA_PEAK_TFLOPS[wl.weight_dtype], "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = "grouped gate/up + SwiGLU (routed)"
+    roof["kernel_us"] = k_ms * 1e3
+
+    result = {
+        "metric": "MoE-layer tokens/sec (prefill) + decode µs/layer; % of MFMA / HBM peak",
+        "value": N / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "us_per_layer": ms * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.weight_dtype,
+        "data": "synthetic (seeded counter-based generator; random-init weights)",
+        "config": {"workload": wl.name, "num_tokens": N, "hidden": H, "num_experts": E, "router_width": R,
+                   "top_k": K, "inter": I, "shared_inter": Is, "scoring": wl.scoring,
+                   "weight_copies_cycled": n_layers, "experts_touched": e_t, "routed_rows": p_r},
+        "layer": {"flops": layer_flops, "alg_bytes": layer_bytes_alg,
+                  "hbm_frac": layer_bytes_alg / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
+                  "mfma_frac": layer_flops / (ms * 1e-3) / (MFMA_PEAK_TFLOPS[wl.weight_dtype] * 1e12)},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(result))
+
+
+def cpu_baseline(wl, seconds: float):
+    """The oracle as it stands, timed on the host cores on a bounded sample:
+    up to 64 tokens of the same layer shape, over 4 weight copies whose touched
+    experts are generated (and cached) before the timed runs."""
+    from threadpoolctl import threadpool_info
+
+    import moe_inputs as mi
+    from oracle import workloads as ow
+
+    n = min(wl.num_tokens, 64)
+    sw = wl.with_tokens(n)
+    copies = []
+    for l in range(4):
+        inp, cache = mi.host_inputs(sw, layer=l), {}
+        ow.run(sw, layer=l, inputs=inp, expert_cache=cache)  # untimed: fills the expert cache
+        copies.append((l, inp, cache))
+    done, t_used, runs = 0, 0.0, 0
+    while t_used < seconds and runs < 10000:
+        l, inp, cache = copies[runs % len(copies)]
+        t0 = time.perf_counter()
+        ow.run(sw, layer=l, inputs=inp, expert_cache=cache)
+        t_used += time.perf_counter() - t0
+        done += n
+        runs += 1
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": done / t_used, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{runs} oracle runs over {n} tokens of the {wl.name} layer shape (4 weight copies, experts "
+                      f"pre-generated), {t_used:.1f} s of host time"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,201 @@
+/*
+ * libmoe: the mixture-of-experts layer forward on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Every tensor argument is a DEVICE pointer to memory the caller owns;
+ * only the two structs (moe_config_t, moe_weights_t) and the size_t* out-arg of
+ * moe_workspace_size live in host memory.  The library never allocates, frees,
+ * synchronises or copies to the host: every call only enqueues kernels on
+ * `stream` (a hipStream_t; NULL is the null stream), so a sequence of calls can
+ * be captured into a HIP graph.  The caller keeps every buffer alive until the
+ * stream has finished the work.
+ *
+ * Layouts are row-major.  "bf16" is bfloat16 (uint16 bit patterns), "e4m3" is
+ * the OCP FP8 E4M3 format (bias 7, max 448, no infinities).  Weights follow the
+ * [out, in] convention of a linear layer: W_gate, W_up are [I, H], W_down is
+ * [H, I].  Ids are int32.  N = num_tokens, K = top_k, R = router_width,
+ * E = num_experts (real experts; router columns [E, R) are zero-computation
+ * "identity" experts), I = inter, Is = shared_inter, P = N*K.
+ *
+ * Errors: every call validates its arguments before it launches anything and
+ * returns a status; moe_last_error() returns a message for the calling thread's
+ * last failure.  No call falls back to another method silently.
+ *
+ * The method follows five pages of MoE dispatch code from two inference
+ * engines; the citations below name the page (its source file path) and the
+ * function or comment on it.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID = 1,     /* null/misaligned pointer, inconsistent sizes, bad enum value */
+  MOE_ERR_UNSUPPORTED = 2, /* a valid request this build does not implement (named in the message) */
+  MOE_ERR_WORKSPACE = 3,   /* workspace smaller than moe_workspace_size() ("need X bytes, have Y") */
+  MOE_ERR_HIP = 4          /* a HIP runtime error from a launch */
+} moe_status_t;
+
+enum { MOE_SCORING_SOFTMAX = 0, MOE_SCORING_SIGMOID = 1 };
+enum { MOE_WEIGHTS_BF16 = 0, MOE_WEIGHTS_FP8_E4M3 = 1 };
+enum { MOE_STAGE_GATE_UP = 0, MOE_STAGE_DOWN = 1 };
+enum { MOE_GROUP_ROUTED = 0, MOE_GROUP_SHARED = 1 };
+
+/* Layer hyper-parameters (the model-config fields the pages read: hidden_size,
+ * num_experts, num_experts_per_tok, moe_intermediate_size,
+ * shared_expert_intermediate_size, scoring_func, norm_topk_prob,
+ * routed_scaling_factor, and the router width router_logits_n).
+ * Supported: N >= 0; H and I multiples of 128; Is = 0 or a multiple of 128;
+ * 1 <= E <= R <= 1024; 1 <= K <= min(R, 32). */
+typedef struct {
+  int32_t num_tokens;   /* N */
+  int32_t hidden;       /* H */
+  int32_t num_experts;  /* E */
+  int32_t router_width; /* R */
+  int32_t top_k;        /* K */
+  int32_t inter;        /* I */
+  int32_t shared_inter; /* Is; 0 = no shared expert */
+  int32_t scoring;      /* MOE_SCORING_* */
+  int32_t renormalize;  /* nonzero: divide the K weights by their sum */
+  float routed_scale;   /* multiplies the (renormalised) weights */
+  int32_t weight_dtype; /* MOE_WEIGHTS_*: type of the expert (routed and shared) weights */
+} moe_config_t;
+
+/* Weights of one layer.  The router is always bf16.  Routed experts are reached
+ * through DEVICE arrays of E device pointers (per-expert pointer tables, as the
+ * pages keep them), so experts may live anywhere in device memory.
+ * bf16: gate_w[e], up_w[e] -> [I, H] bf16; down_w[e] -> [H, I] bf16.
+ * fp8:  the same matrices as e4m3 codes, plus one fp32 scale per 128x128 block:
+ *       gate_s[e], up_s[e] -> [I/128, H/128]; down_s[e] -> [H/128, I/128]
+ *       (dequantised weight = code * scale of its block).
+ * The shared expert, if Is > 0, is given directly (not through tables) with
+ * Is in place of I.  Pointers must be 16-byte aligned. */
+typedef struct {
+  const void* router_w;        /* [R, H] bf16 */
+  const float* correction_bias; /* [R] fp32, or NULL (no bias) */
+  const void* const* gate_w;   /* device array [E] */
+  const void* const* up_w;     /* device array [E] */
+  const void* const* down_w;   /* device array [E] */
+  const float* const* gate_s;  /* device array [E]; fp8 only, else NULL */
+  const float* const* up_s;
+  const float* const* down_s;
+  const void* sh_gate_w; /* [Is, H]; NULL when Is == 0 */
+  const void* sh_up_w;   /* [Is, H] */
+  const void* sh_down_w; /* [H, Is] */
+  const float* sh_gate_s; /* fp8 only: [Is/128, H/128] */
+  const float* sh_up_s;
+  const float* sh_down_s; /* [H/128, Is/128] */
+} moe_weights_t;
+
+/* Bytes of device workspace that moe_forward and moe_permute need for `cfg`
+ * (a function of the sizes only; 256-byte aligned pieces). */
+moe_status_t moe_workspace_size(const moe_config_t* cfg, size_t* bytes);
+
+/* Router gate GEMM + scoring + top-K selection.
+ * forward_prefill.rs page, MoeLayer::forward_prefill gate GEMM and top-K steps;
+ * forward.rs page, MoeLayer::forward top-K arms (moe_topk_softmax;
+ * moe_topk_sigmoid with the correction bias used for selection only;
+ * moe_topk_softmax_bias with the zero-expert fold into zero_accum).
+ *   logits[t,r] = sum_h x[t,h] * router_w[r,h]          (fp32 accumulation)
+ *   p = softmax over all R columns, or sigmoid            (fp32)
+ *   ids[t,0..K) = the K largest p + bias (bias 0 if NULL), slots in descending
+ *                 order, exact ties to the lower column
+ *   w[t,k] = p[ids] (unbiased); / sum_k when renormalize; * routed_scale
+ *   zero_w[t] = sum of w[t,k] over slots with ids >= E
+ * x [N, H] bf16; router_w [R, H] bf16; correction_bias [R] fp32 or NULL;
+ * logits [N, R] fp32 (required: the scores are staged there); topk_ids [N, K]
+ * int32; topk_w [N, K] fp32; zero_w [N] fp32 or NULL. */
+moe_status_t moe_route_topk(const moe_config_t* cfg, const void* x, const void* router_w,
+                            const float* correction_bias, float* logits, int32_t* topk_ids, float* topk_w,
+                            float* zero_w, void* stream);
+
+/* Count and sort the expanded (token, slot) rows by expert.
+ * forward_prefill.rs page, moe_sort_by_expert (sorted_token_ids, expert_offsets,
+ * token_to_perm).  Every router column has a bucket; identity experts sort to
+ * the tail.  Stable: within a bucket rows keep ascending expanded index t*K+k.
+ *   counts[r] = #{(t,k): ids[t,k] == r}                  [R]
+ *   offsets   = exclusive prefix sum of counts            [R + 1], offsets[R] = P
+ *   sorted_ids[p] = the expanded index t*K+k at sorted position p   [P]
+ *   inv_perm[t*K+k] = its sorted position p (token_to_perm)          [P]
+ * ids must lie in [0, R) (an id outside is MOE_ERR_INVALID only if it can be
+ * seen on the host, so callers must pass ids produced by moe_route_topk).
+ * ws: at least moe_workspace_size(cfg) bytes. */
+moe_status_t moe_permute(const moe_config_t* cfg, const int32_t* topk_ids, int32_t* counts, int32_t* offsets,
+                         int32_t* sorted_ids, int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream);
+
+/* fp8 activation quantisation (the FP8 expert path: activations quantised per
+ * token and per 128-column group).  For each row and each group of 128 columns:
+ *   amax = max |x|; inv = 448 / amax (correctly rounded fp32);
+ *   xq = e4m3(x * inv) (round to nearest even, saturating); x_scales = amax / 448;
+ *   an all-zero group gets x_scales = 1 and zero codes.
+ * x [N, H] bf16 -> xq [N, H] e4m3 codes, x_scales [N, H/128] fp32. */
+moe_status_t moe_quantize_fp8(const moe_config_t* cfg, const void* x, uint8_t* xq, float* x_scales,
+                              void* stream);
+
+/* Grouped expert GEMM over the rows sorted by expert.
+ * forward_prefill.rs page, run_routed_grouped_gemm (grouped gate/up GEMM,
+ * activation, grouped down GEMM over expert_offsets / sorted_token_ids) and the
+ * shared expert (run_shared_expert_prefill).
+ * stage MOE_STAGE_GATE_UP:  out[p, :] = silu(a_p W_gate^T) * (a_p W_up^T)     [rows, I]
+ * stage MOE_STAGE_DOWN:     out[p, :] = a_p W_down^T                            [rows, H]
+ * group MOE_GROUP_ROUTED: rows p in [offsets[e], offsets[e+1]) use expert e's
+ *   weights, for e < E (identity-expert rows at the tail are not computed and
+ *   not written).  GATE_UP reads a_p = a[sorted_ids[p] / K] (a is [N, H], the
+ *   token's row); DOWN reads a_p = a[p] (a is the GATE_UP output, [P, I]).
+ * group MOE_GROUP_SHARED: rows t in [0, N) use the shared expert (Is in place
+ *   of I); a_t = a[t]; sorted_ids and offsets are ignored (may be NULL).
+ * bf16 weights: a and out are bf16; a_scales and out_scales are ignored.
+ * fp8 weights: a is e4m3 with a_scales [rows of a, cols/128] fp32 (from
+ *   moe_quantize_fp8 for GATE_UP, from the GATE_UP output for DOWN); GATE_UP
+ *   writes e4m3 codes + out_scales [P or N, I/128] quantised per 128 columns
+ *   like moe_quantize_fp8; DOWN writes bf16.
+ * ws: at least moe_workspace_size(cfg) bytes (may be NULL for this build). */
+moe_status_t moe_grouped_gemm(const moe_config_t* cfg, int32_t stage, int32_t group, const moe_weights_t* w,
+                              const void* a, const float* a_scales, const int32_t* sorted_ids,
+                              const int32_t* offsets, void* out, float* out_scales, void* ws, size_t ws_bytes,
+                              void* stream);
+
+/* Unpermute with the top-K-weighted reduce, plus the shared-expert and
+ * zero-computation-expert blends, rounded once to bf16.
+ * forward_prefill.rs page, moe_unpermute_reduce_indexed and the shared blend
+ * (weight 1 without a shared_expert_gate); forward.rs page,
+ * MoeLayer::apply_zero_expert (out[t,:] += zero_accum[t] * x[t,:]).
+ *   out[t,:] = bf16( sum_{k: ids<E} w[t,k] * y_sorted[inv_perm[t*K+k], :]
+ *                    + (sum_{k: ids>=E} w[t,k]) * x[t,:] + shared_y[t,:] )   (fp32 sum)
+ * y_sorted [P, H] bf16 (the DOWN output); inv_perm [P]; topk_ids, topk_w [N, K];
+ * x [N, H] bf16; shared_y [N, H] bf16 or NULL; out [N, H] bf16. */
+moe_status_t moe_unpermute_reduce(const moe_config_t* cfg, const void* y_sorted, const int32_t* inv_perm,
+                                  const int32_t* topk_ids, const float* topk_w, const void* x,
+                                  const void* shared_y, void* out, void* stream);
+
+/* The whole layer: route -> sort -> [quantise] -> gate/up (+ shared) -> down
+ * (+ shared) -> unpermute-reduce, on one stream with no host synchronisation.
+ * Same result as composing the calls above.  forward_prefill.rs page,
+ * MoeLayer::forward_prefill (the grouped data flow); forward.rs page,
+ * MoeLayer::forward and apply_zero_expert.
+ * x [N, H] bf16 -> out [N, H] bf16; ws: at least moe_workspace_size(cfg) bytes. */
+moe_status_t moe_forward(const moe_config_t* cfg, const moe_weights_t* w, const void* x, void* out, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/* Offsets of the intermediates inside the moe_forward workspace, so a caller
+ * can inspect them after moe_forward (all in bytes from the workspace start;
+ * a piece that the config does not use has offset SIZE_MAX). */
+typedef struct {
+  size_t logits, topk_ids, topk_w, zero_w, counts, offsets, sorted_ids, inv_perm;
+  size_t xq, x_scales, h, h_scales, y, shared_h, shared_h_scales, shared_y, scratch, total;
+} moe_workspace_layout_t;
+moe_status_t moe_workspace_layout(const moe_config_t* cfg, moe_workspace_layout_t* layout);
+
+const char* moe_status_str(moe_status_t status);
+const char* moe_last_error(void); /* thread-local; "" when the last call succeeded */
+
+#ifdef __cplusplus
+}
+#endif
+#endif

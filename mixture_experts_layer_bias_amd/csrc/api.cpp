@@ -1,0 +1,411 @@
+// The C ABI of libmoe (declared and documented in include/moe.h): argument
+// validation, the workspace layout and the launch sequence of moe_forward.
+// Host code only; every launch goes to the caller's stream and nothing here
+// allocates or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "kernels.h"
+#include "moe.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+moe_status_t fail(moe_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+moe_status_t ok() {
+  g_err[0] = '\0';
+  return MOE_OK;
+}
+
+#define MOE_CHECK(cond, st, ...) \
+  do {                           \
+    if (!(cond)) return fail(st, __VA_ARGS__); \
+  } while (0)
+
+#define MOE_HIP(expr)                                                                   \
+  do {                                                                                  \
+    hipError_t e_ = (expr);                                                             \
+    if (e_ != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+#define MOE_RET(expr)                   \
+  do {                                  \
+    moe_status_t s_ = (expr);           \
+    if (s_ != MOE_OK) return s_;        \
+  } while (0)
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+moe_status_t check_ptr(const void* p, size_t align, const char* name) {
+  MOE_CHECK(p != nullptr, MOE_ERR_INVALID, "%s is NULL", name);
+  MOE_CHECK(aligned(p, align), MOE_ERR_INVALID, "%s is not %zu-byte aligned", name, align);
+  return MOE_OK;
+}
+
+moe_status_t check_config(const moe_config_t* c) {
+  MOE_CHECK(c != nullptr, MOE_ERR_INVALID, "config is NULL");
+  MOE_CHECK(c->num_tokens >= 0, MOE_ERR_INVALID, "num_tokens %d < 0", c->num_tokens);
+  MOE_CHECK(c->num_experts >= 1, MOE_ERR_INVALID, "num_experts %d < 1", c->num_experts);
+  MOE_CHECK(c->router_width >= c->num_experts, MOE_ERR_INVALID, "router_width %d < num_experts %d",
+            c->router_width, c->num_experts);
+  MOE_CHECK(c->top_k >= 1 && c->top_k <= c->router_width, MOE_ERR_INVALID, "top_k %d not in [1, router_width %d]",
+            c->top_k, c->router_width);
+  MOE_CHECK(c->scoring == MOE_SCORING_SOFTMAX || c->scoring == MOE_SCORING_SIGMOID, MOE_ERR_INVALID,
+            "scoring %d is not a MOE_SCORING_* value", c->scoring);
+  MOE_CHECK(c->weight_dtype == MOE_WEIGHTS_BF16 || c->weight_dtype == MOE_WEIGHTS_FP8_E4M3, MOE_ERR_INVALID,
+            "weight_dtype %d is not a MOE_WEIGHTS_* value", c->weight_dtype);
+  MOE_CHECK(std::isfinite(c->routed_scale), MOE_ERR_INVALID, "routed_scale is not finite");
+  MOE_CHECK(c->hidden > 0 && c->inter > 0 && c->shared_inter >= 0, MOE_ERR_INVALID,
+            "hidden %d, inter %d must be > 0 and shared_inter %d >= 0", c->hidden, c->inter, c->shared_inter);
+  MOE_CHECK(c->router_width <= 1024, MOE_ERR_UNSUPPORTED, "router_width %d > 1024", c->router_width);
+  MOE_CHECK(c->top_k <= 32, MOE_ERR_UNSUPPORTED, "top_k %d > 32", c->top_k);
+  MOE_CHECK(c->hidden % 128 == 0, MOE_ERR_UNSUPPORTED, "hidden %d is not a multiple of 128", c->hidden);
+  MOE_CHECK(c->inter % 128 == 0, MOE_ERR_UNSUPPORTED, "inter %d is not a multiple of 128", c->inter);
+  MOE_CHECK(c->shared_inter % 128 == 0, MOE_ERR_UNSUPPORTED, "shared_inter %d is not a multiple of 128",
+            c->shared_inter);
+  MOE_CHECK((int64_t)c->num_tokens * c->top_k < (int64_t)1 << 30, MOE_ERR_UNSUPPORTED,
+            "num_tokens * top_k = %lld is too large", (long long)c->num_tokens * c->top_k);
+  return MOE_OK;
+}
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+void compute_layout(const moe_config_t* c, moe_workspace_layout_t* L) {
+  const size_t N = c->num_tokens, H = c->hidden, R = c->router_width, K = c->top_k, I = c->inter,
+               Is = c->shared_inter, P = N * K;
+  const bool fp8 = c->weight_dtype == MOE_WEIGHTS_FP8_E4M3;
+  const size_t none = SIZE_MAX;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  L->logits = take(N * R * 4);
+  L->topk_ids = take(P * 4);
+  L->topk_w = take(P * 4);
+  L->zero_w = take(N * 4);
+  L->counts = take(R * 4);
+  L->offsets = take((R + 1) * 4);
+  L->sorted_ids = take(P * 4);
+  L->inv_perm = take(P * 4);
+  L->scratch = take((size_t)moe::permute_chunks((int)P) * R * 4);
+  L->xq = fp8 ? take(N * H) : none;
+  L->x_scales = fp8 ? take(N * (H / 128) * 4) : none;
+  L->h = take(P * I * (fp8 ? 1 : 2));
+  L->h_scales = fp8 ? take(P * (I / 128) * 4) : none;
+  L->y = take(P * H * 2);
+  L->shared_h = Is ? take(N * Is * (fp8 ? 1 : 2)) : none;
+  L->shared_h_scales = (Is && fp8) ? take(N * (Is / 128) * 4) : none;
+  L->shared_y = Is ? take(N * H * 2) : none;
+  L->total = off;
+}
+
+moe_status_t check_weights(const moe_config_t* c, const moe_weights_t* w) {
+  MOE_CHECK(w != nullptr, MOE_ERR_INVALID, "weights is NULL");
+  MOE_RET(check_ptr(w->router_w, 16, "router_w"));
+  if (w->correction_bias) MOE_RET(check_ptr(w->correction_bias, 4, "correction_bias"));
+  MOE_RET(check_ptr(w->gate_w, 8, "gate_w table"));
+  MOE_RET(check_ptr(w->up_w, 8, "up_w table"));
+  MOE_RET(check_ptr(w->down_w, 8, "down_w table"));
+  const bool fp8 = c->weight_dtype == MOE_WEIGHTS_FP8_E4M3;
+  if (fp8) {
+    MOE_RET(check_ptr(w->gate_s, 8, "gate_s table"));
+    MOE_RET(check_ptr(w->up_s, 8, "up_s table"));
+    MOE_RET(check_ptr(w->down_s, 8, "down_s table"));
+  }
+  if (c->shared_inter > 0) {
+    MOE_RET(check_ptr(w->sh_gate_w, 16, "sh_gate_w"));
+    MOE_RET(check_ptr(w->sh_up_w, 16, "sh_up_w"));
+    MOE_RET(check_ptr(w->sh_down_w, 16, "sh_down_w"));
+    if (fp8) {
+      MOE_RET(check_ptr(w->sh_gate_s, 4, "sh_gate_s"));
+      MOE_RET(check_ptr(w->sh_up_s, 4, "sh_up_s"));
+      MOE_RET(check_ptr(w->sh_down_s, 4, "sh_down_s"));
+    }
+  }
+  return MOE_OK;
+}
+
+moe::GroupedGemmArgs gemm_args(const moe_config_t* c, int stage, int group, const moe_weights_t* w, const void* a,
+                               const float* a_scales, const int32_t* sorted_ids, const int32_t* offsets, void* out,
+                               float* out_scales) {
+  moe::GroupedGemmArgs g{};
+  g.stage = stage;
+  g.shared = group == MOE_GROUP_SHARED;
+  g.N = c->num_tokens;
+  g.H = c->hidden;
+  g.I = g.shared ? c->shared_inter : c->inter;
+  g.K = c->top_k;
+  g.E = c->num_experts;
+  g.P = g.shared ? c->num_tokens : c->num_tokens * c->top_k;
+  g.a = a;
+  g.a_scales = a_scales;
+  g.sorted_ids = sorted_ids;
+  g.offsets = offsets;
+  g.w_gate = w->gate_w;
+  g.w_up = w->up_w;
+  g.w_down = w->down_w;
+  g.s_gate = w->gate_s;
+  g.s_up = w->up_s;
+  g.s_down = w->down_s;
+  g.sh_gate = w->sh_gate_w;
+  g.sh_up = w->sh_up_w;
+  g.sh_down = w->sh_down_w;
+  g.sh_gate_s = w->sh_gate_s;
+  g.sh_up_s = w->sh_up_s;
+  g.sh_down_s = w->sh_down_s;
+  g.out = out;
+  g.out_scales = out_scales;
+  return g;
+}
+
+moe_status_t run_gemm(const moe_config_t* c, const moe::GroupedGemmArgs& g, hipStream_t s) {
+  if (c->weight_dtype == MOE_WEIGHTS_BF16) {
+    MOE_HIP(moe::launch_grouped_gemm_bf16(g, s));
+  } else {
+    return fail(MOE_ERR_UNSUPPORTED, "the fp8 grouped GEMM is not in this build yet");
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(moe_status_t status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID: return "MOE_ERR_INVALID";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_<unknown>";
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+moe_status_t moe_workspace_layout(const moe_config_t* cfg, moe_workspace_layout_t* layout) {
+  MOE_RET(check_config(cfg));
+  MOE_CHECK(layout != nullptr, MOE_ERR_INVALID, "layout is NULL");
+  compute_layout(cfg, layout);
+  return ok();
+}
+
+moe_status_t moe_workspace_size(const moe_config_t* cfg, size_t* bytes) {
+  MOE_RET(check_config(cfg));
+  MOE_CHECK(bytes != nullptr, MOE_ERR_INVALID, "bytes is NULL");
+  moe_workspace_layout_t L;
+  compute_layout(cfg, &L);
+  *bytes = L.total;
+  return ok();
+}
+
+moe_status_t moe_route_topk(const moe_config_t* cfg, const void* x, const void* router_w,
+                            const float* correction_bias, float* logits, int32_t* topk_ids, float* topk_w,
+                            float* zero_w, void* stream) {
+  MOE_RET(check_config(cfg));
+  if (cfg->num_tokens == 0) return ok();
+  MOE_RET(check_ptr(x, 16, "x"));
+  MOE_RET(check_ptr(router_w, 16, "router_w"));
+  if (correction_bias) MOE_RET(check_ptr(correction_bias, 4, "correction_bias"));
+  MOE_RET(check_ptr(logits, 4, "logits"));
+  MOE_RET(check_ptr(topk_ids, 4, "topk_ids"));
+  MOE_RET(check_ptr(topk_w, 4, "topk_w"));
+  if (zero_w) MOE_RET(check_ptr(zero_w, 4, "zero_w"));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const moe_config_t& c = *cfg;
+  MOE_HIP(moe::launch_router_logits(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(router_w), logits,
+                                    c.num_tokens, c.hidden, c.router_width, s));
+  MOE_HIP(moe::launch_topk(logits, correction_bias, topk_ids, topk_w, zero_w, c.num_tokens, c.router_width,
+                           c.num_experts, c.top_k, c.scoring, c.renormalize, c.routed_scale, s));
+  return ok();
+}
+
+moe_status_t moe_permute(const moe_config_t* cfg, const int32_t* topk_ids, int32_t* counts, int32_t* offsets,
+                         int32_t* sorted_ids, int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream) {
+  MOE_RET(check_config(cfg));
+  MOE_RET(check_ptr(counts, 4, "counts"));
+  MOE_RET(check_ptr(offsets, 4, "offsets"));
+  moe_workspace_layout_t L;
+  compute_layout(cfg, &L);
+  MOE_CHECK(ws_bytes >= L.total, MOE_ERR_WORKSPACE, "workspace too small: need %zu bytes, have %zu", L.total,
+            ws_bytes);
+  MOE_RET(check_ptr(ws, 256, "ws"));
+  if (cfg->num_tokens > 0) {
+    MOE_RET(check_ptr(topk_ids, 4, "topk_ids"));
+    MOE_RET(check_ptr(sorted_ids, 4, "sorted_ids"));
+    MOE_RET(check_ptr(inv_perm, 4, "inv_perm"));
+  }
+  const int P = cfg->num_tokens * cfg->top_k;
+  int32_t* hist = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + L.scratch);
+  MOE_HIP(moe::launch_permute(topk_ids, P, cfg->router_width, counts, offsets, sorted_ids, inv_perm, hist,
+                              static_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+moe_status_t moe_quantize_fp8(const moe_config_t* cfg, const void* x, uint8_t* xq, float* x_scales, void* stream) {
+  MOE_RET(check_config(cfg));
+  if (cfg->num_tokens == 0) return ok();
+  MOE_RET(check_ptr(x, 16, "x"));
+  MOE_RET(check_ptr(xq, 16, "xq"));
+  MOE_RET(check_ptr(x_scales, 4, "x_scales"));
+  MOE_HIP(moe::launch_quant_fp8(static_cast<const uint16_t*>(x), xq, x_scales, cfg->num_tokens, cfg->hidden,
+                                static_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+moe_status_t moe_grouped_gemm(const moe_config_t* cfg, int32_t stage, int32_t group, const moe_weights_t* w,
+                              const void* a, const float* a_scales, const int32_t* sorted_ids,
+                              const int32_t* offsets, void* out, float* out_scales, void* ws, size_t ws_bytes,
+                              void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  MOE_RET(check_config(cfg));
+  MOE_CHECK(stage == MOE_STAGE_GATE_UP || stage == MOE_STAGE_DOWN, MOE_ERR_INVALID,
+            "stage %d is not a MOE_STAGE_* value", stage);
+  MOE_CHECK(group == MOE_GROUP_ROUTED || group == MOE_GROUP_SHARED, MOE_ERR_INVALID,
+            "group %d is not a MOE_GROUP_* value", group);
+  MOE_CHECK(w != nullptr, MOE_ERR_INVALID, "weights is NULL");
+  const bool fp8 = cfg->weight_dtype == MOE_WEIGHTS_FP8_E4M3;
+  const bool shared = group == MOE_GROUP_SHARED;
+  if (shared) MOE_CHECK(cfg->shared_inter > 0, MOE_ERR_INVALID, "MOE_GROUP_SHARED with shared_inter == 0");
+  if (cfg->num_tokens == 0) return ok();
+  MOE_RET(check_ptr(a, 16, "a"));
+  MOE_RET(check_ptr(out, 16, "out"));
+  if (fp8) {
+    MOE_RET(check_ptr(a_scales, 4, "a_scales"));
+    if (stage == MOE_STAGE_GATE_UP) MOE_RET(check_ptr(out_scales, 4, "out_scales"));
+  }
+  if (!shared) {
+    MOE_RET(check_ptr(offsets, 4, "offsets"));
+    if (stage == MOE_STAGE_GATE_UP) MOE_RET(check_ptr(sorted_ids, 4, "sorted_ids"));
+    if (stage == MOE_STAGE_GATE_UP) {
+      MOE_RET(check_ptr(w->gate_w, 8, "gate_w table"));
+      MOE_RET(check_ptr(w->up_w, 8, "up_w table"));
+      if (fp8) {
+        MOE_RET(check_ptr(w->gate_s, 8, "gate_s table"));
+        MOE_RET(check_ptr(w->up_s, 8, "up_s table"));
+      }
+    } else {
+      MOE_RET(check_ptr(w->down_w, 8, "down_w table"));
+      if (fp8) MOE_RET(check_ptr(w->down_s, 8, "down_s table"));
+    }
+  } else {
+    if (stage == MOE_STAGE_GATE_UP) {
+      MOE_RET(check_ptr(w->sh_gate_w, 16, "sh_gate_w"));
+      MOE_RET(check_ptr(w->sh_up_w, 16, "sh_up_w"));
+      if (fp8) {
+        MOE_RET(check_ptr(w->sh_gate_s, 4, "sh_gate_s"));
+        MOE_RET(check_ptr(w->sh_up_s, 4, "sh_up_s"));
+      }
+    } else {
+      MOE_RET(check_ptr(w->sh_down_w, 16, "sh_down_w"));
+      if (fp8) MOE_RET(check_ptr(w->sh_down_s, 4, "sh_down_s"));
+    }
+  }
+  const moe::GroupedGemmArgs g = gemm_args(cfg, stage, group, w, a, a_scales, sorted_ids, offsets, out, out_scales);
+  MOE_RET(run_gemm(cfg, g, static_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+moe_status_t moe_unpermute_reduce(const moe_config_t* cfg, const void* y_sorted, const int32_t* inv_perm,
+                                  const int32_t* topk_ids, const float* topk_w, const void* x,
+                                  const void* shared_y, void* out, void* stream) {
+  MOE_RET(check_config(cfg));
+  if (cfg->num_tokens == 0) return ok();
+  MOE_RET(check_ptr(y_sorted, 16, "y_sorted"));
+  MOE_RET(check_ptr(inv_perm, 4, "inv_perm"));
+  MOE_RET(check_ptr(topk_ids, 4, "topk_ids"));
+  MOE_RET(check_ptr(topk_w, 4, "topk_w"));
+  MOE_RET(check_ptr(x, 16, "x"));
+  if (shared_y) MOE_RET(check_ptr(shared_y, 16, "shared_y"));
+  MOE_RET(check_ptr(out, 16, "out"));
+  MOE_HIP(moe::launch_unpermute_reduce(static_cast<const uint16_t*>(y_sorted), inv_perm, topk_ids, topk_w,
+                                       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(shared_y),
+                                       static_cast<uint16_t*>(out), cfg->num_tokens, cfg->hidden, cfg->top_k,
+                                       cfg->num_experts, static_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+moe_status_t moe_forward(const moe_config_t* cfg, const moe_weights_t* w, const void* x, void* out, void* ws,
+                         size_t ws_bytes, void* stream) {
+  MOE_RET(check_config(cfg));
+  MOE_RET(check_weights(cfg, w));
+  moe_workspace_layout_t L;
+  compute_layout(cfg, &L);
+  MOE_CHECK(ws_bytes >= L.total, MOE_ERR_WORKSPACE, "workspace too small: need %zu bytes, have %zu", L.total,
+            ws_bytes);
+  if (cfg->num_tokens == 0) return ok();
+  MOE_RET(check_ptr(x, 16, "x"));
+  MOE_RET(check_ptr(out, 16, "out"));
+  MOE_RET(check_ptr(ws, 256, "ws"));
+  const moe_config_t& c = *cfg;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  auto at = [&](size_t off) -> void* { return off == SIZE_MAX ? nullptr : base + off; };
+  float* logits = static_cast<float*>(at(L.logits));
+  int32_t* ids = static_cast<int32_t*>(at(L.topk_ids));
+  float* tw = static_cast<float*>(at(L.topk_w));
+  float* zw = static_cast<float*>(at(L.zero_w));
+  int32_t* counts = static_cast<int32_t*>(at(L.counts));
+  int32_t* offsets = static_cast<int32_t*>(at(L.offsets));
+  int32_t* sorted_ids = static_cast<int32_t*>(at(L.sorted_ids));
+  int32_t* inv_perm = static_cast<int32_t*>(at(L.inv_perm));
+  int32_t* hist = static_cast<int32_t*>(at(L.scratch));
+  const bool fp8 = c.weight_dtype == MOE_WEIGHTS_FP8_E4M3;
+  const int P = c.num_tokens * c.top_k;
+
+  MOE_HIP(moe::launch_router_logits(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w->router_w),
+                                    logits, c.num_tokens, c.hidden, c.router_width, s));
+  MOE_HIP(moe::launch_topk(logits, w->correction_bias, ids, tw, zw, c.num_tokens, c.router_width, c.num_experts,
+                           c.top_k, c.scoring, c.renormalize, c.routed_scale, s));
+  MOE_HIP(moe::launch_permute(ids, P, c.router_width, counts, offsets, sorted_ids, inv_perm, hist, s));
+  const void* a = x;
+  const float* a_scales = nullptr;
+  if (fp8) {
+    MOE_HIP(moe::launch_quant_fp8(static_cast<const uint16_t*>(x), static_cast<uint8_t*>(at(L.xq)),
+                                  static_cast<float*>(at(L.x_scales)), c.num_tokens, c.hidden, s));
+    a = at(L.xq);
+    a_scales = static_cast<const float*>(at(L.x_scales));
+  }
+  MOE_RET(run_gemm(cfg,
+                   gemm_args(cfg, MOE_STAGE_GATE_UP, MOE_GROUP_ROUTED, w, a, a_scales, sorted_ids, offsets, at(L.h),
+                             static_cast<float*>(at(L.h_scales))),
+                   s));
+  if (c.shared_inter > 0)
+    MOE_RET(run_gemm(cfg,
+                     gemm_args(cfg, MOE_STAGE_GATE_UP, MOE_GROUP_SHARED, w, a, a_scales, nullptr, nullptr,
+                               at(L.shared_h), static_cast<float*>(at(L.shared_h_scales))),
+                     s));
+  MOE_RET(run_gemm(cfg,
+                   gemm_args(cfg, MOE_STAGE_DOWN, MOE_GROUP_ROUTED, w, at(L.h), static_cast<float*>(at(L.h_scales)),
+                             sorted_ids, offsets, at(L.y), nullptr),
+                   s));
+  if (c.shared_inter > 0)
+    MOE_RET(run_gemm(cfg,
+                     gemm_args(cfg, MOE_STAGE_DOWN, MOE_GROUP_SHARED, w, at(L.shared_h),
+                               static_cast<float*>(at(L.shared_h_scales)), nullptr, nullptr, at(L.shared_y), nullptr),
+                     s));
+  MOE_HIP(moe::launch_unpermute_reduce(static_cast<const uint16_t*>(at(L.y)), inv_perm, ids, tw,
+                                       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(at(L.shared_y)),
+                                       static_cast<uint16_t*>(out), c.num_tokens, c.hidden, c.top_k, c.num_experts,
+                                       s));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,57 @@
+// Launch functions of the gfx950 MoE kernels (internal to libmoe; the C ABI in
+// include/moe.h validates arguments before calling these).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// a1 + a2: router logits and top-K selection
+hipError_t launch_router_logits(const uint16_t* x, const uint16_t* router_w, float* logits, int N, int H, int R,
+                                hipStream_t s);
+hipError_t launch_topk(const float* logits, const float* bias, int32_t* ids, float* w, float* zero_w, int N, int R,
+                       int E, int K, int scoring, int renormalize, float routed_scale, hipStream_t s);
+
+// a3: stable counting sort by expert; hist is [permute_chunks(P) * R] int32 scratch
+int permute_chunks(int P);
+hipError_t launch_permute(const int32_t* ids, int P, int R, int32_t* counts, int32_t* offsets, int32_t* sorted_ids,
+                          int32_t* inv_perm, int32_t* hist, hipStream_t s);
+
+// a4: per-token, per-128-column e4m3 quantisation of bf16 rows
+hipError_t launch_quant_fp8(const uint16_t* x, uint8_t* xq, float* xs, int rows, int cols, hipStream_t s);
+
+// a5 / a6: grouped expert GEMMs
+struct GroupedGemmArgs {
+  int stage;   // 0: gate/up + SwiGLU, 1: down
+  int shared;  // 1: the shared expert over all N rows (identity row map, direct weights)
+  int N, H, I, K, E;  // I is the expert's intermediate size (Is for the shared expert)
+  int P;               // N*K (routed) or N (shared): upper bound of rows
+  const void* a;        // gate/up: x [N,H] (bf16 or e4m3); down: h [rows, I]
+  const float* a_scales;  // fp8 only
+  const int32_t* sorted_ids;  // routed only
+  const int32_t* offsets;     // routed only: [E+1] (only the first E+1 entries are read)
+  const void* const* w_gate;  // routed: device tables; shared: nullptr
+  const void* const* w_up;
+  const void* const* w_down;
+  const float* const* s_gate;
+  const float* const* s_up;
+  const float* const* s_down;
+  const void* sh_gate;  // shared: direct pointers
+  const void* sh_up;
+  const void* sh_down;
+  const float* sh_gate_s;
+  const float* sh_up_s;
+  const float* sh_down_s;
+  void* out;           // gate/up: h [rows, I] (bf16 or e4m3); down: y [rows, H] bf16
+  float* out_scales;   // fp8 gate/up only: [rows, I/128]
+};
+hipError_t launch_grouped_gemm_bf16(const GroupedGemmArgs& g, hipStream_t s);
+hipError_t launch_grouped_gemm_fp8(const GroupedGemmArgs& g, hipStream_t s);
+
+// a7: unpermute + weighted reduce + identity-expert and shared blends
+hipError_t launch_unpermute_reduce(const uint16_t* y_sorted, const int32_t* inv_perm, const int32_t* ids,
+                                   const float* w, const uint16_t* x, const uint16_t* shared_y, uint16_t* out, int N,
+                                   int H, int K, int E, hipStream_t s);
+
+}  // namespace moe

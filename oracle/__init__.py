@@ -19,6 +19,10 @@ from .moe import (  # noqa: F401
     OracleResult,
     dequant_blocks,
     dequant_rows,
+    down_bf16,
+    down_fp8,
+    gate_up_bf16,
+    gate_up_fp8,
     moe_forward,
     quantize_fp8_groups,
     router_logits,

@@ -193,34 +193,52 @@ def silu(z: np.ndarray) -> np.ndarray:
     return z / (1.0 + np.exp(-z))
 
 
-def swiglu_expert_bf16(xrows: np.ndarray, wg_bits, wu_bits, wd_bits) -> np.ndarray:
-    """y = W_down * bf16(silu(W_gate x) * (W_up x)) for each row of xrows (float64).
+def gate_up_bf16(xrows: np.ndarray, wg_bits, wu_bits) -> np.ndarray:
+    """h = bf16(silu(W_gate x) * (W_up x)) for each row of xrows (float64 inputs).
 
-    forward_prefill.rs page: grouped gate/up GEMM, activation, grouped down
-    GEMM; W_gate, W_up are [I, H] and W_down is [H, I] (out x in).  h is
-    rounded to bf16, the down GEMM's operand type.
+    forward_prefill.rs page: grouped gate/up GEMM and the activation;
+    W_gate and W_up are [I, H] (out x in).  h is rounded to bf16, the down
+    GEMM's operand type.  Returns bf16 bits [rows, I].
     """
     g = xrows @ bf16_to_f64(wg_bits).T
     u = xrows @ bf16_to_f64(wu_bits).T
-    h = bf16_to_f64(f64_to_bf16(silu(g) * u))
-    return h @ bf16_to_f64(wd_bits).T
+    return f64_to_bf16(silu(g) * u)
 
 
-def swiglu_expert_fp8(xq_rows: np.ndarray, xs_rows: np.ndarray, wg, wu, wd) -> np.ndarray:
-    """The same expert on e4m3 operands with fp32 block scales.
+def down_bf16(h_bits: np.ndarray, wd_bits) -> np.ndarray:
+    """y = W_down h (float64, not rounded); W_down is [H, I].  forward_prefill.rs
+    page: grouped down GEMM."""
+    return bf16_to_f64(h_bits) @ bf16_to_f64(wd_bits).T
+
+
+def swiglu_expert_bf16(xrows: np.ndarray, wg_bits, wu_bits, wd_bits) -> np.ndarray:
+    """y = W_down * bf16(silu(W_gate x) * (W_up x)) for each row of xrows (float64)."""
+    return down_bf16(gate_up_bf16(xrows, wg_bits, wu_bits), wd_bits)
+
+
+def gate_up_fp8(xq_rows: np.ndarray, xs_rows: np.ndarray, wg, wu):
+    """The gate/up GEMM and activation on e4m3 operands with fp32 block scales.
 
     x rows arrive quantised per 128 columns; each weight is (codes, scales per
     128x128 block).  Dequantising both operands is exact in float64, so the
     float64 product equals the sum over 128-blocks of (s_x * S_w) times the
-    block's code dot product.  h is quantised per 128 columns like x (its
-    quantisation decision taken on fp32(h)) before the down GEMM.
+    block's code dot product.  h is then quantised per 128 columns like x (its
+    quantisation decision taken on fp32(h)).  Returns (codes, scales).
     """
     x = dequant_rows(xq_rows, xs_rows)
     g = x @ dequant_blocks(*wg).T
     u = x @ dequant_blocks(*wu).T
-    h32 = (silu(g) * u).astype(np.float32)
-    hq, hs = quantize_fp8_groups(h32)
+    return quantize_fp8_groups((silu(g) * u).astype(np.float32))
+
+
+def down_fp8(hq: np.ndarray, hs: np.ndarray, wd) -> np.ndarray:
+    """y = W_down h on e4m3 operands (float64 result, not rounded)."""
     return dequant_rows(hq, hs) @ dequant_blocks(*wd).T
+
+
+def swiglu_expert_fp8(xq_rows: np.ndarray, xs_rows: np.ndarray, wg, wu, wd) -> np.ndarray:
+    """The fp8 expert: gate_up_fp8 then down_fp8."""
+    return down_fp8(*gate_up_fp8(xq_rows, xs_rows, wg, wu), wd)
 
 
 # ----------------------------------------------------------------------------- the layer
@@ -244,8 +262,7 @@ ExpertFn = Callable[[int], tuple]
 
 
 def moe_forward(cfg: MoeConfig, x_bits: np.ndarray, router_bits: np.ndarray, bias: Optional[np.ndarray],
-                expert: ExpertFn, shared: Optional[tuple], tokens: Optional[np.ndarray] = None,
-                ids_override: Optional[dict] = None) -> OracleResult:
+                expert: ExpertFn, shared: Optional[tuple], tokens: Optional[np.ndarray] = None) -> OracleResult:
     """out[t] = bf16( sum_{k: id<E} w[t,k] * y_{t,k} + zero_accum[t] * x[t] + shared[t] ).
 
     Every token is independent, so ``x_bits`` may hold any subset of the
@@ -253,9 +270,6 @@ def moe_forward(cfg: MoeConfig, x_bits: np.ndarray, router_bits: np.ndarray, bia
     ``expert(e)`` returns routed expert e's weights (bf16 bit arrays
     (Wg, Wu, Wd), or fp8 ((codes, scales) x 3)), fetched only for experts some
     row selects; ``shared`` is the shared expert in the same form or None.
-    ``ids_override`` maps a row index to the K ids to use instead of the
-    oracle's own selection (for rows whose K-th and (K+1)-th selection scores
-    are nearly tied); weights are then taken for those ids.
 
     Steps as on the forward_prefill.rs page: gate GEMM, top-K, grouped
     gate/up + SwiGLU, grouped down, unpermute + top-K-weighted reduce, shared
@@ -269,9 +283,6 @@ def moe_forward(cfg: MoeConfig, x_bits: np.ndarray, router_bits: np.ndarray, bia
     logits = router_logits(x_bits, router_bits)
     p = scores(logits, cfg.scoring)
     ids, gap = select_topk(p, bias, K)
-    if ids_override:
-        for row, forced in ids_override.items():
-            ids[row] = np.asarray(forced, dtype=np.int32)
     w, zero_accum = routing_weights(p, ids, cfg.renormalize, cfg.routed_scale, E)
 
     x64 = bf16_to_f64(x_bits)

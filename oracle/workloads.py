@@ -20,7 +20,7 @@ def config_of(wl: mi.Workload) -> MoeConfig:
                      renormalize=wl.renormalize, routed_scale=wl.routed_scale, weight_dtype=wl.weight_dtype)
 
 
-def run(wl: mi.Workload, tokens: Optional[np.ndarray] = None, layer: int = 0, ids_override: Optional[dict] = None,
+def run(wl: mi.Workload, tokens: Optional[np.ndarray] = None, layer: int = 0,
         inputs: Optional[mi.HostInputs] = None, expert_cache: Optional[dict] = None) -> OracleResult:
     """The oracle on workload ``wl`` (all tokens, or the rows ``tokens``)."""
     inp = inputs if inputs is not None else mi.host_inputs(wl, layer) if tokens is None else None
@@ -31,15 +31,14 @@ def run(wl: mi.Workload, tokens: Optional[np.ndarray] = None, layer: int = 0, id
         x = inp.x[tokens] if inp is not None else mi.host_tokens(wl, tokens, layer)
         full = inp if inp is not None else _router_only(wl, layer)
         router, bias = full.router, full.bias
-    cache = expert_cache if expert_cache is not None else {}
-
     def expert(e: int):
-        if e not in cache:
-            cache[e] = mi.host_expert(wl, e, layer)
-        return cache[e]
+        if expert_cache is None:
+            return mi.host_expert(wl, e, layer)
+        if e not in expert_cache:
+            expert_cache[e] = mi.host_expert(wl, e, layer)
+        return expert_cache[e]
 
-    return moe_forward(config_of(wl), x, router, bias, expert, mi.host_shared(wl, layer), tokens=tokens,
-                       ids_override=ids_override)
+    return moe_forward(config_of(wl), x, router, bias, expert, mi.host_shared(wl, layer), tokens=tokens)
 
 
 @functools.lru_cache(maxsize=8)

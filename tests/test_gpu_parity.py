@@ -1,0 +1,289 @@
+"""Parity of the HIP path (through the C ABI) with the oracle, stage by stage
+and end to end, on small, ragged and full-size seeded workloads."""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_bias_amd as moe
+import moe_inputs as mi
+from oracle import moe as om
+from oracle import workloads as ow
+from tests import golden_cases
+from tests.gpu_common import (BF16_TOL, FP8_TOL, NEAR_TIE, assert_close, bits, check_routing, config_of, f64,
+                              from_bits, require_gpu, run_forward, weights_of)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+W = mi.Workload
+SMALL = {
+    "tiny": mi.TINY,
+    "decode": mi.DECODE,
+    "ragged_37tok_e16_top4": W("ragged", 37, 256, 16, 16, 4, 256, 0, "softmax", True, 1.0, "bf16", False, seed=3),
+    "sigmoid_bias_shared": W("sigmoid", 45, 512, 32, 32, 8, 256, 128, "sigmoid", True, 2.5, "bf16", True, seed=4),
+    "zero_experts_small": W("zero", 29, 384, 24, 36, 6, 128, 0, "softmax", False, 1.0, "bf16", True, seed=5),
+    "k_equals_r": W("k_eq_r", 9, 128, 4, 4, 4, 128, 0, "softmax", True, 1.0, "bf16", False, seed=6),
+    "one_expert": W("one_expert", 5, 128, 1, 1, 1, 128, 0, "softmax", True, 1.0, "bf16", False, seed=7),
+    "many_tiles_300tok": W("tiles", 300, 256, 8, 8, 2, 384, 256, "softmax", True, 1.0, "bf16", False, seed=8),
+}
+
+
+def _tol(wl):
+    return FP8_TOL if wl.weight_dtype == "fp8" else BF16_TOL
+
+
+# ============================================================================ generator
+
+def test_device_generator_matches_host():
+    t = torch.empty((300, 257), dtype=torch.bfloat16, device="cuda")
+    mi.dev_bf16(t, 5, mi.TAG_UP, 17, mi.SIGMA_W)
+    assert np.array_equal(bits(t), mi.host_bf16((300, 257), 5, mi.TAG_UP, 17, mi.SIGMA_W))
+    f = torch.empty((1000,), dtype=torch.float32, device="cuda")
+    mi.dev_f32(f, 1, mi.TAG_BIAS, 0, mi.SIGMA_BIAS, first=12345)
+    assert np.array_equal(f.cpu().numpy(), mi.host_f32((1000,), 1, mi.TAG_BIAS, 0, mi.SIGMA_BIAS, first=12345))
+    q = torch.empty((384, 256), dtype=torch.uint8, device="cuda")
+    s = torch.empty((3, 2), dtype=torch.float32, device="cuda")
+    mi.dev_e4m3(q, s, 384, 256, 0, mi.TAG_DOWN, 3, mi.SIGMA_W)
+    hq, hs = mi.host_e4m3(384, 256, 0, mi.TAG_DOWN, 3, mi.SIGMA_W)
+    assert np.array_equal(q.cpu().numpy(), hq) and np.array_equal(s.cpu().numpy(), hs)
+
+
+# ============================================================================ worked examples
+
+@pytest.mark.parametrize("ex", golden_cases.load(), ids=lambda e: e["name"])
+def test_hand_derived_worked_examples(ex):
+    g = golden_cases.tensors(ex)
+    c = ex["config"]
+    cfg = moe.make_config(1, c["hidden"], c["num_experts"], c["router_width"], c["top_k"], c["inter"],
+                          c["shared_inter"], c["scoring"], c["renormalize"], c["routed_scale"], "bf16")
+    stack = lambda i: from_bits(np.stack([e[i] for e in g["experts"]]))
+    sh = [None] * 3 if g["shared"] is None else [from_bits(a) for a in g["shared"]]
+    bias = None if g["bias"] is None else torch.from_numpy(g["bias"]).cuda()
+    w = moe.weights_from_stacked(from_bits(g["router"]), bias, stack(0), stack(1), stack(2), sh_gate=sh[0],
+                                 sh_up=sh[1], sh_down=sh[2])
+    x = from_bits(g["x"])
+    out, ws = run_forward(cfg, w, x)
+    torch.cuda.synchronize()
+    L = moe.moe_workspace_layout(cfg)
+    ids = ws[L["topk_ids"]:L["topk_ids"] + 4 * c["top_k"]].view(torch.int32).cpu().numpy()
+    wts = ws[L["topk_w"]:L["topk_w"] + 4 * c["top_k"]].view(torch.float32).cpu().numpy()
+    assert list(ids) == ex["ids"]
+    assert np.allclose(wts, ex["weights"], rtol=2e-6)
+    assert np.array_equal(f64(out)[0], g["expected_out"])
+
+
+# ============================================================================ stage by stage
+
+def _alloc(n, dtype, dev="cuda"):
+    return torch.empty(n, dtype=dtype, device=dev)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_stages_match_oracle(name):
+    wl = SMALL[name]
+    print(f"\n[case] stages {name}", flush=True)
+    N, H, E, R, K, I, Is = (wl.num_tokens, wl.hidden, wl.num_experts, wl.router_width, wl.top_k, wl.inter,
+                            wl.shared_inter)
+    P = N * K
+    dl = mi.device.device_layer(wl)
+    cfg, w = config_of(wl), weights_of(dl)
+    host = mi.host_inputs(wl)
+    res = ow.run(wl, inputs=host)
+    ws = _alloc(moe.moe_workspace_size(cfg), torch.uint8)
+
+    # ---- route
+    logits, ids, tw, zw = (_alloc((N, R), torch.float32), _alloc((N, K), torch.int32), _alloc((N, K), torch.float32),
+                           _alloc((N,), torch.float32))
+    moe.moe_route_topk(cfg, dl.x, dl.router, dl.bias, logits, ids, tw, zw)
+    torch.cuda.synchronize()
+    assert_close(f64(logits), res.logits, 1e-5, "logits")
+    gids = ids.cpu().numpy()
+    same = check_routing(gids, res, K)
+    assert np.abs(f64(tw)[same] - res.weights[same]).max() <= 1e-5 * max(1.0, np.abs(res.weights).max())
+    assert np.abs(f64(zw)[same] - res.zero_accum[same]).max() <= 1e-5
+
+    # ---- permute (GPU ids): a stable bijection consistent with the ids; bit-exact vs the oracle when ids agree
+    counts, offsets, sorted_ids, inv_perm = (_alloc((R,), torch.int32), _alloc((R + 1,), torch.int32),
+                                            _alloc((P,), torch.int32), _alloc((P,), torch.int32))
+    moe.moe_permute(cfg, ids, counts, offsets, sorted_ids, inv_perm, ws)
+    torch.cuda.synchronize()
+    c_, o_, s_, i_ = (t.cpu().numpy() for t in (counts, offsets, sorted_ids, inv_perm))
+    flat = gids.reshape(-1)
+    assert np.array_equal(c_, np.bincount(flat, minlength=R)) and o_[R] == P
+    assert np.array_equal(i_[s_], np.arange(P))
+    assert np.array_equal(s_, np.argsort(flat, kind="stable"))
+    oc, oo, osid, oinv = om.sort_by_expert(res.ids, R)
+    if same.all():
+        for a, b in ((c_, oc), (o_, oo), (s_, osid), (i_, oinv)):
+            assert np.array_equal(a, b)
+
+    # ---- gate/up and down, fed with the oracle's permutation and intermediates
+    Pr = int(oo[E])
+    x64 = om.bf16_to_f64(host.x)
+    h_ref = np.zeros((P, I), np.uint16)
+    y_ref = np.zeros((P, H))
+    for e in range(E):
+        rows = np.arange(oo[e], oo[e + 1])
+        if len(rows) == 0:
+            continue
+        wg, wu, wd = mi.host_expert(wl, e)
+        h_ref[rows] = om.gate_up_bf16(x64[osid[rows] // K], wg, wu)
+        y_ref[rows] = om.down_bf16(h_ref[rows], wd)
+    sid_d = torch.from_numpy(osid).cuda()
+    off_d = torch.from_numpy(oo).cuda()
+    h = torch.zeros((P, I), dtype=torch.bfloat16, device="cuda")
+    moe.moe_grouped_gemm(cfg, moe.MOE_STAGE_GATE_UP, moe.MOE_GROUP_ROUTED, w, dl.x, None, sid_d, off_d, h, None, ws)
+    y = torch.zeros((P, H), dtype=torch.bfloat16, device="cuda")
+    moe.moe_grouped_gemm(cfg, moe.MOE_STAGE_DOWN, moe.MOE_GROUP_ROUTED, w, from_bits(h_ref), None, sid_d, off_d, y,
+                         None, ws)
+    torch.cuda.synchronize()
+    if Pr:
+        assert_close(f64(h)[:Pr], om.bf16_to_f64(h_ref[:Pr]), BF16_TOL, "h (gate/up + SwiGLU)")
+        assert_close(f64(y)[:Pr], y_ref[:Pr], BF16_TOL, "y (down)")
+    assert (bits(h)[Pr:] == 0).all() and (bits(y)[Pr:] == 0).all(), "identity-expert rows must not be written"
+
+    shared_y = None
+    if Is:
+        sg, su, sd = mi.host_shared(wl)
+        sh_ref = om.gate_up_bf16(x64, sg, su)
+        shy_ref = om.down_bf16(sh_ref, sd)
+        shh = _alloc((N, Is), torch.bfloat16)
+        moe.moe_grouped_gemm(cfg, moe.MOE_STAGE_GATE_UP, moe.MOE_GROUP_SHARED, w, dl.x, None, None, None, shh)
+        shared_y = _alloc((N, H), torch.bfloat16)
+        moe.moe_grouped_gemm(cfg, moe.MOE_STAGE_DOWN, moe.MOE_GROUP_SHARED, w, from_bits(sh_ref), None, None, None,
+                             shared_y)
+        torch.cuda.synchronize()
+        assert_close(f64(shh), om.bf16_to_f64(sh_ref), BF16_TOL, "shared h")
+        assert_close(f64(shared_y), shy_ref, BF16_TOL, "shared y")
+
+    # ---- unpermute-reduce on the oracle's intermediates
+    out = _alloc((N, H), torch.bfloat16)
+    y_in = from_bits(om.f64_to_bf16(y_ref))
+    moe.moe_unpermute_reduce(cfg, y_in, torch.from_numpy(oinv).cuda(), torch.from_numpy(res.ids).cuda(),
+                             torch.from_numpy(res.weights.astype(np.float32)).cuda(), dl.x,
+                             None if shared_y is None else from_bits(om.f64_to_bf16(res.shared)), out)
+    torch.cuda.synchronize()
+    assert_close(f64(out), res.out_f64, BF16_TOL, "unpermute-reduce output")
+
+
+# ============================================================================ end to end
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_forward_matches_oracle_and_composed_stages(name):
+    wl = SMALL[name]
+    print(f"\n[case] forward {name}", flush=True)
+    dl = mi.device.device_layer(wl)
+    cfg, w = config_of(wl), weights_of(dl)
+    out, ws = run_forward(cfg, w, dl.x)
+    torch.cuda.synchronize()
+    res = ow.run(wl)
+    L = moe.moe_workspace_layout(cfg)
+    N, K = wl.num_tokens, wl.top_k
+    gids = ws[L["topk_ids"]:L["topk_ids"] + 4 * N * K].view(torch.int32).cpu().numpy().reshape(N, K)
+    same = check_routing(gids, res, K)
+    assert_close(f64(out)[same], res.out_f64[same], _tol(wl), "moe_forward output")
+
+    # the same layer through the stage calls is bit-identical
+    ws2 = torch.empty_like(ws)
+    s = lambda k: ws2[L[k]:]
+    P, R, H = N * K, wl.router_width, wl.hidden
+    logits = s("logits")[:4 * N * R].view(torch.float32)
+    ids = s("topk_ids")[:4 * P].view(torch.int32)
+    tw = s("topk_w")[:4 * P].view(torch.float32)
+    moe.moe_route_topk(cfg, dl.x, dl.router, dl.bias, logits, ids, tw, s("zero_w")[:4 * N].view(torch.float32))
+    counts, offsets = s("counts")[:4 * R].view(torch.int32), s("offsets")[:4 * (R + 1)].view(torch.int32)
+    sid, inv = s("sorted_ids")[:4 * P].view(torch.int32), s("inv_perm")[:4 * P].view(torch.int32)
+    moe.moe_permute(cfg, ids, counts, offsets, sid, inv, ws2)
+    h = s("h")[:2 * P * wl.inter].view(torch.bfloat16)
+    y = s("y")[:2 * P * H].view(torch.bfloat16)
+    moe.moe_grouped_gemm(cfg, 0, 0, w, dl.x, None, sid, offsets, h)
+    moe.moe_grouped_gemm(cfg, 1, 0, w, h, None, sid, offsets, y)
+    shy = None
+    if wl.shared_inter:
+        shh = s("shared_h")[:2 * N * wl.shared_inter].view(torch.bfloat16)
+        shy = s("shared_y")[:2 * N * H].view(torch.bfloat16)
+        moe.moe_grouped_gemm(cfg, 0, 1, w, dl.x, None, None, None, shh)
+        moe.moe_grouped_gemm(cfg, 1, 1, w, shh, None, None, None, shy)
+    out2 = torch.empty_like(out)
+    moe.moe_unpermute_reduce(cfg, y, inv, ids, tw, dl.x, shy, out2)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+def test_forward_is_deterministic():
+    wl = SMALL["many_tiles_300tok"]
+    dl = mi.device.device_layer(wl)
+    cfg, w = config_of(wl), weights_of(dl)
+    a, _ = run_forward(cfg, w, dl.x)
+    b, _ = run_forward(cfg, w, dl.x)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_zero_tokens_is_a_no_op():
+    wl = SMALL["tiny"]
+    dl = mi.device.device_layer(wl)
+    cfg = moe.config_with_tokens(config_of(wl), 0)
+    w = weights_of(dl)
+    ws = torch.empty(max(moe.moe_workspace_size(cfg), 256), dtype=torch.uint8, device="cuda")
+    out = torch.full_like(dl.x, 3.0)
+    moe.moe_forward(cfg, w, dl.x, out, ws)  # N = 0: nothing is read or written
+    torch.cuda.synchronize()
+    assert (out == 3.0).all()
+
+
+def test_workspace_too_small_is_refused():
+    wl = SMALL["tiny"]
+    dl = mi.device.device_layer(wl)
+    cfg, w = config_of(wl), weights_of(dl)
+    ws = torch.empty(moe.moe_workspace_size(cfg) - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(moe.MoeError) as e:
+        moe.moe_forward(cfg, w, dl.x, torch.empty_like(dl.x), ws)
+    assert e.value.status == moe.MOE_ERR_WORKSPACE and "need" in e.value.message
+
+
+# ============================================================================ full size
+
+FULL = {"decode": mi.DECODE, "prefill_zipf": mi.PREFILL_ZIPF, "zero_experts": mi.ZERO_EXPERTS}
+SAMPLE_TOKENS = {"decode": 4, "prefill_zipf": 48, "zero_experts": 12}
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_full_size_matches_oracle(name):
+    """Routing and the permutation over every token; outputs on sampled tokens."""
+    wl = FULL[name]
+    print(f"\n[case] full size {name} {wl.name}", flush=True)
+    N, K, R, E = wl.num_tokens, wl.top_k, wl.router_width, wl.num_experts
+    dl = mi.device.device_layer(wl)
+    cfg, w = config_of(wl), weights_of(dl)
+    out, ws = run_forward(cfg, w, dl.x)
+    torch.cuda.synchronize()
+    L = moe.moe_workspace_layout(cfg)
+    rd = lambda k, n: ws[L[k]:L[k] + 4 * n].view(torch.int32).cpu().numpy()
+    gids = rd("topk_ids", N * K).reshape(N, K)
+
+    host = mi.host_inputs(wl)
+    p = om.scores(om.router_logits(host.x, host.router), wl.scoring)
+    oids, gap = om.select_topk(p, host.bias, K)
+    near = gap < NEAR_TIE
+    same = (gids == oids).all(1)
+    assert not (~same & ~near).any()
+    print(f"near-tie rows: {near.sum()} of {N}; rows whose ids differ: {(~same).sum()}", flush=True)
+    if same.all():
+        oc, oo, osid, oinv = om.sort_by_expert(oids, R)
+        assert np.array_equal(rd("counts", R), oc) and np.array_equal(rd("offsets", R + 1), oo)
+        assert np.array_equal(rd("sorted_ids", N * K), osid) and np.array_equal(rd("inv_perm", N * K), oinv)
+
+    n_s = min(SAMPLE_TOKENS[name], N)
+    hot = np.bincount(oids.ravel(), minlength=R)[:E].argmax()
+    cand = np.unique(np.concatenate([np.linspace(0, N - 1, n_s).astype(int),
+                                     np.nonzero((oids == hot).any(1))[0][:4], [N - 1]]))
+    toks = cand[same[cand]]
+    res = ow.run(wl, tokens=toks, inputs=host)
+    assert np.array_equal(res.ids, gids[toks])
+    assert_close(f64(out)[toks], res.out_f64, _tol(wl), f"{name} sampled outputs")
