@@ -6,6 +6,7 @@ import torch
 
 import mixture_experts_layer_bias_amd as moe
 import moe_inputs as mi
+import moe_inputs.device  # noqa: F401  (mi.device)
 from oracle import moe as om
 from oracle import workloads as ow
 from tests import golden_cases
