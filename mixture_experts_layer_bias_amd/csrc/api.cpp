@@ -177,7 +177,7 @@ moe_status_t run_gemm(const moe_config_t* c, const moe::GroupedGemmArgs& g, hipS
   if (c->weight_dtype == MOE_WEIGHTS_BF16) {
     MOE_HIP(moe::launch_grouped_gemm_bf16(g, s));
   } else {
-    return fail(MOE_ERR_UNSUPPORTED, "the fp8 grouped GEMM is not in this build yet");
+    MOE_HIP(moe::launch_grouped_gemm_fp8(g, s));
   }
   return MOE_OK;
 }

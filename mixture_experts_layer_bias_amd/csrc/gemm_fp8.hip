@@ -1,0 +1,262 @@
+// Grouped expert GEMMs on OCP e4m3 weights with fp32 128x128 block scales, for
+// gfx950 (v_mfma_f32_32x32x64_f8f6f4, e4m3 x e4m3 -> fp32).
+//
+// Same data flow as the bf16 kernels (forward_prefill.rs page,
+// run_routed_grouped_gemm; the FP8 expert tables of the forward.rs page carry
+// one weight pointer and one scale pointer per expert).  The activation rows
+// carry one fp32 scale per 128 columns and the weights one per 128x128 block,
+// neither of which is the power-of-two block scale the scaled MFMA consumes, so
+// every K step is exactly one 128-column scale block: its MFMA sums start from
+// zero, and the block result is promoted into the fp32 accumulator with the
+// product (row scale x weight-block scale) on the vector ALU.
+//
+// Block tile BM = 128 rows x BN = 128 output columns, K step 128 bytes, 4 waves
+// in 2 x 2, each wave 64 x 64 (x2 for gate and up).  The gate/up epilogue
+// computes h = silu(g) * u and quantises it per row over the tile's 128 columns
+// (one e4m3 scale group, the same recipe as moe_quantize_fp8), so h leaves the
+// kernel as e4m3 codes + one fp32 scale per 128 columns.
+#include "common.h"
+#include "gemm_common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int BM = 128, BN = 128, BK = 128;
+constexpr int LDS_STRIDE = BK + 16;  // bytes per LDS row
+
+template <int STAGE>
+struct Fp8Tile {
+  static constexpr int BROWS = STAGE == 0 ? 2 * BN : BN;
+  static constexpr int A_LOADS = BM * (BK / 16) / 256;  // 16-byte chunks per thread
+  static constexpr int B_LOADS = BROWS * (BK / 16) / 256;
+  static constexpr int LDS_BYTES = (BM + BROWS) * LDS_STRIDE;
+};
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+
+template <int STAGE>
+__global__ __launch_bounds__(256, STAGE == 0 ? 1 : 2) void k_grouped_gemm_fp8(GroupedGemmArgs g) {
+  using T = Fp8Tile<STAGE>;
+  __shared__ __align__(16) uint8_t lds[T::LDS_BYTES];
+  __shared__ float s_asc[BM];   // row scales of the current K block
+  __shared__ float s_amax[2][BM];  // gate/up epilogue: per-row amax of each column half
+  uint8_t* a_lds = lds;
+  uint8_t* b_lds = lds + BM * LDS_STRIDE;
+  __shared__ int s_prefix[kMaxGroups + 1];
+  __shared__ int s_wsum[4];
+
+  const int KD = STAGE == 0 ? g.H : g.I;
+  const int NCOLS = STAGE == 0 ? g.I : g.H;
+  const int NT = NCOLS / BN;
+  const int KB = KD / 128;  // scale blocks along K
+  const TileCoord tc =
+      schedule_tile(g.offsets, g.shared ? 1 : g.E, g.shared ? g.N : -1, BM, NT, s_prefix, s_wsum);
+  if (tc.expert < 0) return;
+
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int n0 = tc.n_tile * BN;
+
+  const uint8_t *wa, *wb = nullptr;
+  const float *sa_w, *sb_w = nullptr;  // weight block scales
+  if (STAGE == 0) {
+    wa = static_cast<const uint8_t*>(g.shared ? g.sh_gate : g.w_gate[tc.expert]);
+    wb = static_cast<const uint8_t*>(g.shared ? g.sh_up : g.w_up[tc.expert]);
+    sa_w = g.shared ? g.sh_gate_s : g.s_gate[tc.expert];
+    sb_w = g.shared ? g.sh_up_s : g.s_up[tc.expert];
+  } else {
+    wa = static_cast<const uint8_t*>(g.shared ? g.sh_down : g.w_down[tc.expert]);
+    sa_w = g.shared ? g.sh_down_s : g.s_down[tc.expert];
+  }
+  // weight scales of this tile's 128 output columns: row block n0/128 of the [NCOLS/128, KB] scale grid
+  const float* swa = sa_w + (size_t)(n0 / 128) * KB;
+  const float* swb = STAGE == 0 ? sb_w + (size_t)(n0 / 128) * KB : nullptr;
+
+  const uint8_t* a_src = static_cast<const uint8_t*>(g.a);
+  const int lrow = tid >> 3;        // 0..31
+  const int lcol = (tid & 7) * 16;  // byte column of this thread's 16-byte chunk
+  const uint8_t* a_ptr[T::A_LOADS];
+#pragma unroll
+  for (int i = 0; i < T::A_LOADS; ++i) {
+    int p = tc.row0 + lrow + 32 * i;
+    if (p >= tc.row_end) p = tc.row_end - 1;
+    long arow = STAGE == 0 ? (g.shared ? p : g.sorted_ids[p] / g.K) : p;
+    a_ptr[i] = a_src + (size_t)arow * KD + lcol;
+  }
+  // the row-scale row of the A row this thread stages (threads 0..127, one row each)
+  const float* asc_ptr = nullptr;
+  if (tid < BM) {
+    int p = tc.row0 + tid;
+    if (p >= tc.row_end) p = tc.row_end - 1;
+    long arow = STAGE == 0 ? (g.shared ? p : g.sorted_ids[p] / g.K) : p;
+    asc_ptr = g.a_scales + (size_t)arow * KB;
+  }
+  const uint8_t* b_ptr[T::B_LOADS];
+#pragma unroll
+  for (int i = 0; i < T::B_LOADS; ++i) {
+    const int r = lrow + 32 * i;
+    if (STAGE == 0) b_ptr[i] = (r < BN ? wa + (size_t)(n0 + r) * KD : wb + (size_t)(n0 + r - BN) * KD) + lcol;
+    else b_ptr[i] = wa + (size_t)(n0 + r) * KD + lcol;
+  }
+
+  u32x4 ra[T::A_LOADS], rb[T::B_LOADS];
+  float rsc = 0.f;
+  auto load_tile = [&](int kb) {
+    const int k0 = kb * BK;
+#pragma unroll
+    for (int i = 0; i < T::A_LOADS; ++i) ra[i] = ld16(a_ptr[i] + k0);
+#pragma unroll
+    for (int i = 0; i < T::B_LOADS; ++i) rb[i] = ld16(b_ptr[i] + k0);
+    if (tid < BM) rsc = asc_ptr[kb];
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int i = 0; i < T::A_LOADS; ++i) st16(a_lds + (lrow + 32 * i) * LDS_STRIDE + lcol, ra[i]);
+#pragma unroll
+    for (int i = 0; i < T::B_LOADS; ++i) st16(b_lds + (lrow + 32 * i) * LDS_STRIDE + lcol, rb[i]);
+    if (tid < BM) s_asc[tid] = rsc;
+  };
+
+  constexpr int NB = STAGE == 0 ? 4 : 2;
+  f32x16 acc[2][NB];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][nb][r] = 0.f;
+
+  const int wm = wave >> 1, wn = wave & 1;
+  const int frow = lane & 31, fk = (lane >> 5) * 32;
+  // rows of this lane's accumulator items (32x32 D layout), relative to the wave's 32-row sub-tile
+  auto item_row = [&](int r) { return 8 * (r / 4) + 4 * (lane / 32) + (r % 4); };
+
+  load_tile(0);
+  store_tile();
+  __syncthreads();
+  for (int kb = 0; kb < KB; ++kb) {
+    const float wsa = swa[kb];
+    const float wsb = STAGE == 0 ? swb[kb] : 0.f;
+    if (kb + 1 < KB) load_tile(kb + 1);
+    f32x16 blk[2][NB];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) blk[mi][nb][r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 64) {
+      i32x8 af[2], bfr[NB];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) {
+        const uint8_t* p = a_lds + (wm * 64 + mi * 32 + frow) * LDS_STRIDE + kk + fk;
+        const u32x4 lo = ld16(p), hi = ld16(p + 16);
+        af[mi] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int brow = (STAGE == 0 && nb >= 2 ? BN : 0) + wn * 64 + (nb & 1) * 32 + frow;
+        const uint8_t* p = b_lds + brow * LDS_STRIDE + kk + fk;
+        const u32x4 lo = ld16(p), hi = ld16(p + 16);
+        bfr[nb] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      }
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) blk[mi][nb] = mfma_32x32x64_fp8(af[mi], bfr[nb], blk[mi][nb]);
+    }
+    // promote this scale block: acc += blk * (row scale * weight-block scale)
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float rs = s_asc[wm * 64 + mi * 32 + item_row(r)];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const float ws = (STAGE == 0 && nb >= 2) ? wsb : wsa;
+          acc[mi][nb][r] += blk[mi][nb][r] * (rs * ws);
+        }
+      }
+    __syncthreads();
+    if (kb + 1 < KB) {
+      store_tile();
+      __syncthreads();
+    }
+  }
+
+  if (STAGE == 1) {
+    uint16_t* out = static_cast<uint16_t*>(g.out);
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = tc.row0 + wm * 64 + mi * 32 + item_row(r);
+        if (row >= tc.row_end) continue;
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) {
+          const int col = n0 + wn * 64 + ni * 32 + (lane % 32);
+          out[(size_t)row * NCOLS + col] = (uint16_t)f32_to_bf16(acc[mi][ni][r]);
+        }
+      }
+    return;
+  }
+
+  // ---- gate/up epilogue: h = silu(g) * u, quantised per row over this tile's 128 columns
+  float h[2][16][2];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float m = 0.f;
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) {
+        h[mi][r][ni] = silu(acc[mi][ni][r]) * acc[mi][ni + 2][r];
+        m = fmaxf(m, fabsf(h[mi][r][ni]));
+      }
+      // max over the 32 lanes that hold this row (same lane / 32)
+#pragma unroll
+      for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+      if ((lane & 31) == 0) s_amax[wn][wm * 64 + mi * 32 + item_row(r)] = m;
+    }
+  __syncthreads();
+  uint8_t* out = static_cast<uint8_t*>(g.out);
+  const int groups = NCOLS / 128;
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int trow = wm * 64 + mi * 32 + item_row(r);
+      const int row = tc.row0 + trow;
+      const float amax = fmaxf(s_amax[0][trow], s_amax[1][trow]);
+      const float inv = amax > 0.f ? 448.0f / amax : 1.0f;
+      if (row < tc.row_end) {
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) {
+          const int col = n0 + wn * 64 + ni * 32 + (lane % 32);
+          out[(size_t)row * NCOLS + col] = (uint8_t)f32_to_e4m3(h[mi][r][ni] * inv);
+        }
+        if (wn == 0 && (lane & 31) == 0)
+          g.out_scales[(size_t)row * groups + tc.n_tile] = amax > 0.f ? amax / 448.0f : 1.0f;
+      }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_grouped_gemm_fp8(const GroupedGemmArgs& g, hipStream_t s) {
+  const int groups = g.shared ? 1 : g.E;
+  const int rows = g.shared ? g.N : g.P;
+  if (rows == 0) return hipSuccess;
+  if (g.stage == 0) {
+    const unsigned grid = grouped_grid(rows, groups, BM, g.I / BN);
+    k_grouped_gemm_fp8<0><<<grid, 256, 0, s>>>(g);
+  } else {
+    const unsigned grid = grouped_grid(rows, groups, BM, g.H / BN);
+    k_grouped_gemm_fp8<1><<<grid, 256, 0, s>>>(g);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

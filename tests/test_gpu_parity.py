@@ -32,6 +32,11 @@ SMALL = {
     "one_expert": W("one_expert", 5, 128, 1, 1, 1, 128, 0, "softmax", True, 1.0, "bf16", False, seed=7),
     "many_tiles_300tok": W("tiles", 300, 256, 8, 8, 2, 384, 256, "softmax", True, 1.0, "bf16", False, seed=8),
 }
+FP8_SMALL = {
+    "fp8_sigmoid_bias_shared": W("fp8s", 33, 512, 8, 8, 2, 256, 128, "sigmoid", True, 2.5, "fp8", True, seed=9),
+    "fp8_ragged_70tok_e16_top4": W("fp8r", 70, 256, 16, 16, 4, 384, 0, "softmax", True, 1.0, "fp8", False, seed=10),
+    "fp8_300tok_shared": W("fp8t", 300, 384, 8, 8, 3, 256, 256, "sigmoid", True, 2.5, "fp8", True, seed=11),
+}
 
 
 def _tol(wl):
@@ -172,11 +177,89 @@ def test_stages_match_oracle(name):
     assert_close(f64(out), res.out_f64, BF16_TOL, "unpermute-reduce output")
 
 
+# ============================================================================ fp8 stages
+
+def _dequant_dev(q: torch.Tensor, sc: torch.Tensor) -> np.ndarray:
+    return om.dequant_rows(q.cpu().numpy(), sc.cpu().numpy())
+
+
+def test_quantize_fp8_is_bit_exact():
+    """Activation codes and scales equal the oracle's fp32 recipe bit for bit,
+    including zero groups, tiny groups and large magnitudes."""
+    cfg = moe.make_config(64, 1024, 8, 8, 2, 128, weight_dtype="fp8")
+    x = torch.empty((64, 1024), dtype=torch.bfloat16, device="cuda")
+    mi.dev_bf16(x, 2, mi.TAG_X, 0, 1.0)
+    x[3, :128] = 0.0  # zero group -> scale 1, codes 0
+    x[4, 128:256] *= 1e-30  # deep subnormal e4m3 range after scaling? (amax maps to 448)
+    x[5, 256:384] *= 3e4
+    x[6, 384:512] = 0.0
+    x[6, 400] = -2.0  # one nonzero element
+    xq = torch.empty((64, 1024), dtype=torch.uint8, device="cuda")
+    xs = torch.empty((64, 8), dtype=torch.float32, device="cuda")
+    moe.moe_quantize_fp8(cfg, x, xq, xs)
+    torch.cuda.synchronize()
+    q_ref, s_ref = om.quantize_fp8_groups(f64(x).astype(np.float32))
+    assert np.array_equal(xs.cpu().numpy(), s_ref)
+    assert np.array_equal(xq.cpu().numpy(), q_ref)
+
+
+@pytest.mark.parametrize("name", list(FP8_SMALL))
+def test_fp8_stages_match_oracle(name):
+    wl = FP8_SMALL[name]
+    print(f"\n[case] fp8 stages {name}", flush=True)
+    N, H, E, R, K, I, Is = (wl.num_tokens, wl.hidden, wl.num_experts, wl.router_width, wl.top_k, wl.inter,
+                            wl.shared_inter)
+    P = N * K
+    dl = mi.device.device_layer(wl)
+    cfg, w = config_of(wl), weights_of(dl)
+    host = mi.host_inputs(wl)
+    res = ow.run(wl, inputs=host)
+    oc, oo, osid, oinv = om.sort_by_expert(res.ids, R)
+    xq_ref, xs_ref = om.quantize_fp8_groups(om.bf16_to_f64(host.x).astype(np.float32))
+    Pr = int(oo[E])
+    hq_ref = np.zeros((P, I), np.uint8)
+    hs_ref = np.ones((P, I // 128), np.float32)
+    y_ref = np.zeros((P, H))
+    for e in range(E):
+        rows = np.arange(oo[e], oo[e + 1])
+        if len(rows) == 0:
+            continue
+        wg, wu, wd = mi.host_expert(wl, e)
+        t = osid[rows] // K
+        hq_ref[rows], hs_ref[rows] = om.gate_up_fp8(xq_ref[t], xs_ref[t], wg, wu)
+        y_ref[rows] = om.down_fp8(hq_ref[rows], hs_ref[rows], wd)
+    xq_d, xs_d = torch.from_numpy(xq_ref).cuda(), torch.from_numpy(xs_ref).cuda()
+    sid_d, off_d = torch.from_numpy(osid).cuda(), torch.from_numpy(oo).cuda()
+    hq = torch.zeros((P, I), dtype=torch.uint8, device="cuda")
+    hs = torch.zeros((P, I // 128), dtype=torch.float32, device="cuda")
+    moe.moe_grouped_gemm(cfg, 0, 0, w, xq_d, xs_d, sid_d, off_d, hq, hs)
+    y = torch.zeros((P, H), dtype=torch.bfloat16, device="cuda")
+    moe.moe_grouped_gemm(cfg, 1, 0, w, torch.from_numpy(hq_ref).cuda(), torch.from_numpy(hs_ref).cuda(), sid_d,
+                         off_d, y)
+    torch.cuda.synchronize()
+    h_ref = om.dequant_rows(hq_ref[:Pr], hs_ref[:Pr])
+    assert_close(_dequant_dev(hq, hs)[:Pr], h_ref, FP8_TOL, "fp8 h (gate/up + SwiGLU + quantise)")
+    assert_close(f64(y)[:Pr], y_ref[:Pr], FP8_TOL, "fp8 y (down)")
+    assert (hq[Pr:] == 0).all() and (bits(y)[Pr:] == 0).all()
+    if Is:
+        sg, su, sd = mi.host_shared(wl)
+        shq_ref, shs_ref = om.gate_up_fp8(xq_ref, xs_ref, sg, su)
+        shq = torch.empty((N, Is), dtype=torch.uint8, device="cuda")
+        shs = torch.empty((N, Is // 128), dtype=torch.float32, device="cuda")
+        moe.moe_grouped_gemm(cfg, 0, 1, w, xq_d, xs_d, None, None, shq, shs)
+        shy = torch.empty((N, H), dtype=torch.bfloat16, device="cuda")
+        moe.moe_grouped_gemm(cfg, 1, 1, w, torch.from_numpy(shq_ref).cuda(), torch.from_numpy(shs_ref).cuda(), None,
+                             None, shy)
+        torch.cuda.synchronize()
+        assert_close(_dequant_dev(shq, shs), om.dequant_rows(shq_ref, shs_ref), FP8_TOL, "fp8 shared h")
+        assert_close(f64(shy), om.down_fp8(shq_ref, shs_ref, sd), FP8_TOL, "fp8 shared y")
+
+
 # ============================================================================ end to end
 
-@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("name", list(SMALL) + list(FP8_SMALL))
 def test_forward_matches_oracle_and_composed_stages(name):
-    wl = SMALL[name]
+    wl = SMALL.get(name) or FP8_SMALL[name]
     print(f"\n[case] forward {name}", flush=True)
     dl = mi.device.device_layer(wl)
     cfg, w = config_of(wl), weights_of(dl)
@@ -200,16 +283,30 @@ def test_forward_matches_oracle_and_composed_stages(name):
     counts, offsets = s("counts")[:4 * R].view(torch.int32), s("offsets")[:4 * (R + 1)].view(torch.int32)
     sid, inv = s("sorted_ids")[:4 * P].view(torch.int32), s("inv_perm")[:4 * P].view(torch.int32)
     moe.moe_permute(cfg, ids, counts, offsets, sid, inv, ws2)
-    h = s("h")[:2 * P * wl.inter].view(torch.bfloat16)
+    fp8 = wl.weight_dtype == "fp8"
+    a, a_sc, hs, shs = dl.x, None, None, None
+    if fp8:
+        a = s("xq")[:N * H]
+        a_sc = s("x_scales")[:4 * N * (H // 128)].view(torch.float32)
+        moe.moe_quantize_fp8(cfg, dl.x, a, a_sc)
+        h = s("h")[:P * wl.inter]
+        hs = s("h_scales")[:4 * P * (wl.inter // 128)].view(torch.float32)
+    else:
+        h = s("h")[:2 * P * wl.inter].view(torch.bfloat16)
     y = s("y")[:2 * P * H].view(torch.bfloat16)
-    moe.moe_grouped_gemm(cfg, 0, 0, w, dl.x, None, sid, offsets, h)
-    moe.moe_grouped_gemm(cfg, 1, 0, w, h, None, sid, offsets, y)
+    moe.moe_grouped_gemm(cfg, 0, 0, w, a, a_sc, sid, offsets, h, hs)
+    moe.moe_grouped_gemm(cfg, 1, 0, w, h, hs, sid, offsets, y)
     shy = None
     if wl.shared_inter:
-        shh = s("shared_h")[:2 * N * wl.shared_inter].view(torch.bfloat16)
+        Is = wl.shared_inter
+        if fp8:
+            shh = s("shared_h")[:N * Is]
+            shs = s("shared_h_scales")[:4 * N * (Is // 128)].view(torch.float32)
+        else:
+            shh = s("shared_h")[:2 * N * Is].view(torch.bfloat16)
         shy = s("shared_y")[:2 * N * H].view(torch.bfloat16)
-        moe.moe_grouped_gemm(cfg, 0, 1, w, dl.x, None, None, None, shh)
-        moe.moe_grouped_gemm(cfg, 1, 1, w, shh, None, None, None, shy)
+        moe.moe_grouped_gemm(cfg, 0, 1, w, a, a_sc, None, None, shh, shs)
+        moe.moe_grouped_gemm(cfg, 1, 1, w, shh, shs, None, None, shy)
     out2 = torch.empty_like(out)
     moe.moe_unpermute_reduce(cfg, y, inv, ids, tw, dl.x, shy, out2)
     torch.cuda.synchronize()
@@ -250,8 +347,9 @@ def test_workspace_too_small_is_refused():
 
 # ============================================================================ full size
 
-FULL = {"decode": mi.DECODE, "prefill_zipf": mi.PREFILL_ZIPF, "zero_experts": mi.ZERO_EXPERTS}
-SAMPLE_TOKENS = {"decode": 4, "prefill_zipf": 48, "zero_experts": 12}
+FULL = {"decode": mi.DECODE, "prefill_zipf": mi.PREFILL_ZIPF, "zero_experts": mi.ZERO_EXPERTS,
+        "fp8_sigmoid": mi.FP8_SIGMOID}
+SAMPLE_TOKENS = {"decode": 4, "prefill_zipf": 48, "zero_experts": 12, "fp8_sigmoid": 10}
 
 
 @pytest.mark.parametrize("name", list(FULL))
