@@ -75,9 +75,19 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
-// 16-byte global load / store helpers
+// 16-byte load / store through a generic pointer (LDS or global, whichever the
+// compiler can prove)
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// 16-byte load from GLOBAL memory.  Pointers read out of a device pointer table
+// are generic to the compiler, which would emit flat loads; a flat load also
+// counts against the LDS counter, so a wait for LDS reads would then wait for
+// the in-flight prefetch from HBM as well.  The cast makes it a global load.
+typedef const u32x4 __attribute__((address_space(1))) global_u32x4;
+__device__ __forceinline__ u32x4 ldg16(const void* p) { return *(global_u32x4*)(p); }
+typedef const float __attribute__((address_space(1))) global_f32;
+__device__ __forceinline__ float ldg_f32(const float* p) { return *(global_f32*)(p); }
 
 __device__ __forceinline__ f32x16 mfma_32x32x16_bf16(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,

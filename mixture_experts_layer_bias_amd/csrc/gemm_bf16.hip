@@ -90,9 +90,9 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_bf16(GroupedGemmArgs g)
   u32x4 ra[T::A_LOADS], rb[T::B_LOADS];
   auto load_tile = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < T::A_LOADS; ++i) ra[i] = ld16(a_ptr[i] + k0);
+    for (int i = 0; i < T::A_LOADS; ++i) ra[i] = ldg16(a_ptr[i] + k0);
 #pragma unroll
-    for (int i = 0; i < T::B_LOADS; ++i) rb[i] = ld16(b_ptr[i] + k0);
+    for (int i = 0; i < T::B_LOADS; ++i) rb[i] = ldg16(b_ptr[i] + k0);
   };
   auto store_tile = [&]() {
 #pragma unroll

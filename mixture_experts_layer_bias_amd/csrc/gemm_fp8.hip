@@ -105,10 +105,10 @@ __global__ __launch_bounds__(256, STAGE == 0 ? 1 : 2) void k_grouped_gemm_fp8(Gr
   auto load_tile = [&](int kb) {
     const int k0 = kb * BK;
 #pragma unroll
-    for (int i = 0; i < T::A_LOADS; ++i) ra[i] = ld16(a_ptr[i] + k0);
+    for (int i = 0; i < T::A_LOADS; ++i) ra[i] = ldg16(a_ptr[i] + k0);
 #pragma unroll
-    for (int i = 0; i < T::B_LOADS; ++i) rb[i] = ld16(b_ptr[i] + k0);
-    if (tid < BM) rsc = asc_ptr[kb];
+    for (int i = 0; i < T::B_LOADS; ++i) rb[i] = ldg16(b_ptr[i] + k0);
+    if (tid < BM) rsc = ldg_f32(asc_ptr + kb);
   };
   auto store_tile = [&]() {
 #pragma unroll
@@ -136,8 +136,8 @@ __global__ __launch_bounds__(256, STAGE == 0 ? 1 : 2) void k_grouped_gemm_fp8(Gr
   store_tile();
   __syncthreads();
   for (int kb = 0; kb < KB; ++kb) {
-    const float wsa = swa[kb];
-    const float wsb = STAGE == 0 ? swb[kb] : 0.f;
+    const float wsa = ldg_f32(swa + kb);
+    const float wsb = STAGE == 0 ? ldg_f32(swb + kb) : 0.f;
     if (kb + 1 < KB) load_tile(kb + 1);
     f32x16 blk[2][NB];
 #pragma unroll
