@@ -97,7 +97,8 @@ typedef struct {
  * (a function of the sizes only; 256-byte aligned pieces). */
 moe_status_t moe_workspace_size(const moe_config_t* cfg, size_t* bytes);
 
-/* Router gate GEMM + scoring + top-K selection.
+/* Router gate GEMM + scoring + top-K selection.  ws: at least
+ * moe_workspace_size(cfg) bytes (split-K partial logits are staged there).
  * forward_prefill.rs page, MoeLayer::forward_prefill gate GEMM and top-K steps;
  * forward.rs page, MoeLayer::forward top-K arms (moe_topk_softmax;
  * moe_topk_sigmoid with the correction bias used for selection only;
@@ -113,7 +114,7 @@ moe_status_t moe_workspace_size(const moe_config_t* cfg, size_t* bytes);
  * int32; topk_w [N, K] fp32; zero_w [N] fp32 or NULL. */
 moe_status_t moe_route_topk(const moe_config_t* cfg, const void* x, const void* router_w,
                             const float* correction_bias, float* logits, int32_t* topk_ids, float* topk_w,
-                            float* zero_w, void* stream);
+                            float* zero_w, void* ws, size_t ws_bytes, void* stream);
 
 /* Count and sort the expanded (token, slot) rows by expert.
  * forward_prefill.rs page, moe_sort_by_expert (sorted_token_ids, expert_offsets,
@@ -123,8 +124,9 @@ moe_status_t moe_route_topk(const moe_config_t* cfg, const void* x, const void* 
  *   offsets   = exclusive prefix sum of counts            [R + 1], offsets[R] = P
  *   sorted_ids[p] = the expanded index t*K+k at sorted position p   [P]
  *   inv_perm[t*K+k] = its sorted position p (token_to_perm)          [P]
- * ids must lie in [0, R) (an id outside is MOE_ERR_INVALID only if it can be
- * seen on the host, so callers must pass ids produced by moe_route_topk).
+ * The ids are device data the host cannot check: an id outside [0, R) is not
+ * counted and its row is not written, so the outputs are then not a
+ * permutation (ids from moe_route_topk are always in range).
  * ws: at least moe_workspace_size(cfg) bytes. */
 moe_status_t moe_permute(const moe_config_t* cfg, const int32_t* topk_ids, int32_t* counts, int32_t* offsets,
                          int32_t* sorted_ids, int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream);

@@ -72,7 +72,7 @@ def lib() -> ctypes.CDLL:
         sig = {
             "moe_workspace_size": [cfgp, ctypes.POINTER(sz)],
             "moe_workspace_layout": [cfgp, ctypes.POINTER(moe_workspace_layout_t)],
-            "moe_route_topk": [cfgp, vp, vp, vp, vp, vp, vp, vp, vp],
+            "moe_route_topk": [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
             "moe_permute": [cfgp, vp, vp, vp, vp, vp, vp, sz, vp],
             "moe_quantize_fp8": [cfgp, vp, vp, vp, vp],
             "moe_grouped_gemm": [cfgp, i32, i32, ctypes.POINTER(moe_weights_t), vp, vp, vp, vp, vp, vp, vp, sz, vp],
@@ -200,11 +200,12 @@ def moe_workspace_layout(cfg: moe_config_t) -> dict:
     return {name: getattr(L, name) for name, _ in moe_workspace_layout_t._fields_}
 
 
-def moe_route_topk(cfg, x, router_w, correction_bias, logits, topk_ids, topk_w, zero_w=None, stream=None) -> None:
+def moe_route_topk(cfg, x, router_w, correction_bias, logits, topk_ids, topk_w, zero_w, ws, stream=None) -> None:
     _check(lib().moe_route_topk(ctypes.byref(cfg), _ptr(x, "x", 2), _ptr(router_w, "router_w", 2),
                                 _ptr(correction_bias, "correction_bias", 4, True), _ptr(logits, "logits", 4),
                                 _ptr(topk_ids, "topk_ids", 4), _ptr(topk_w, "topk_w", 4),
-                                _ptr(zero_w, "zero_w", 4, True), _stream(stream)))
+                                _ptr(zero_w, "zero_w", 4, True), _ptr(ws, "ws"), ws.numel() * ws.element_size(),
+                                _stream(stream)))
 
 
 def moe_permute(cfg, topk_ids, counts, offsets, sorted_ids, inv_perm, ws, stream=None) -> None:

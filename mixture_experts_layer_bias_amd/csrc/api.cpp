@@ -102,7 +102,10 @@ void compute_layout(const moe_config_t* c, moe_workspace_layout_t* L) {
   L->offsets = take((R + 1) * 4);
   L->sorted_ids = take(P * 4);
   L->inv_perm = take(P * 4);
-  L->scratch = take((size_t)moe::permute_chunks((int)P) * R * 4);
+  const int slices = moe::router_slices((int)N, (int)H, (int)R);
+  const size_t hist_bytes = (size_t)moe::permute_chunks((int)P) * R * 4;
+  const size_t part_bytes = slices > 1 ? (size_t)slices * N * R * 4 : 0;
+  L->scratch = take(hist_bytes > part_bytes ? hist_bytes : part_bytes);
   L->xq = fp8 ? take(N * H) : none;
   L->x_scales = fp8 ? take(N * (H / 128) * 4) : none;
   L->h = take(P * I * (fp8 ? 1 : 2));
@@ -182,6 +185,17 @@ moe_status_t run_gemm(const moe_config_t* c, const moe::GroupedGemmArgs& g, hipS
   return MOE_OK;
 }
 
+moe_status_t launch_route(const moe_config_t* c, const void* x, const void* router_w, const float* bias,
+                          float* logits, int32_t* ids, float* tw, float* zw, float* scratch, hipStream_t s) {
+  const int slices = moe::router_slices(c->num_tokens, c->hidden, c->router_width);
+  float* part = slices > 1 ? scratch : logits;
+  MOE_HIP(moe::launch_router_logits(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(router_w), part,
+                                    c->num_tokens, c->hidden, c->router_width, slices, s));
+  MOE_HIP(moe::launch_topk(part, slices, logits, bias, ids, tw, zw, c->num_tokens, c->router_width, c->num_experts,
+                           c->top_k, c->scoring, c->renormalize, c->routed_scale, s));
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -217,8 +231,12 @@ moe_status_t moe_workspace_size(const moe_config_t* cfg, size_t* bytes) {
 
 moe_status_t moe_route_topk(const moe_config_t* cfg, const void* x, const void* router_w,
                             const float* correction_bias, float* logits, int32_t* topk_ids, float* topk_w,
-                            float* zero_w, void* stream) {
+                            float* zero_w, void* ws, size_t ws_bytes, void* stream) {
   MOE_RET(check_config(cfg));
+  moe_workspace_layout_t L;
+  compute_layout(cfg, &L);
+  MOE_CHECK(ws_bytes >= L.total, MOE_ERR_WORKSPACE, "workspace too small: need %zu bytes, have %zu", L.total,
+            ws_bytes);
   if (cfg->num_tokens == 0) return ok();
   MOE_RET(check_ptr(x, 16, "x"));
   MOE_RET(check_ptr(router_w, 16, "router_w"));
@@ -227,12 +245,9 @@ moe_status_t moe_route_topk(const moe_config_t* cfg, const void* x, const void* 
   MOE_RET(check_ptr(topk_ids, 4, "topk_ids"));
   MOE_RET(check_ptr(topk_w, 4, "topk_w"));
   if (zero_w) MOE_RET(check_ptr(zero_w, 4, "zero_w"));
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const moe_config_t& c = *cfg;
-  MOE_HIP(moe::launch_router_logits(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(router_w), logits,
-                                    c.num_tokens, c.hidden, c.router_width, s));
-  MOE_HIP(moe::launch_topk(logits, correction_bias, topk_ids, topk_w, zero_w, c.num_tokens, c.router_width,
-                           c.num_experts, c.top_k, c.scoring, c.renormalize, c.routed_scale, s));
+  MOE_RET(check_ptr(ws, 256, "ws"));
+  MOE_RET(launch_route(cfg, x, router_w, correction_bias, logits, topk_ids, topk_w, zero_w,
+                       reinterpret_cast<float*>(static_cast<char*>(ws) + L.scratch), static_cast<hipStream_t>(stream)));
   return ok();
 }
 
@@ -370,10 +385,7 @@ moe_status_t moe_forward(const moe_config_t* cfg, const moe_weights_t* w, const 
   const bool fp8 = c.weight_dtype == MOE_WEIGHTS_FP8_E4M3;
   const int P = c.num_tokens * c.top_k;
 
-  MOE_HIP(moe::launch_router_logits(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w->router_w),
-                                    logits, c.num_tokens, c.hidden, c.router_width, s));
-  MOE_HIP(moe::launch_topk(logits, w->correction_bias, ids, tw, zw, c.num_tokens, c.router_width, c.num_experts,
-                           c.top_k, c.scoring, c.renormalize, c.routed_scale, s));
+  MOE_RET(launch_route(cfg, x, w->router_w, w->correction_bias, logits, ids, tw, zw, reinterpret_cast<float*>(hist), s));
   MOE_HIP(moe::launch_permute(ids, P, c.router_width, counts, offsets, sorted_ids, inv_perm, hist, s));
   const void* a = x;
   const float* a_scales = nullptr;

@@ -7,11 +7,15 @@
 
 namespace moe {
 
-// a1 + a2: router logits and top-K selection
-hipError_t launch_router_logits(const uint16_t* x, const uint16_t* router_w, float* logits, int N, int H, int R,
-                                hipStream_t s);
-hipError_t launch_topk(const float* logits, const float* bias, int32_t* ids, float* w, float* zero_w, int N, int R,
-                       int E, int K, int scoring, int renormalize, float routed_scale, hipStream_t s);
+// a1 + a2: router logits (split over `slices` parts of H, each writing an [N, R]
+// partial plane) and top-K selection (adds the planes in order; when slices > 1
+// it also writes the summed logits to `logits`)
+int router_slices(int N, int H, int R);
+hipError_t launch_router_logits(const uint16_t* x, const uint16_t* router_w, float* part, int N, int H, int R,
+                                int slices, hipStream_t s);
+hipError_t launch_topk(const float* part, int slices, float* logits, const float* bias, int32_t* ids, float* w,
+                       float* zero_w, int N, int R, int E, int K, int scoring, int renormalize, float routed_scale,
+                       hipStream_t s);
 
 // a3: stable counting sort by expert; hist is [permute_chunks(P) * R] int32 scratch
 int permute_chunks(int P);

@@ -12,56 +12,84 @@
 namespace moe {
 
 // logits[N, R] = x[N, H] . router_w[R, H]^T on v_mfma_f32_16x16x32_bf16.
-// A block of 4 waves covers MT*16 tokens x 64 router columns; each wave owns
-// 16 columns and MT 16-row sub-tiles, so one B fragment feeds MT MFMAs.
-// Operand fragments are loaded straight from global memory (16 B per lane):
-// lane l holds row l%16 and the 8 consecutive k of chunk l/16 for both A and B,
-// which is a consistent k assignment for the dot product.  The router is
-// < 1% of the layer's work, so it does not stage through LDS.
-template <int MT>
+// A block of 4 waves computes a 32-token x 64-column tile over one slice of H
+// (split-K: blockIdx.z selects the slice; the host picks the number of slices
+// so that small batches still spread over the chip).  A and B are staged
+// through LDS 128 columns of H at a time, with the next slab's global loads in
+// flight during the MFMAs.  Wave w owns columns [16w, 16w+16) and both 16-row
+// halves.  Each slice writes its own partial [N, R] plane; the top-K kernel
+// adds the planes in slice order, so the sum order is fixed.
+constexpr int RT_BM = 32, RT_BN = 64, RT_BK = 128, RT_LDS = RT_BK + 8;  // bf16 elements per LDS row
+
 __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restrict__ x,
-                                                       const uint16_t* __restrict__ wr, float* __restrict__ logits,
-                                                       int N, int H, int R) {
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int m0 = blockIdx.x * (16 * MT);
-  const int ncol = blockIdx.y * 64 + wave * 16 + (lane % 16);
-  const int kofs = (lane / 16) * 8;
-  const bool nvalid = ncol < R;
-  const uint16_t* bp = wr + (size_t)(nvalid ? ncol : 0) * H + kofs;
-  const uint16_t* ap[MT];
-  bool avalid[MT];
+                                                       const uint16_t* __restrict__ wr, float* __restrict__ part,
+                                                       int N, int H, int R, int kslice) {
+  __shared__ __align__(16) uint16_t a_lds[RT_BM * RT_LDS];
+  __shared__ __align__(16) uint16_t b_lds[RT_BN * RT_LDS];
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int m0 = blockIdx.x * RT_BM, n0 = blockIdx.y * RT_BN;
+  const int k_begin = blockIdx.z * kslice;
+  // staging: row = tid / 16 (+16 i), 16-byte chunk = tid % 16
+  const int lrow = tid >> 4, lcol = (tid & 15) * 8;
+  const uint16_t* ap[2];
+  const uint16_t* bp[4];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    int row = m0 + mt * 16 + (lane % 16);
-    avalid[mt] = row < N;
-    ap[mt] = x + (size_t)(avalid[mt] ? row : 0) * H + kofs;
+  for (int i = 0; i < 2; ++i) {
+    int row = m0 + lrow + 16 * i;
+    row = row < N ? row : N - 1;  // clamp: extra rows are computed, never stored
+    ap[i] = x + (size_t)row * H + k_begin + lcol;
   }
-  f32x4 acc[MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  for (int k = 0; k < H; k += 64) {
-    u32x4 b0 = nvalid ? ld16(bp + k) : zero;
-    u32x4 b1 = nvalid ? ld16(bp + k + 32) : zero;
-    u32x4 a0[MT], a1[MT];
+  for (int i = 0; i < 4; ++i) {
+    int col = n0 + lrow + 16 * i;
+    col = col < R ? col : R - 1;
+    bp[i] = wr + (size_t)col * H + k_begin + lcol;
+  }
+  u32x4 ra[2], rb[4];
+  auto load = [&](int k) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      a0[mt] = avalid[mt] ? ld16(ap[mt] + k) : zero;
-      a1[mt] = avalid[mt] ? ld16(ap[mt] + k + 32) : zero;
+    for (int i = 0; i < 2; ++i) ra[i] = ldg16(ap[i] + k);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rb[i] = ldg16(bp[i] + k);
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) st16(a_lds + (lrow + 16 * i) * RT_LDS + lcol, ra[i]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st16(b_lds + (lrow + 16 * i) * RT_LDS + lcol, rb[i]);
+  };
+  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  const int frow = lane & 15, fk = (lane >> 4) * 8;
+  load(0);
+  store();
+  __syncthreads();
+  const int nk = kslice / RT_BK;
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk) load((kt + 1) * RT_BK);
+#pragma unroll
+    for (int kk = 0; kk < RT_BK; kk += 32) {
+      const u32x4 b = ld16(b_lds + (wave * 16 + frow) * RT_LDS + kk + fk);
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) {
+        const u32x4 a = ld16(a_lds + (mi * 16 + frow) * RT_LDS + kk + fk);
+        acc[mi] = mfma_16x16x32_bf16(a, b, acc[mi]);
+      }
     }
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      acc[mt] = mfma_16x16x32_bf16(a0[mt], b0, acc[mt]);
-      acc[mt] = mfma_16x16x32_bf16(a1[mt], b1, acc[mt]);
+    __syncthreads();
+    if (kt + 1 < nk) {
+      store();
+      __syncthreads();
     }
   }
   // D layout of the 16x16 MFMA: lane l, item r -> row 4*(l/16) + r, column l%16
+  float* out = part + (size_t)blockIdx.z * N * R;
+  const int col = n0 + wave * 16 + (lane & 15);
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+  for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      int row = m0 + mt * 16 + (lane / 16) * 4 + r;
-      if (row < N && nvalid) logits[(size_t)row * R + ncol] = acc[mt][r];
+      const int row = m0 + mi * 16 + (lane >> 4) * 4 + r;
+      if (row < N && col < R) out[(size_t)row * R + col] = acc[mi][r];
     }
 }
 
@@ -75,7 +103,8 @@ __device__ __forceinline__ uint32_t order_bits(float f) {
 }
 
 template <int MAXJ>
-__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, const float* __restrict__ bias,
+__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ part, int nslices,
+                                              float* __restrict__ logits, const float* __restrict__ bias,
                                               int32_t* __restrict__ ids, float* __restrict__ w,
                                               float* __restrict__ zero_w, int N, int R, int E, int K, int scoring,
                                               int renorm, float scale) {
@@ -83,17 +112,25 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int t = blockIdx.x * 4 + wave;
   if (t >= N) return;  // the whole wave leaves; no block barrier below
-  const float* lg = logits + (size_t)t * R;
+  // logits of this token: the split-K partial planes added in slice order
+  float v[MAXJ];
+#pragma unroll
+  for (int j = 0; j < MAXJ; ++j) {
+    const int r = lane + 64 * j;
+    if (r < R) {
+      float acc = part[(size_t)t * R + r];
+      for (int z = 1; z < nslices; ++z) acc += part[((size_t)z * N + t) * R + r];
+      v[j] = acc;
+      if (nslices > 1) logits[(size_t)t * R + r] = acc;
+    } else {
+      v[j] = -INFINITY;
+    }
+  }
   float p[MAXJ];
   if (scoring == 0) {
-    float v[MAXJ];
     float m = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < MAXJ; ++j) {
-      int r = lane + 64 * j;
-      v[j] = r < R ? lg[r] : -INFINITY;
-      m = fmaxf(m, v[j]);
-    }
+    for (int j = 0; j < MAXJ; ++j) m = fmaxf(m, v[j]);
     m = wave_max(m);
     float s = 0.f;
 #pragma unroll
@@ -108,7 +145,7 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
 #pragma unroll
     for (int j = 0; j < MAXJ; ++j) {
       int r = lane + 64 * j;
-      p[j] = r < R ? 1.0f / (1.0f + expf(-lg[r])) : 0.f;
+      p[j] = r < R ? 1.0f / (1.0f + expf(-v[j])) : 0.f;
     }
   }
   float sel[MAXJ];
@@ -157,31 +194,33 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
   if (lane == 0 && zero_w) zero_w[t] = zsum;
 }
 
-hipError_t launch_router_logits(const uint16_t* x, const uint16_t* router_w, float* logits, int N, int H, int R,
-                                hipStream_t s) {
+int router_slices(int N, int H, int R) {
+  const long tiles = (long)((N + RT_BM - 1) / RT_BM) * ((R + RT_BN - 1) / RT_BN);
+  int S = 1;
+  while (tiles * S < 256 && (H / 128) % (2 * S) == 0) S *= 2;
+  return S;
+}
+
+hipError_t launch_router_logits(const uint16_t* x, const uint16_t* router_w, float* part, int N, int H, int R,
+                                int slices, hipStream_t s) {
   if (N == 0) return hipSuccess;
-  dim3 block(256);
-  if (N >= 256) {
-    dim3 grid((N + 63) / 64, (R + 63) / 64);
-    k_router_logits<4><<<grid, block, 0, s>>>(x, router_w, logits, N, H, R);
-  } else {
-    dim3 grid((N + 15) / 16, (R + 63) / 64);
-    k_router_logits<1><<<grid, block, 0, s>>>(x, router_w, logits, N, H, R);
-  }
+  dim3 grid((N + RT_BM - 1) / RT_BM, (R + RT_BN - 1) / RT_BN, slices);
+  k_router_logits<<<grid, 256, 0, s>>>(x, router_w, part, N, H, R, H / slices);
   return hipGetLastError();
 }
 
-hipError_t launch_topk(const float* logits, const float* bias, int32_t* ids, float* w, float* zero_w, int N, int R,
-                       int E, int K, int scoring, int renormalize, float routed_scale, hipStream_t s) {
+hipError_t launch_topk(const float* part, int slices, float* logits, const float* bias, int32_t* ids, float* w,
+                       float* zero_w, int N, int R, int E, int K, int scoring, int renormalize, float routed_scale,
+                       hipStream_t s) {
   if (N == 0) return hipSuccess;
   dim3 grid((N + 3) / 4), block(256);
   const int maxj = (R + 63) / 64;
-#define MOE_TOPK_CASE(J)                                                                                 \
-  case J:                                                                                                \
-    k_topk<J><<<grid, block, 0, s>>>(logits, bias, ids, w, zero_w, N, R, E, K, scoring, renormalize,     \
-                                     routed_scale);                                                      \
+#define MOE_TOPK_CASE(J)                                                                                      \
+  case J:                                                                                                     \
+    k_topk<J><<<grid, block, 0, s>>>(part, slices, logits, bias, ids, w, zero_w, N, R, E, K, scoring,        \
+                                     renormalize, routed_scale);                                              \
     break;
-  switch (maxj) {
+  switch (maxj <= 6 ? maxj : (maxj <= 8 ? 8 : 16)) {
     MOE_TOPK_CASE(1)
     MOE_TOPK_CASE(2)
     MOE_TOPK_CASE(3)
@@ -190,13 +229,6 @@ hipError_t launch_topk(const float* logits, const float* bias, int32_t* ids, flo
     MOE_TOPK_CASE(6)
     MOE_TOPK_CASE(8)
     MOE_TOPK_CASE(16)
-    default:
-      if (maxj <= 8)
-        k_topk<8><<<grid, block, 0, s>>>(logits, bias, ids, w, zero_w, N, R, E, K, scoring, renormalize,
-                                         routed_scale);
-      else
-        k_topk<16><<<grid, block, 0, s>>>(logits, bias, ids, w, zero_w, N, R, E, K, scoring, renormalize,
-                                          routed_scale);
   }
 #undef MOE_TOPK_CASE
   return hipGetLastError();

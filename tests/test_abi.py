@@ -86,9 +86,11 @@ def _fake(addr=0x10000):
 def test_null_and_misaligned_pointers_are_refused():
     lib = moe.lib()
     c = _cfg()
-    st = lib.moe_route_topk(ctypes.byref(c), None, _fake(), None, _fake(), _fake(), _fake(), None, None)
+    st = lib.moe_route_topk(ctypes.byref(c), None, _fake(), None, _fake(), _fake(), _fake(), None, _fake(256),
+                            moe.moe_workspace_size(c), None)
     assert st == moe.MOE_ERR_INVALID and b"x is NULL" in lib.moe_last_error()
-    st = lib.moe_route_topk(ctypes.byref(c), _fake() + 2, _fake(), None, _fake(), _fake(), _fake(), None, None)
+    st = lib.moe_route_topk(ctypes.byref(c), _fake() + 2, _fake(), None, _fake(), _fake(), _fake(), None, _fake(256),
+                            moe.moe_workspace_size(c), None)
     assert st == moe.MOE_ERR_INVALID and b"aligned" in lib.moe_last_error()
     st = lib.moe_unpermute_reduce(ctypes.byref(c), _fake(), None, _fake(), _fake(), _fake(), None, _fake(), None)
     assert st == moe.MOE_ERR_INVALID and b"inv_perm" in lib.moe_last_error()

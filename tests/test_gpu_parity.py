@@ -105,7 +105,7 @@ def test_stages_match_oracle(name):
     # ---- route
     logits, ids, tw, zw = (_alloc((N, R), torch.float32), _alloc((N, K), torch.int32), _alloc((N, K), torch.float32),
                            _alloc((N,), torch.float32))
-    moe.moe_route_topk(cfg, dl.x, dl.router, dl.bias, logits, ids, tw, zw)
+    moe.moe_route_topk(cfg, dl.x, dl.router, dl.bias, logits, ids, tw, zw, ws)
     torch.cuda.synchronize()
     assert_close(f64(logits), res.logits, 1e-5, "logits")
     gids = ids.cpu().numpy()
@@ -279,7 +279,7 @@ def test_forward_matches_oracle_and_composed_stages(name):
     logits = s("logits")[:4 * N * R].view(torch.float32)
     ids = s("topk_ids")[:4 * P].view(torch.int32)
     tw = s("topk_w")[:4 * P].view(torch.float32)
-    moe.moe_route_topk(cfg, dl.x, dl.router, dl.bias, logits, ids, tw, s("zero_w")[:4 * N].view(torch.float32))
+    moe.moe_route_topk(cfg, dl.x, dl.router, dl.bias, logits, ids, tw, s("zero_w")[:4 * N].view(torch.float32), ws2)
     counts, offsets = s("counts")[:4 * R].view(torch.int32), s("offsets")[:4 * (R + 1)].view(torch.int32)
     sid, inv = s("sorted_ids")[:4 * P].view(torch.int32), s("inv_perm")[:4 * P].view(torch.int32)
     moe.moe_permute(cfg, ids, counts, offsets, sid, inv, ws2)
