@@ -51,6 +51,10 @@ struct GroupedGemmArgs {
   float* out_scales;   // fp8 gate/up only: [rows, I/128]
 };
 hipError_t launch_grouped_gemm_bf16(const GroupedGemmArgs& g, hipStream_t s);
+// bf16 streaming kernel for a few rows per expert (decode)
+bool decode_gemm_fits(const GroupedGemmArgs& g);
+hipError_t launch_grouped_gemm_decode(const GroupedGemmArgs& g, hipStream_t s);
+
 hipError_t launch_grouped_gemm_fp8(const GroupedGemmArgs& g, hipStream_t s);
 
 // a7: unpermute + weighted reduce + identity-expert and shared blends
