@@ -35,6 +35,10 @@ def parse():
                     help="distinct weight copies cycled through (0: enough to exceed the 256 MB MALL)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches only (no HIP graph replay)")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a plain device copy of this many bytes --steps times (the reference kernel for "
+                         "scaling the FETCH_SIZE / WRITE_SIZE counters), then exit")
     return ap.parse_args()
 
 
@@ -51,15 +55,25 @@ def main():
     import moe_inputs as mi
     import moe_inputs.device as mid
 
-    wl = mi.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_bytes:
+        src = torch.empty(args.copy_bytes, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.copy_bytes, "steps": args.steps}))
+        return
+    wl = mi.WORKLOADS[args.workload]
     N, H, E, R, K, I, Is = (wl.num_tokens, wl.hidden, wl.num_experts, wl.router_width, wl.top_k, wl.inter,
                             wl.shared_inter)
     fp8 = wl.weight_dtype == "fp8"
     wbytes = 1 if fp8 else 2
     layer_bytes = 3 * E * I * H * wbytes
-    n_layers = args.layers or max(1, min(8, int(np.ceil(1.0e9 / layer_bytes)) + 1))
+    # enough distinct weight copies that the touched experts of consecutive steps cannot be
+    # served from the 256 MB Infinity Cache (at least ~8 GB of weights in rotation, at most 8 copies)
+    n_layers = args.layers or max(2, min(8, int(np.ceil(8.0e9 / layer_bytes))))
     if layer_bytes * n_layers > 150e9:
         n_layers = max(1, int(150e9 // layer_bytes))
 
@@ -80,7 +94,7 @@ def main():
         dl, w = layers[i % n_layers]
         moe.moe_forward(cfg, w, dl.x, out, ws, stream)
 
-    # ---- whole-layer timing
+    # ---- whole-layer timing, eager launches
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -89,7 +103,33 @@ def main():
         step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms = (t1 - t0) * 1e3 / args.steps
+    ms_eager = (t1 - t0) * 1e3 / args.steps
+
+    # ---- the same steps replayed from HIP graphs (one captured moe_forward per weight copy), the way a
+    # serving loop runs a decode layer: the launches are the library's own, only host overhead goes away
+    ms_graph = None
+    if not args.no_graph:
+        graphs = []
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            for l in range(n_layers):
+                gph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gph, stream=cap):
+                    dl, w = layers[l]
+                    moe.moe_forward(cfg, w, dl.x, out, ws)
+                graphs.append(gph)
+        torch.cuda.synchronize()
+        for i in range(args.warmup):
+            graphs[i % n_layers].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            graphs[i % n_layers].replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ms_graph = (t1 - t0) * 1e3 / args.steps
+    ms = ms_graph if ms_graph is not None else ms_eager
 
     # ---- realised routing per layer (for the algorithmic bytes / flops)
     touched, rows_real = [], []
@@ -152,6 +192,8 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": ms,
         "us_per_layer": ms * 1e3,
+        "timing": "hip_graph_replay" if ms_graph is not None else "eager",
+        "ms_per_step_eager": ms_eager,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -385,8 +385,20 @@ moe_status_t moe_forward(const moe_config_t* cfg, const moe_weights_t* w, const 
   const bool fp8 = c.weight_dtype == MOE_WEIGHTS_FP8_E4M3;
   const int P = c.num_tokens * c.top_k;
 
-  MOE_RET(launch_route(cfg, x, w->router_w, w->correction_bias, logits, ids, tw, zw, reinterpret_cast<float*>(hist), s));
-  MOE_HIP(moe::launch_permute(ids, P, c.router_width, counts, offsets, sorted_ids, inv_perm, hist, s));
+  if (moe::topk_sort_small_fits(c.num_tokens, c.top_k)) {
+    // small batch: router GEMM, then top-K and the sort in one block
+    const int slices = moe::router_slices(c.num_tokens, c.hidden, c.router_width);
+    float* part = slices > 1 ? reinterpret_cast<float*>(hist) : logits;
+    MOE_HIP(moe::launch_router_logits(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w->router_w),
+                                      part, c.num_tokens, c.hidden, c.router_width, slices, s));
+    MOE_HIP(moe::launch_topk_sort_small(part, slices, logits, w->correction_bias, ids, tw, zw, counts, offsets,
+                                        sorted_ids, inv_perm, c.num_tokens, c.router_width, c.num_experts, c.top_k,
+                                        c.scoring, c.renormalize, c.routed_scale, s));
+  } else {
+    MOE_RET(launch_route(cfg, x, w->router_w, w->correction_bias, logits, ids, tw, zw, reinterpret_cast<float*>(hist),
+                         s));
+    MOE_HIP(moe::launch_permute(ids, P, c.router_width, counts, offsets, sorted_ids, inv_perm, hist, s));
+  }
   const void* a = x;
   const float* a_scales = nullptr;
   if (fp8) {

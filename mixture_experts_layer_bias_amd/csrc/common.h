@@ -52,27 +52,61 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
   return sign | code;
 }
 
+// Wave-wide reductions on DPP moves (no LDS round trips): an inclusive scan
+// inside each 16-lane row with row_shr 1, 2, 4, 8, then row_bcast:15 and
+// row_bcast:31 carry rows 0..2 into rows 1..3, so lane 63 holds the result,
+// which readlane broadcasts.  Lanes a DPP move cannot source keep the identity.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t identity, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)identity, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  const uint32_t id = __float_as_uint(-INFINITY);
+#define MOE_STEP(C, M) v = fmaxf(v, __uint_as_float(dpp_u32<C, M>(id, __float_as_uint(v))))
+  MOE_STEP(kDppRowShr1, 0xF);
+  MOE_STEP(kDppRowShr2, 0xF);
+  MOE_STEP(kDppRowShr4, 0xF);
+  MOE_STEP(kDppRowShr8, 0xF);
+  MOE_STEP(kDppRowBcast15, 0xA);
+  MOE_STEP(kDppRowBcast31, 0xC);
+#undef MOE_STEP
+  return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 63));
 }
 
+// Sum in a fixed lane order (deterministic).
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+#define MOE_STEP(C, M) v = v + __uint_as_float(dpp_u32<C, M>(0u, __float_as_uint(v)))
+  MOE_STEP(kDppRowShr1, 0xF);
+  MOE_STEP(kDppRowShr2, 0xF);
+  MOE_STEP(kDppRowShr4, 0xF);
+  MOE_STEP(kDppRowShr8, 0xF);
+  MOE_STEP(kDppRowBcast15, 0xA);
+  MOE_STEP(kDppRowBcast31, 0xC);
+#undef MOE_STEP
+  return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 63));
 }
 
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    uint32_t lo = __shfl_xor((uint32_t)v, o, kWave);
-    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, kWave);
-    uint64_t w = ((uint64_t)hi << 32) | lo;
-    v = w > v ? w : v;
+#define MOE_STEP(C, M)                                                   \
+  {                                                                      \
+    const uint32_t lo = dpp_u32<C, M>(0u, (uint32_t)v);                  \
+    const uint32_t hi = dpp_u32<C, M>(0u, (uint32_t)(v >> 32));          \
+    const uint64_t o = ((uint64_t)hi << 32) | lo;                        \
+    v = o > v ? o : v;                                                   \
   }
-  return v;
+  MOE_STEP(kDppRowShr1, 0xF);
+  MOE_STEP(kDppRowShr2, 0xF);
+  MOE_STEP(kDppRowShr4, 0xF);
+  MOE_STEP(kDppRowShr8, 0xF);
+  MOE_STEP(kDppRowBcast15, 0xA);
+  MOE_STEP(kDppRowBcast31, 0xC);
+#undef MOE_STEP
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, 63);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 // 16-byte load / store through a generic pointer (LDS or global, whichever the

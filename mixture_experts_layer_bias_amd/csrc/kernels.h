@@ -17,6 +17,13 @@ hipError_t launch_topk(const float* part, int slices, float* logits, const float
                        float* zero_w, int N, int R, int E, int K, int scoring, int renormalize, float routed_scale,
                        hipStream_t s);
 
+// a2 + a3 for small batches (N <= 64, N*K <= 1024): top-K and the stable sort in one block
+bool topk_sort_small_fits(int N, int K);
+hipError_t launch_topk_sort_small(const float* part, int slices, float* logits, const float* bias, int32_t* ids,
+                                  float* w, float* zero_w, int32_t* counts, int32_t* offsets, int32_t* sorted_ids,
+                                  int32_t* inv_perm, int N, int R, int E, int K, int scoring, int renormalize,
+                                  float routed_scale, hipStream_t s);
+
 // a3: stable counting sort by expert; hist is [permute_chunks(P) * R] int32 scratch
 int permute_chunks(int P);
 hipError_t launch_permute(const int32_t* ids, int P, int R, int32_t* counts, int32_t* offsets, int32_t* sorted_ids,

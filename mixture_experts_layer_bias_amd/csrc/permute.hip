@@ -103,7 +103,7 @@ __global__ __launch_bounds__(256) void k_perm_scatter(const int32_t* __restrict_
     uint64_t pending = __ballot(v >= 0);
     while (pending) {  // one pass per distinct id in this group of 64 rows (wave-uniform)
       const int leader = __ffsll((unsigned long long)pending) - 1;
-      const int lv = __shfl(v, leader, kWave);
+      const int lv = __builtin_amdgcn_readlane(v, leader);
       const uint64_t same = __ballot(v == lv);
       if (v == lv) {
         const int pos = cur[wave][lv] + __popcll(same & lt_mask);

@@ -102,24 +102,29 @@ __device__ __forceinline__ uint32_t order_bits(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Scores and top-K of token t for the calling wave.  p_w is this wave's LDS row
+// of MAXJ*64 floats.  Returns the wave's slot id (lane k holds slot k's column;
+// lanes >= K hold 0) after writing ids / w / zero_w for the token.
 template <int MAXJ>
-__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ part, int nslices,
-                                              float* __restrict__ logits, const float* __restrict__ bias,
-                                              int32_t* __restrict__ ids, float* __restrict__ w,
-                                              float* __restrict__ zero_w, int N, int R, int E, int K, int scoring,
-                                              int renorm, float scale) {
-  __shared__ float p_lds[4][MAXJ * 64];
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int t = blockIdx.x * 4 + wave;
-  if (t >= N) return;  // the whole wave leaves; no block barrier below
+__device__ __forceinline__ int topk_token(const float* __restrict__ part, int nslices, float* __restrict__ logits,
+                                          const float* __restrict__ bias, int32_t* __restrict__ ids,
+                                          float* __restrict__ w, float* __restrict__ zero_w, float* p_w, int t, int N,
+                                          int R, int E, int K, int scoring, int renorm, float scale) {
+  const int lane = threadIdx.x % kWave;
   // logits of this token: the split-K partial planes added in slice order
   float v[MAXJ];
 #pragma unroll
   for (int j = 0; j < MAXJ; ++j) {
     const int r = lane + 64 * j;
     if (r < R) {
-      float acc = part[(size_t)t * R + r];
-      for (int z = 1; z < nslices; ++z) acc += part[((size_t)z * N + t) * R + r];
+      // all planes are loaded before the (in-order) additions, so the loads overlap
+      float pl[16];
+#pragma unroll
+      for (int z = 0; z < 16; ++z) pl[z] = z < nslices ? part[((size_t)z * N + t) * R + r] : 0.f;
+      float acc = pl[0];
+#pragma unroll
+      for (int z = 1; z < 16; ++z)
+        if (z < nslices) acc += pl[z];
       v[j] = acc;
       if (nslices > 1) logits[(size_t)t * R + r] = acc;
     } else {
@@ -154,7 +159,7 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ part, in
   for (int j = 0; j < MAXJ; ++j) {
     int r = lane + 64 * j;
     if (r < R) {
-      p_lds[wave][r] = p[j];
+      p_w[r] = p[j];
       sel[j] = bias ? p[j] + bias[r] : p[j];
       avail |= 1u << j;
     } else {
@@ -179,7 +184,7 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ part, in
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  float my_p = lane < K ? p_lds[wave][my_id] : 0.f;
+  float my_p = lane < K ? p_w[my_id] : 0.f;
   float wk = my_p;
   if (renorm) {
     float tot = wave_sum(my_p);
@@ -192,12 +197,103 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ part, in
     w[(size_t)t * K + lane] = wk;
   }
   if (lane == 0 && zero_w) zero_w[t] = zsum;
+  return my_id;
+}
+
+template <int MAXJ>
+__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ part, int nslices,
+                                              float* __restrict__ logits, const float* __restrict__ bias,
+                                              int32_t* __restrict__ ids, float* __restrict__ w,
+                                              float* __restrict__ zero_w, int N, int R, int E, int K, int scoring,
+                                              int renorm, float scale) {
+  __shared__ float p_lds[4][MAXJ * 64];
+  const int wave = threadIdx.x / kWave;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= N) return;  // the whole wave leaves; no block barrier below
+  topk_token<MAXJ>(part, nslices, logits, bias, ids, w, zero_w, p_lds[wave], t, N, R, E, K, scoring, renorm, scale);
+}
+
+// Small batches (N <= 64, N*K <= 1024): top-K of every token and the stable
+// counting sort by expert in ONE block of 16 waves, so a decode step spends one
+// launch on both (same results as k_topk followed by the three sort passes).
+template <int MAXJ>
+__global__ __launch_bounds__(1024) void k_topk_sort_small(const float* __restrict__ part, int nslices,
+                                                         float* __restrict__ logits, const float* __restrict__ bias,
+                                                         int32_t* __restrict__ ids, float* __restrict__ w,
+                                                         float* __restrict__ zero_w, int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ sorted_ids,
+                                                         int32_t* __restrict__ inv_perm, int N, int R, int E, int K,
+                                                         int scoring, int renorm, float scale) {
+  __shared__ float p_lds[16][MAXJ * 64];
+  __shared__ int s_ids[1024];
+  __shared__ int s_cnt[16][1024];  // per-wave bucket counts, then per-wave cursors
+  __shared__ int s_scan[1024];
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int P = N * K;
+  for (int i = tid; i < 16 * R; i += 1024) s_cnt[i / R][i % R] = 0;
+  for (int t = wave; t < N; t += 16) {
+    const int my_id = topk_token<MAXJ>(part, nslices, logits, bias, ids, w, zero_w, p_lds[wave], t, N, R, E, K,
+                                       scoring, renorm, scale);
+    if (lane < K) s_ids[t * K + lane] = my_id;
+  }
+  __syncthreads();
+  // one expanded row per thread, in order: wave w holds rows 64w .. 64w+63
+  const int v = tid < P ? s_ids[tid] : -1;
+  if (v >= 0) atomicAdd(&s_cnt[wave][v], 1);
+  __syncthreads();
+  // bucket totals (thread r owns bucket r) -> exclusive scan over buckets: a wave-level
+  // inclusive scan on DPP, then the 16 wave totals added in order
+  int total = 0;
+  if (tid < R)
+    for (int ww = 0; ww < 16; ++ww) total += s_cnt[ww][tid];
+  int incl = total;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int x = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += x;
+  }
+  if (lane == kWave - 1) s_scan[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int ww = 0; ww < wave; ++ww) before += s_scan[ww];
+  incl += before;
+  if (tid < R) {
+    const int excl = incl - total;
+    counts[tid] = total;
+    offsets[tid] = excl;
+    int run = excl;
+    for (int ww = 0; ww < 16; ++ww) {
+      const int c = s_cnt[ww][tid];
+      s_cnt[ww][tid] = run;
+      run += c;
+    }
+    if (tid == R - 1) offsets[R] = incl;
+  }
+  __syncthreads();
+  // stable rank inside the wave: one ballot pass per distinct id (the leader's id is
+  // read with readlane: the loop is wave-uniform)
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int base = v >= 0 ? s_cnt[wave][v] : 0;  // this wave's cursor for my bucket
+  int rank = 0;
+  uint64_t pending = __ballot(v >= 0);
+  while (pending) {
+    const int leader = __ffsll((unsigned long long)pending) - 1;
+    const int lv = __builtin_amdgcn_readlane(v, leader);
+    const uint64_t same = __ballot(v == lv);
+    if (v == lv) rank = __popcll(same & lt_mask);
+    pending &= ~same;
+  }
+  if (v >= 0) {
+    sorted_ids[base + rank] = tid;
+    inv_perm[tid] = base + rank;
+  }
 }
 
 int router_slices(int N, int H, int R) {
   const long tiles = (long)((N + RT_BM - 1) / RT_BM) * ((R + RT_BN - 1) / RT_BN);
   int S = 1;
-  while (tiles * S < 256 && (H / 128) % (2 * S) == 0) S *= 2;
+  while (tiles * S < 256 && S < 16 && (H / 128) % (2 * S) == 0) S *= 2;  // topk adds at most 16 planes
   return S;
 }
 
@@ -231,6 +327,30 @@ hipError_t launch_topk(const float* part, int slices, float* logits, const float
     MOE_TOPK_CASE(16)
   }
 #undef MOE_TOPK_CASE
+  return hipGetLastError();
+}
+
+bool topk_sort_small_fits(int N, int K) { return N <= 64 && N * K <= 1024; }
+
+hipError_t launch_topk_sort_small(const float* part, int slices, float* logits, const float* bias, int32_t* ids,
+                                  float* w, float* zero_w, int32_t* counts, int32_t* offsets, int32_t* sorted_ids,
+                                  int32_t* inv_perm, int N, int R, int E, int K, int scoring, int renormalize,
+                                  float routed_scale, hipStream_t s) {
+  if (N == 0) return hipSuccess;
+  const int maxj = (R + 63) / 64;
+#define MOE_SMALL_CASE(J)                                                                                      \
+  case J:                                                                                                      \
+    k_topk_sort_small<J><<<1, 1024, 0, s>>>(part, slices, logits, bias, ids, w, zero_w, counts, offsets,        \
+                                            sorted_ids, inv_perm, N, R, E, K, scoring, renormalize, routed_scale); \
+    break;
+  switch (maxj <= 2 ? maxj : (maxj <= 4 ? 4 : (maxj <= 6 ? 6 : 16))) {
+    MOE_SMALL_CASE(1)
+    MOE_SMALL_CASE(2)
+    MOE_SMALL_CASE(4)
+    MOE_SMALL_CASE(6)
+    MOE_SMALL_CASE(16)
+  }
+#undef MOE_SMALL_CASE
   return hipGetLastError();
 }
 

@@ -386,3 +386,28 @@ def test_full_size_matches_oracle(name):
     res = ow.run(wl, tokens=toks, inputs=host)
     assert np.array_equal(res.ids, gids[toks])
     assert_close(f64(out)[toks], res.out_f64, _tol(wl), f"{name} sampled outputs")
+
+
+def test_forward_replays_from_a_hip_graph():
+    """moe_forward captured into a graph: every replay equals the eager result,
+    with eager work and synchronisations between replays."""
+    wl = SMALL["decode"]
+    dl = mi.device.device_layer(wl)
+    cfg, w = config_of(wl), weights_of(dl)
+    ref, ws = run_forward(cfg, w, dl.x)
+    torch.cuda.synchronize()
+    out = torch.empty_like(ref)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            moe.moe_forward(cfg, w, dl.x, out, ws)
+    torch.cuda.synchronize()
+    for i in range(3):
+        out.fill_(0)
+        junk = torch.randn(1024, 1024, device="cuda") @ torch.randn(1024, 1024, device="cuda")  # eager work
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"replay {i}"
+        del junk
