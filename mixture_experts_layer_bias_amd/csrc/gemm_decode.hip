@@ -8,18 +8,18 @@
 // With one to a few rows per expert the layer is bound by reading the touched
 // experts' weights from HBM, so the kernel is built to keep many bytes in
 // flight: a 4-stage LDS ring filled by direct global -> LDS loads
-// (global_load_lds_dwordx4, 16 bytes per lane, whole 128-byte row segments),
-// three K steps of loads ahead of the MFMAs, and two blocks per CU (the ring is
-// the block's only LDS; the tile scheduler's scratch is aliased onto it).
-// Tile: 32 sorted rows x 128 weight rows (gate/up: 64 output columns of gate
-// and the same 64 of up; down: 128 output columns), K step = 64 bf16.  Each wave owns all 32 rows and 32 weight rows
-// (gate/up: 16 columns of gate + the same 16 of up) as 2 x 2 tiles of
-// v_mfma_f32_16x16x32_bf16.  Chunk c of LDS row r is stored at chunk
-// c ^ (r & 7), since the DMA writes rows unpadded in lane order.
+// (global_load_lds_dwordx4, 16 bytes per lane) of whole row segments, three K
+// steps of loads ahead of the MFMAs, and two blocks per CU (the ring is the
+// block's only LDS; the tile scheduler's scratch and the epilogue's partial
+// sums are aliased onto it).  Each weight row is read in 256-byte segments
+// where K is long (gate/up), which streams faster than 128-byte ones.  Chunk c
+// of LDS row r is stored at 16-byte slot c ^ (r % (segment / 16)), since the
+// loads write rows unpadded in lane order.
 //
 // Waits are explicit (vmcnt of this wave's own loads, then a plain s_barrier):
 // a __syncthreads would wait for every stage still in flight.
 #include "common.h"
+#include "dma.h"
 #include "gemm_common.h"
 #include "kernels.h"
 
@@ -27,64 +27,70 @@ namespace moe {
 
 namespace {
 
-constexpr int DC_BM = 32;
-constexpr int DC_BNB = 128;
-constexpr int DC_ROWB = 128;  // bytes per row per K step
-constexpr int DC_ABYTES = DC_BM * DC_ROWB;    // 4 KB: 1 DMA instruction per wave
-constexpr int DC_BBYTES = DC_BNB * DC_ROWB;   // 16 KB: 4 per wave
-constexpr int DC_STAGE = DC_ABYTES + DC_BBYTES;
-constexpr int DC_NSTAGE = 4;  // 80 KB: two blocks per CU, so every tile of a decode layer is resident
-constexpr int DC_VM = 5;  // DMA instructions per wave per stage
+// Tile shapes.  Both move 20 KB per stage (A: BM x ROWB = 4 KB, one load instruction per
+// wave; B: BNB x ROWB = 16 KB, four per wave), so the ring and the waits are shared.
+//   gate/up (K = H, long): 16 rows x 64 weight rows x 256-byte segments; wave w computes the
+//     32-wide k slice w of every step for the whole tile (partial sums added in the epilogue).
+//   down (K = I, short):   32 rows x 128 weight rows x 128-byte segments (half as many tiles,
+//     so a decode layer's tiles are all resident); wave w owns weight rows 32w .. 32w+31.
+constexpr int DC_STAGE = 20480;
+constexpr int DC_NSTAGE = 4;  // 80 KB: two blocks per CU
+constexpr int DC_VM = 5;      // load instructions per wave per stage
 
-typedef const void __attribute__((address_space(1)))* gptr_t;
-typedef void __attribute__((address_space(3)))* lptr_t;
-
-__device__ __forceinline__ void dma16(const void* src, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)lds_wave_base, 16, 0, 0);
-}
-
-// s_waitcnt vmcnt(N) lgkmcnt(0)
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt(0x0070 | (N & 0xF) | ((N >> 4) << 14));
-}
+template <int STAGE>
+struct DecodeShape;
+template <>
+struct DecodeShape<0> {
+  static constexpr int BM = 16, BNB = 64, ROWB = 256, WK = 4;
+};
+template <>
+struct DecodeShape<1> {
+  static constexpr int BM = 32, BNB = 128, ROWB = 128, WK = 1;
+};
 
 // wait until at most `stages_after` later stages (DC_VM loads each) are still in flight
 __device__ __forceinline__ void wait_stages(int stages_after) {
   static_assert(DC_NSTAGE == 4, "one case per possible count of later stages");
   switch (stages_after) {
-    case 0: wait_vm<0>(); break;
-    case 1: wait_vm<1 * DC_VM>(); break;
-    default: wait_vm<2 * DC_VM>(); break;
+    case 0: dma_wait<0>(); break;
+    case 1: dma_wait<1 * DC_VM>(); break;
+    default: dma_wait<2 * DC_VM>(); break;
   }
-}
-
-__device__ __forceinline__ u32x4 lds_chunk(const uint8_t* base, int row, int chunk) {
-  return *reinterpret_cast<const u32x4*>(base + row * DC_ROWB + ((chunk ^ (row & 7)) << 4));
 }
 
 __device__ __forceinline__ float silu_d(float g) { return g / (1.0f + __expf(-g)); }
 
 template <int STAGE>
-__global__ __launch_bounds__(256, 1) void k_grouped_gemm_decode(GroupedGemmArgs g) {
+__global__ __launch_bounds__(256, 2) void k_grouped_gemm_decode(GroupedGemmArgs g) {
+  using S = DecodeShape<STAGE>;
+  constexpr int BM = S::BM, BNB = S::BNB, ROWB = S::ROWB, WK = S::WK, WN = 4 / WK;
+  constexpr int ABYTES = BM * ROWB;
+  constexpr int LPR = ROWB / 16;          // lanes per row in one load instruction
+  constexpr int RPI = 64 / LPR;           // rows per load instruction
+  constexpr int NSUB = ROWB / 64;         // 32-wide k slices per K step
+  constexpr int MT = BM / 16;             // 16-row MFMA blocks
+  constexpr int NTW = BNB / WN / 16;      // 16-wide weight blocks per wave
+  constexpr int SUBW = NSUB / WK;         // k slices per wave per step
+  static_assert(ABYTES == 4096 && BNB * ROWB == 16384 && ABYTES + BNB * ROWB == DC_STAGE, "stage layout");
+  static_assert(WK == 1 || 4 * BNB * BM * 4 <= DC_NSTAGE * DC_STAGE, "epilogue partial sums fit in the ring");
+
   extern __shared__ __align__(16) uint8_t smem[];  // DC_NSTAGE * DC_STAGE bytes
-  int* s_prefix = reinterpret_cast<int*>(smem);     // scheduler scratch, dead before the first DMA
+  int* s_prefix = reinterpret_cast<int*>(smem);     // scheduler scratch, dead before the first load
   int* s_wsum = s_prefix + kMaxGroups + 1;
 
   const int KD = STAGE == 0 ? g.H : g.I;
   const int NCOLS = STAGE == 0 ? g.I : g.H;
-  const int COLS_PER_TILE = STAGE == 0 ? DC_BNB / 2 : DC_BNB;
+  const int COLS_PER_TILE = STAGE == 0 ? BNB / 2 : BNB;
   const int NT = NCOLS / COLS_PER_TILE;
-  const TileCoord tc = schedule_tile(g.offsets, g.shared ? 1 : g.E, g.shared ? g.N : -1, DC_BM, NT, s_prefix, s_wsum);
+  const TileCoord tc = schedule_tile(g.offsets, g.shared ? 1 : g.E, g.shared ? g.N : -1, BM, NT, s_prefix, s_wsum);
   if (tc.expert < 0) return;  // the same decision in every thread of the block
-  __syncthreads();               // every wave is done with the scheduler scratch before the DMA reuses it
+  __syncthreads();               // every wave is done with the scheduler scratch before the loads reuse it
 
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int n0 = tc.n_tile * COLS_PER_TILE;
   const size_t row_bytes = (size_t)KD * 2;
-  const int nk = KD / 64;
+  const int nk = KD / (ROWB / 2);
 
   const uint8_t *wa, *wb = nullptr;
   if (STAGE == 0) {
@@ -94,47 +100,60 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_decode(GroupedGemmArgs 
     wa = static_cast<const uint8_t*>(g.shared ? g.sh_down : g.w_down[tc.expert]);
   }
 
-  // DMA sources.  A: wave w fills tile rows 8w..8w+7; B: instruction i of wave w fills
-  // weight rows (4w + i) * 8 + lane / 8 (gate/up: rows 0..63 gate, 64..127 up).
-  const int prow = lane >> 3, pch = lane & 7;
+  // Load sources.  One instruction writes RPI rows x ROWB bytes; lane l covers row l / LPR
+  // of its group and 16-byte slot l % LPR, i.e. logical chunk (l % LPR) ^ (row % LPR).
+  // A: wave w fills tile rows RPI w ..; B: instruction i of wave w fills weight rows
+  // RPI (4w + i) .. (gate/up: the first BNB / 2 rows gate, the rest up).
+  const int prow = lane / LPR, pslot = lane % LPR;
   const uint8_t* a_ptr;
   {
-    const int trow = wave * 8 + prow;
+    const int trow = wave * RPI + prow;
     int p = tc.row0 + trow;
     if (p >= tc.row_end) p = tc.row_end - 1;  // rows past the segment are computed, never stored
     long arow;
     if (STAGE == 0) arow = g.shared ? p : g.sorted_ids[p] / g.K;
     else arow = p;
-    a_ptr = static_cast<const uint8_t*>(g.a) + (size_t)arow * row_bytes + ((pch ^ (trow & 7)) << 4);
+    a_ptr = static_cast<const uint8_t*>(g.a) + (size_t)arow * row_bytes + ((pslot ^ (trow % LPR)) << 4);
   }
   const uint8_t* b_ptr[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int trow = (wave * 4 + i) * 8 + prow;
+    const int trow = (wave * 4 + i) * RPI + prow;
     const uint8_t* base;
-    if (STAGE == 0) base = trow < 64 ? wa + (size_t)(n0 + trow) * row_bytes : wb + (size_t)(n0 + trow - 64) * row_bytes;
-    else base = wa + (size_t)(n0 + trow) * row_bytes;
-    b_ptr[i] = base + ((pch ^ (trow & 7)) << 4);
+    if (STAGE == 0)
+      base = trow < BNB / 2 ? wa + (size_t)(n0 + trow) * row_bytes : wb + (size_t)(n0 + trow - BNB / 2) * row_bytes;
+    else
+      base = wa + (size_t)(n0 + trow) * row_bytes;
+    b_ptr[i] = base + ((pslot ^ (trow % LPR)) << 4);
   }
   auto issue = [&](int stage, int kstep) {
     uint8_t* sa = smem + stage * DC_STAGE;
-    uint8_t* sb = sa + DC_ABYTES;
-    const size_t koff = (size_t)kstep * DC_ROWB;
+    uint8_t* sb = sa + ABYTES;
+    const size_t koff = (size_t)kstep * ROWB;
     dma16(a_ptr + koff, sa + wave * 1024);
 #pragma unroll
     for (int i = 0; i < 4; ++i) dma16(b_ptr[i] + koff, sb + (wave * 4 + i) * 1024);
   };
+  auto lds_chunk = [&](const uint8_t* base, int row, int chunk) {
+    return *reinterpret_cast<const u32x4*>(base + row * ROWB + ((chunk ^ (row % LPR)) << 4));
+  };
 
-  // weight rows of this wave's two fragments
-  const int frow = lane & 15, fq = lane >> 4;  // 16x16x32 operand: row l%16, 8-element chunk l/16
-  const int br0 = STAGE == 0 ? wave * 16 + frow : wave * 32 + frow;
-  const int br1 = STAGE == 0 ? 64 + wave * 16 + frow : wave * 32 + 16 + frow;
-
-  f32x4 acc[2][2];
+  // this wave's weight blocks and k slices
+  const int wn = wave % WN, wk = wave / WN;
+  auto wrow0 = [&](int j) {  // first weight row of block j
+    if (STAGE == 0) {
+      const int half = j / (NTW / 2), idx = j % (NTW / 2);  // gate blocks, then the matching up blocks
+      return half * (BNB / 2) + wn * (BNB / 2 / WN) + idx * 16;
+    }
+    return wn * (BNB / WN) + j * 16;
+  };
+  // 16x16x32 operands: lane l holds row l % 16, 8-element chunk 4 s + l / 16 of k slice s
+  const int frow = lane & 15, fq = lane >> 4;
+  f32x4 acc[MT][NTW];
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int mi = 0; mi < MT; ++mi)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) acc[mi][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NTW; ++j) acc[mi][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
   for (int s = 0; s < DC_NSTAGE - 1; ++s)
@@ -147,40 +166,71 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_decode(GroupedGemmArgs 
     __builtin_amdgcn_sched_barrier(0);
     if (k + DC_NSTAGE - 1 < nk) issue((k + DC_NSTAGE - 1) % DC_NSTAGE, k + DC_NSTAGE - 1);
     const uint8_t* sa = smem + (k % DC_NSTAGE) * DC_STAGE;
-    const uint8_t* sb = sa + DC_ABYTES;
+    const uint8_t* sb = sa + ABYTES;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {  // 32-element k steps: logical chunk 4j + l/16
-      const int ch = 4 * j + fq;
-      const u32x4 b0 = lds_chunk(sb, br0, ch), b1 = lds_chunk(sb, br1, ch);
+    for (int u = 0; u < SUBW; ++u) {
+      const int ch = 4 * (wk * SUBW + u) + fq;
+      u32x4 b[NTW];
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi) {
+      for (int j = 0; j < NTW; ++j) b[j] = lds_chunk(sb, wrow0(j) + frow, ch);
+#pragma unroll
+      for (int mi = 0; mi < MT; ++mi) {
         const u32x4 a = lds_chunk(sa, mi * 16 + frow, ch);
-        acc[mi][0] = mfma_16x16x32_bf16(a, b0, acc[mi][0]);
-        acc[mi][1] = mfma_16x16x32_bf16(a, b1, acc[mi][1]);
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) acc[mi][j] = mfma_16x16x32_bf16(a, b[j], acc[mi][j]);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // epilogue.  16x16 D layout: lane l, item r -> row 4*(l/16) + r, column l%16
+  // epilogue.  16x16 D layout: lane l, item r -> row 16 mi + 4 (l / 16) + r, column l % 16 of the block
   uint16_t* out = static_cast<uint16_t*>(g.out);
+  if (WK == 1) {  // every wave holds whole sums for its weight blocks
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+    for (int mi = 0; mi < MT; ++mi)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = tc.row0 + mi * 16 + 4 * fq + r;
-      if (row >= tc.row_end) continue;
-      if (STAGE == 0) {
-        const int col = n0 + wave * 16 + frow;
-        out[(size_t)row * NCOLS + col] = (uint16_t)f32_to_bf16(silu_d(acc[mi][0][r]) * acc[mi][1][r]);
-      } else {
+      for (int r = 0; r < 4; ++r) {
+        const int row = tc.row0 + mi * 16 + 4 * fq + r;
+        if (row >= tc.row_end) continue;
+        if (STAGE == 0) {
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const int col = n0 + wave * 32 + nb * 16 + frow;
-          out[(size_t)row * NCOLS + col] = (uint16_t)f32_to_bf16(acc[mi][nb][r]);
+          for (int idx = 0; idx < NTW / 2; ++idx) {
+            const int col = n0 + wn * (BNB / 2 / WN) + idx * 16 + frow;
+            out[(size_t)row * NCOLS + col] =
+                (uint16_t)f32_to_bf16(silu_d(acc[mi][idx][r]) * acc[mi][NTW / 2 + idx][r]);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < NTW; ++j) {
+            const int col = n0 + wn * (BNB / WN) + j * 16 + frow;
+            out[(size_t)row * NCOLS + col] = (uint16_t)f32_to_bf16(acc[mi][j][r]);
+          }
         }
       }
+  } else {  // WN == 1: the waves' partial sums meet in LDS and are added in wave order
+    __syncthreads();  // the ring is free once every wave is past its last read
+    float* part = reinterpret_cast<float*>(smem);  // [wave][tile row][weight row]
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+      for (int j = 0; j < NTW; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) part[(wave * BM + mi * 16 + 4 * fq + r) * BNB + j * 16 + frow] = acc[mi][j][r];
+    __syncthreads();
+    auto sum4 = [&](int row, int wr) {
+      float v = part[row * BNB + wr];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) v += part[(w * BM + row) * BNB + wr];
+      return v;
+    };
+    constexpr int OC = STAGE == 0 ? BNB / 2 : BNB;  // output columns of the tile
+    for (int o = tid; o < BM * OC; o += 256) {
+      const int row = o / OC, col = o % OC;
+      if (tc.row0 + row >= tc.row_end) continue;
+      const float v = STAGE == 0 ? silu_d(sum4(row, col)) * sum4(row, BNB / 2 + col) : sum4(row, col);
+      out[(size_t)(tc.row0 + row) * NCOLS + n0 + col] = (uint16_t)f32_to_bf16(v);
     }
+  }
 }
 
 template <int STAGE>
@@ -192,7 +242,8 @@ hipError_t launch_decode(const GroupedGemmArgs& g, int groups, int rows, int nt,
     if (e != hipSuccess) return e;
     configured = true;
   }
-  k_grouped_gemm_decode<STAGE><<<grouped_grid(rows, groups, DC_BM, nt), 256, DC_NSTAGE * DC_STAGE, s>>>(g);
+  k_grouped_gemm_decode<STAGE>
+      <<<grouped_grid(rows, groups, DecodeShape<STAGE>::BM, nt), 256, DC_NSTAGE * DC_STAGE, s>>>(g);
   return hipGetLastError();
 }
 
@@ -201,15 +252,18 @@ hipError_t launch_decode(const GroupedGemmArgs& g, int groups, int rows, int nt,
 bool decode_gemm_fits(const GroupedGemmArgs& g) {
   const int groups = g.shared ? 1 : g.E;
   const int rows = g.shared ? g.N : g.P;
-  const bool few_rows = rows <= 8L * groups && rows <= 512;  // about one 32-row tile per touched expert
-  return few_rows && (g.stage == 0 ? g.I % 64 == 0 : g.H % 128 == 0);
+  const bool few_rows = rows <= 8L * groups && rows <= 512;  // about one row tile per touched expert
+  if (!few_rows) return false;
+  return g.stage == 0 ? (g.H % 128 == 0 && g.I % (DecodeShape<0>::BNB / 2) == 0)
+                      : (g.I % 64 == 0 && g.H % DecodeShape<1>::BNB == 0);
 }
 
 hipError_t launch_grouped_gemm_decode(const GroupedGemmArgs& g, hipStream_t s) {
   const int groups = g.shared ? 1 : g.E;
   const int rows = g.shared ? g.N : g.P;
   if (rows == 0) return hipSuccess;
-  return g.stage == 0 ? launch_decode<0>(g, groups, rows, g.I / 64, s) : launch_decode<1>(g, groups, rows, g.H / 128, s);
+  return g.stage == 0 ? launch_decode<0>(g, groups, rows, g.I / (DecodeShape<0>::BNB / 2), s)
+                      : launch_decode<1>(g, groups, rows, g.H / DecodeShape<1>::BNB, s);
 }
 
 }  // namespace moe

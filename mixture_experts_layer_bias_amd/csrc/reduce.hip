@@ -9,9 +9,11 @@
 
 namespace moe {
 
-constexpr int kMaxTopK = 32;
-
-// One block per token; threads stride over 8-column (16-byte) chunks of H.
+// One block per token; threads stride over 8-column (16-byte) chunks of H.  A
+// thread issues the loads of all K slot rows (and of x and the shared output)
+// of a chunk before its first add, so a chunk costs one memory round trip; the
+// adds then run in slot order.  KB >= K.
+template <int KB>
 __global__ __launch_bounds__(256) void k_unpermute_reduce(const uint16_t* __restrict__ y,
                                                           const int32_t* __restrict__ inv_perm,
                                                           const int32_t* __restrict__ ids,
@@ -19,53 +21,52 @@ __global__ __launch_bounds__(256) void k_unpermute_reduce(const uint16_t* __rest
                                                           const uint16_t* __restrict__ x,
                                                           const uint16_t* __restrict__ shared_y,
                                                           uint16_t* __restrict__ out, int H, int K, int E) {
-  __shared__ int rows[kMaxTopK];
-  __shared__ float wk[kMaxTopK];
-  __shared__ float zero_s;
+  __shared__ int rows[KB];
+  __shared__ float wk[KB];
   const int t = blockIdx.x;
   if (threadIdx.x < K) {
     const int id = ids[(size_t)t * K + threadIdx.x];
-    const bool real = id < E;
-    rows[threadIdx.x] = real ? inv_perm[(size_t)t * K + threadIdx.x] : -1;
+    rows[threadIdx.x] = id < E ? inv_perm[(size_t)t * K + threadIdx.x] : -1;
     wk[threadIdx.x] = w[(size_t)t * K + threadIdx.x];
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    float z = 0.f;
-    for (int k = 0; k < K; ++k)
-      if (rows[k] < 0) z += wk[k];
-    zero_s = z;
-  }
-  __syncthreads();
-  const float zero = zero_s;
+  float zero = 0.f;  // the identity experts' summed weight, added in slot order
+  for (int k = 0; k < K; ++k)
+    if (rows[k] < 0) zero += wk[k];
   const size_t xrow = (size_t)t * H;
+  const u32x4 z4 = {0u, 0u, 0u, 0u};
   for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
+    u32x4 v[KB];
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      const int r = k < K ? rows[k] : -1;
+      v[k] = r >= 0 ? ld16(y + (size_t)r * H + c) : z4;
+    }
+    const u32x4 xv = zero != 0.f ? ld16(x + xrow + c) : z4;
+    const u32x4 sv = shared_y ? ld16(shared_y + xrow + c) : z4;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < K; ++k) {
-      const int r = rows[k];
-      if (r < 0) continue;
-      const u32x4 v = ld16(y + (size_t)r * H + c);
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      if (k >= K || rows[k] < 0) continue;
       const float wv = wk[k];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        acc[2 * j] += wv * bf16_to_f32(v[j] & 0xFFFFu);
-        acc[2 * j + 1] += wv * bf16_to_f32(v[j] >> 16);
+        acc[2 * j] += wv * bf16_to_f32(v[k][j] & 0xFFFFu);
+        acc[2 * j + 1] += wv * bf16_to_f32(v[k][j] >> 16);
       }
     }
     if (zero != 0.f) {
-      const u32x4 v = ld16(x + xrow + c);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        acc[2 * j] += zero * bf16_to_f32(v[j] & 0xFFFFu);
-        acc[2 * j + 1] += zero * bf16_to_f32(v[j] >> 16);
+        acc[2 * j] += zero * bf16_to_f32(xv[j] & 0xFFFFu);
+        acc[2 * j + 1] += zero * bf16_to_f32(xv[j] >> 16);
       }
     }
     if (shared_y) {
-      const u32x4 v = ld16(shared_y + xrow + c);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        acc[2 * j] += bf16_to_f32(v[j] & 0xFFFFu);
-        acc[2 * j + 1] += bf16_to_f32(v[j] >> 16);
+        acc[2 * j] += bf16_to_f32(sv[j] & 0xFFFFu);
+        acc[2 * j + 1] += bf16_to_f32(sv[j] >> 16);
       }
     }
     u32x4 o;
@@ -79,7 +80,9 @@ hipError_t launch_unpermute_reduce(const uint16_t* y_sorted, const int32_t* inv_
                                    const float* w, const uint16_t* x, const uint16_t* shared_y, uint16_t* out, int N,
                                    int H, int K, int E, hipStream_t s) {
   if (N == 0) return hipSuccess;
-  k_unpermute_reduce<<<N, 256, 0, s>>>(y_sorted, inv_perm, ids, w, x, shared_y, out, H, K, E);
+  if (K <= 8) k_unpermute_reduce<8><<<N, 256, 0, s>>>(y_sorted, inv_perm, ids, w, x, shared_y, out, H, K, E);
+  else if (K <= 16) k_unpermute_reduce<16><<<N, 256, 0, s>>>(y_sorted, inv_perm, ids, w, x, shared_y, out, H, K, E);
+  else k_unpermute_reduce<32><<<N, 256, 0, s>>>(y_sorted, inv_perm, ids, w, x, shared_y, out, H, K, E);
   return hipGetLastError();
 }
 

@@ -93,13 +93,83 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restric
     }
 }
 
-// One wave per token: scores in fp32, then K rounds of a wave-wide arg-max on
-// a 64-bit key (order-preserving score bits, then the complement of the
-// column), so ties go to the lower column and slots come out in descending
-// order.  MAXJ = ceil(R/64) scores per lane.
+// Router logits for a handful of tokens (N <= RG_MAXN): one wave per router
+// column.  Lane l holds 16-byte chunks l, l + 64, ... of the column's weight
+// row and of each token's row; each lane adds its products in chunk order and
+// the wave adds the 64 lane sums on DPP, so the sum order is fixed.  The
+// logits come out whole (no split planes), and every load of a lane is issued
+// before its first multiply.
+constexpr int RG_MAXN = 8;
+
+__device__ __forceinline__ void bf16x8_to_f32(const u32x4& v, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(v[i] << 16);
+    f[2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
+  }
+}
+
+template <int NT, int G>  // NT >= N tokens, G chunks per lane in flight
+__global__ __launch_bounds__(256) void k_router_gemv(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+                                                     float* __restrict__ logits, int N, int H, int R) {
+  const int lane = threadIdx.x % kWave;
+  const int r = blockIdx.x * 4 + threadIdx.x / kWave;
+  if (r >= R) return;  // the whole wave leaves
+  const int nch = H / 8;
+  float acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = 0.f;
+  for (int c0 = lane; c0 < nch; c0 += G * kWave) {
+    u32x4 wv[G], xv[G][NT];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int c = c0 + g * kWave;
+      wv[g] = c < nch ? ldg16(wr + (size_t)r * H + c * 8) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        xv[g][t] = (c < nch && t < N) ? ldg16(x + (size_t)t * H + c * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float wf[8];
+      bf16x8_to_f32(wv[g], wf);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        float xf[8];
+        bf16x8_to_f32(xv[g][t], xf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[t] = fmaf(wf[e], xf[e], acc[t]);
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if (t < N) {  // uniform
+      const float s = wave_sum(acc[t]);
+      if (lane == 0) logits[(size_t)t * R + r] = s;
+    }
+  }
+}
+
+// One wave per token: scores in fp32, then K rounds of a wave-wide arg-max:
+// the largest order-preserving key of the selection scores (a DPP max), then a
+// ballot for the lowest column holding it, so ties go to the lower column and
+// slots come out in descending order.  MAXJ = ceil(R/64) scores per lane.
 __device__ __forceinline__ uint32_t order_bits(float f) {
   uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#define MOE_STEP(C, M) v = max(v, dpp_u32<C, M>(0u, v))
+  MOE_STEP(kDppRowShr1, 0xF);
+  MOE_STEP(kDppRowShr2, 0xF);
+  MOE_STEP(kDppRowShr4, 0xF);
+  MOE_STEP(kDppRowShr8, 0xF);
+  MOE_STEP(kDppRowBcast15, 0xA);
+  MOE_STEP(kDppRowBcast31, 0xC);
+#undef MOE_STEP
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
 // Scores and top-K of token t for the calling wave.  p_w is this wave's LDS row
@@ -166,19 +236,28 @@ __device__ __forceinline__ int topk_token(const float* __restrict__ part, int ns
       sel[j] = 0.f;
     }
   }
+  // K rounds: the largest key left, then the lowest column holding it (ties go to the
+  // lower column; the key order is the score order, so slots come out descending)
+  uint32_t key[MAXJ];
+#pragma unroll
+  for (int j = 0; j < MAXJ; ++j) key[j] = order_bits(sel[j]);
   int my_id = 0;
   for (int k = 0; k < K; ++k) {
-    uint64_t best = 0;
-#pragma unroll
-    for (int j = 0; j < MAXJ; ++j) {
-      uint64_t key = ((uint64_t)order_bits(sel[j]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)(lane + 64 * j));
-      if ((avail >> j) & 1u) best = key > best ? key : best;
-    }
-    best = wave_max_u64(best);
-    const int r_star = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFu));
+    uint32_t best = 0;
 #pragma unroll
     for (int j = 0; j < MAXJ; ++j)
-      if (lane + 64 * j == r_star) avail &= ~(1u << j);
+      if ((avail >> j) & 1u) best = key[j] > best ? key[j] : best;
+    best = wave_max_u32(best);
+    int r_star = 0;
+#pragma unroll
+    for (int j = 0; j < MAXJ; ++j) {
+      const uint64_t hit = __ballot(((avail >> j) & 1u) && key[j] == best);
+      if (hit) {  // uniform
+        r_star = 64 * j + (int)__builtin_ctzll(hit);
+        break;
+      }
+    }
+    if (lane == (r_star & 63)) avail &= ~(1u << (r_star >> 6));
     if (lane == k) my_id = r_star;
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -216,6 +295,8 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ part, in
 // Small batches (N <= 64, N*K <= 1024): top-K of every token and the stable
 // counting sort by expert in ONE block of 16 waves, so a decode step spends one
 // launch on both (same results as k_topk followed by the three sort passes).
+// Expanded row i of expert e lands at offsets[e] + (the number of rows j < i of
+// expert e), counted from LDS broadcast reads of the ids.
 template <int MAXJ>
 __global__ __launch_bounds__(1024) void k_topk_sort_small(const float* __restrict__ part, int nslices,
                                                          float* __restrict__ logits, const float* __restrict__ bias,
@@ -226,71 +307,58 @@ __global__ __launch_bounds__(1024) void k_topk_sort_small(const float* __restric
                                                          int32_t* __restrict__ inv_perm, int N, int R, int E, int K,
                                                          int scoring, int renorm, float scale) {
   __shared__ float p_lds[16][MAXJ * 64];
-  __shared__ int s_ids[1024];
-  __shared__ int s_cnt[16][1024];  // per-wave bucket counts, then per-wave cursors
-  __shared__ int s_scan[1024];
+  __shared__ __align__(16) int s_ids[1024];
+  __shared__ int s_off[1024];  // bucket counts, then bucket offsets
+  __shared__ int s_wsum[16];
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int P = N * K;
-  for (int i = tid; i < 16 * R; i += 1024) s_cnt[i / R][i % R] = 0;
+  if (tid < R) s_off[tid] = 0;
   for (int t = wave; t < N; t += 16) {
     const int my_id = topk_token<MAXJ>(part, nslices, logits, bias, ids, w, zero_w, p_lds[wave], t, N, R, E, K,
                                        scoring, renorm, scale);
     if (lane < K) s_ids[t * K + lane] = my_id;
   }
   __syncthreads();
-  // one expanded row per thread, in order: wave w holds rows 64w .. 64w+63
+  // one expanded row per thread, in order
   const int v = tid < P ? s_ids[tid] : -1;
-  if (v >= 0) atomicAdd(&s_cnt[wave][v], 1);
+  if (v >= 0) atomicAdd(&s_off[v], 1);
   __syncthreads();
-  // bucket totals (thread r owns bucket r) -> exclusive scan over buckets: a wave-level
-  // inclusive scan on DPP, then the 16 wave totals added in order
-  int total = 0;
-  if (tid < R)
-    for (int ww = 0; ww < 16; ++ww) total += s_cnt[ww][tid];
+  // exclusive scan over the buckets (thread b owns bucket b): a wave scan, then the
+  // wave totals added in order
+  const int total = tid < R ? s_off[tid] : 0;
   int incl = total;
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {
-    const int x = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += x;
+    const int xo = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += xo;
   }
-  if (lane == kWave - 1) s_scan[wave] = incl;
+  if (lane == kWave - 1) s_wsum[wave] = incl;
   __syncthreads();
   int before = 0;
-  for (int ww = 0; ww < wave; ++ww) before += s_scan[ww];
+  for (int ww = 0; ww < wave; ++ww) before += s_wsum[ww];
   incl += before;
   if (tid < R) {
-    const int excl = incl - total;
     counts[tid] = total;
-    offsets[tid] = excl;
-    int run = excl;
-    for (int ww = 0; ww < 16; ++ww) {
-      const int c = s_cnt[ww][tid];
-      s_cnt[ww][tid] = run;
-      run += c;
-    }
+    offsets[tid] = incl - total;
+    s_off[tid] = incl - total;
     if (tid == R - 1) offsets[R] = incl;
   }
   __syncthreads();
-  // stable rank inside the wave: one ballot pass per distinct id (the leader's id is
-  // read with readlane: the loop is wave-uniform)
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const int base = v >= 0 ? s_cnt[wave][v] : 0;  // this wave's cursor for my bucket
-  int rank = 0;
-  uint64_t pending = __ballot(v >= 0);
-  while (pending) {
-    const int leader = __ffsll((unsigned long long)pending) - 1;
-    const int lv = __builtin_amdgcn_readlane(v, leader);
-    const uint64_t same = __ballot(v == lv);
-    if (v == lv) rank = __popcll(same & lt_mask);
-    pending &= ~same;
-  }
   if (v >= 0) {
-    sorted_ids[base + rank] = tid;
-    inv_perm[tid] = base + rank;
+    int rank = 0, j = 0;
+    for (; j + 4 <= tid; j += 4) {
+      const int4 q = *reinterpret_cast<const int4*>(&s_ids[j]);
+      rank += (q.x == v) + (q.y == v) + (q.z == v) + (q.w == v);
+    }
+    for (; j < tid; ++j) rank += s_ids[j] == v;
+    const int pos = s_off[v] + rank;
+    sorted_ids[pos] = tid;
+    inv_perm[tid] = pos;
   }
 }
 
 int router_slices(int N, int H, int R) {
+  if (N <= RG_MAXN) return 1;  // the GEMV router writes whole logits
   const long tiles = (long)((N + RT_BM - 1) / RT_BM) * ((R + RT_BN - 1) / RT_BN);
   int S = 1;
   while (tiles * S < 256 && S < 16 && (H / 128) % (2 * S) == 0) S *= 2;  // topk adds at most 16 planes
@@ -300,6 +368,12 @@ int router_slices(int N, int H, int R) {
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* router_w, float* part, int N, int H, int R,
                                 int slices, hipStream_t s) {
   if (N == 0) return hipSuccess;
+  if (N <= RG_MAXN) {
+    const unsigned blocks = (unsigned)((R + 3) / 4);
+    if (N <= 4) k_router_gemv<4, 4><<<blocks, 256, 0, s>>>(x, router_w, part, N, H, R);
+    else k_router_gemv<8, 2><<<blocks, 256, 0, s>>>(x, router_w, part, N, H, R);
+    return hipGetLastError();
+  }
   dim3 grid((N + RT_BM - 1) / RT_BM, (R + RT_BN - 1) / RT_BN, slices);
   k_router_logits<<<grid, 256, 0, s>>>(x, router_w, part, N, H, R, H / slices);
   return hipGetLastError();

@@ -31,6 +31,8 @@ SMALL = {
     "k_equals_r": W("k_eq_r", 9, 128, 4, 4, 4, 128, 0, "softmax", True, 1.0, "bf16", False, seed=6),
     "one_expert": W("one_expert", 5, 128, 1, 1, 1, 128, 0, "softmax", True, 1.0, "bf16", False, seed=7),
     "many_tiles_300tok": W("tiles", 300, 256, 8, 8, 2, 384, 256, "softmax", True, 1.0, "bf16", False, seed=8),
+    # several 256-column gate/up and 512-column down tiles, ragged row tiles per expert
+    "wide_tiles_200tok": W("wide", 200, 1024, 8, 8, 2, 512, 0, "softmax", True, 1.0, "bf16", False, seed=12),
 }
 FP8_SMALL = {
     "fp8_sigmoid_bias_shared": W("fp8s", 33, 512, 8, 8, 2, 256, 128, "sigmoid", True, 2.5, "fp8", True, seed=9),
