@@ -31,10 +31,11 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}  # dense MFMA peaks
 MEASURED_TRAFFIC = {
     "decode_4tok_h2048_e128_top8_i768": {
         "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_decode.hip",
+                    "mixture_experts_layer_bias_amd/csrc/dma.h",
                     "mixture_experts_layer_bias_amd/csrc/gemm_common.h",
                     "mixture_experts_layer_bias_amd/csrc/common.h"],
-        "sha256": "3ce80cc51728a42501ff0549ed3325fa7137e78465f8036b1fa806df11ab0857",
-        "fetch_kib": 93327.67, "write_kib": 48.0, "fetch_scale": 2.0, "write_scale": 1.0,
+        "sha256": "ce42f5a540ac3494055cff0a5ffb616880b2485479bdd6127561eaf2002c9905",
+        "fetch_kib": 93346.44, "write_kib": 48.46, "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
 
