@@ -16,6 +16,7 @@
 // (one e4m3 scale group, the same recipe as moe_quantize_fp8), so h leaves the
 // kernel as e4m3 codes + one fp32 scale per 128 columns.
 #include "common.h"
+#include "dma.h"
 #include "gemm_common.h"
 #include "kernels.h"
 
@@ -243,12 +244,250 @@ __global__ __launch_bounds__(256, STAGE == 0 ? 1 : 2) void k_grouped_gemm_fp8(Gr
     }
 }
 
+// ---- streaming kernel for groups of up to a few hundred rows (the routed experts)
+//
+// There the GEMM is bound by streaming the weights from HBM, and the MFMAs and
+// the per-scale-block promotions must hide under that stream.  A tile spans a
+// whole group of up to 128 rows (each weight slab enters LDS once) and 256
+// weight rows (gate/up: 128 columns of gate and the same 128 of up, so the
+// tile's 128 h columns are one quantisation group; down: 256 output columns, two
+// weight-scale blocks).  K step = 128 bytes = one scale block.  The operands go
+// through a 3-stage LDS ring filled by direct global -> LDS loads, two steps
+// ahead of the MFMAs; the activation rows' scales of each step ride in the ring
+// (one 4-byte load per lane, 16 rows per wave), the tile's weight-block scales
+// are read into LDS once.  8 waves (two per SIMD, so one wave's promotions
+// overlap the other's MFMAs) in 2 x 4, each 64 rows x 2 blocks of 32 weight rows
+// (gate/up: one gate block and the matching up block; down: 64 columns); a
+// wave's block sums and accumulators stay in its VGPRs, so a promotion is one
+// FMA per value.  Chunk c of LDS row r sits at 16-byte slot c ^ (r % 8).
+constexpr int SBM = 128, SBNB = 256, SROWB = 128, SNSTAGE = 3, SWAVES = 8;
+constexpr int SABYTES = SBM * SROWB, SBBYTES = SBNB * SROWB;
+constexpr int SSTAGE = SABYTES + SBBYTES + SBM * 4;  // 48.5 KB
+constexpr int SVM = 2 + 4 + 1;                       // load instructions per wave per stage
+constexpr int SMAXKB = 64;                           // weight-scale blocks along K held in LDS (K <= 8192)
+constexpr int SLDS = SNSTAGE * SSTAGE + 2 * SMAXKB * 4;  // 146 KB: one block per CU
+
+template <int STAGE>
+__global__ __launch_bounds__(512, 1) void k_grouped_gemm_fp8_stream(GroupedGemmArgs g) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  int* s_prefix = reinterpret_cast<int*>(smem);  // scheduler scratch, dead before the first load
+  int* s_wsum = s_prefix + kMaxGroups + 1;
+  float* s_ws = reinterpret_cast<float*>(smem + SNSTAGE * SSTAGE);  // [2][SMAXKB] weight-block scales
+
+  const int KD = STAGE == 0 ? g.H : g.I;
+  const int NCOLS = STAGE == 0 ? g.I : g.H;
+  const int COLS = STAGE == 0 ? SBNB / 2 : SBNB;  // output columns per tile
+  const int NT = NCOLS / COLS;
+  const int KB = KD / 128;
+  const TileCoord tc =
+      schedule_tile(g.offsets, g.shared ? 1 : g.E, g.shared ? g.N : -1, SBM, NT, s_prefix, s_wsum);
+  if (tc.expert < 0) return;  // the same decision in every thread
+
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int n0 = tc.n_tile * COLS;
+
+  const uint8_t *wa, *wb = nullptr;
+  const float *sa_w, *sb_w = nullptr;
+  if (STAGE == 0) {
+    wa = static_cast<const uint8_t*>(g.shared ? g.sh_gate : g.w_gate[tc.expert]);
+    wb = static_cast<const uint8_t*>(g.shared ? g.sh_up : g.w_up[tc.expert]);
+    sa_w = g.shared ? g.sh_gate_s : g.s_gate[tc.expert];
+    sb_w = g.shared ? g.sh_up_s : g.s_up[tc.expert];
+  } else {
+    wa = static_cast<const uint8_t*>(g.shared ? g.sh_down : g.w_down[tc.expert]);
+    sa_w = g.shared ? g.sh_down_s : g.s_down[tc.expert];
+  }
+  __syncthreads();  // every wave is done with the scheduler scratch before the loads reuse it
+  // weight-block scales ([NCOLS / 128, KB] grid) of the tile into LDS: gate/up: row 0 the gate
+  // block, row 1 the up block of the tile's 128 columns; down: the tile's two column blocks
+  if (tid < 2 * SMAXKB) {
+    const int which = tid / SMAXKB, kb = tid % SMAXKB;
+    if (kb < KB) {
+      const float* src = STAGE == 0 ? (which == 0 ? sa_w : sb_w) + (size_t)tc.n_tile * KB
+                                    : sa_w + (size_t)(2 * tc.n_tile + which) * KB;
+      s_ws[which * SMAXKB + kb] = ldg_f32(src + kb);
+    }
+  }
+
+  // load sources.  One 16-byte instruction writes 8 rows x 128 B; lane l covers row l / 8 of
+  // its group and slot l % 8, i.e. logical chunk (l % 8) ^ (row % 8).
+  const int prow = lane >> 3, lch = (lane & 7) ^ prow;
+  auto a_row = [&](int trow) -> long {  // source row of tile row trow (clamped into the segment)
+    int p = tc.row0 + trow;
+    if (p >= tc.row_end) p = tc.row_end - 1;  // rows past the segment are computed, never stored
+    return STAGE == 0 ? (g.shared ? p : g.sorted_ids[p] / g.K) : p;
+  };
+  const uint8_t* a_ptr[2];  // A: wave w fills tile rows 16 w .. 16 w + 15
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    a_ptr[i] = static_cast<const uint8_t*>(g.a) + (size_t)a_row(wave * 16 + 8 * i + prow) * KD + (lch << 4);
+  // B: wave w fills weight rows 32 w .. 32 w + 31 (gate/up: waves 0..3 gate, waves 4..7 up)
+  const uint8_t* b_ptr;
+  if (STAGE == 0) b_ptr = (wave < 4 ? wa : wb) + (size_t)(n0 + (wave & 3) * 32 + prow) * KD + (lch << 4);
+  else b_ptr = wa + (size_t)(n0 + wave * 32 + prow) * KD + (lch << 4);
+  // row scales: lanes 0..15 of wave w load the scale of tile row 16 w + lane
+  const float* sc_ptr = g.a_scales + (size_t)a_row(wave * 16 + (lane & 15)) * KB;
+
+  auto issue = [&](int buf, int kb) {
+    uint8_t* sa = smem + buf * SSTAGE;
+    uint8_t* sb = sa + SABYTES;
+    uint8_t* ss = sb + SBBYTES;
+    const size_t koff = (size_t)kb * SROWB;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma16(a_ptr[i] + koff, sa + (wave * 2 + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(b_ptr + (size_t)(8 * i) * KD + koff, sb + (wave * 4 + i) * 1024);
+    if (lane < 16)
+      __builtin_amdgcn_global_load_lds((dma_gptr_t)(sc_ptr + kb), (dma_lptr_t)(ss + wave * 64), 4, 0, 0);
+  };
+  auto lds16 = [&](const uint8_t* base, int row, int chunk) {
+    return *reinterpret_cast<const u32x4*>(base + row * SROWB + ((chunk ^ (row & 7)) << 4));
+  };
+
+  f32x16 acc[2][2], blk[2][2];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][nb][r] = 0.f;
+
+  // 32x32x64 operands: lane l holds row l % 32 and bytes 32 (l / 32) .. +31 of the 64-byte k slice;
+  // D: lane l, item r -> row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
+  const int frow = lane & 31, fh = lane >> 5;
+  auto item_row = [&](int r) { return 8 * (r / 4) + 4 * fh + (r % 4); };
+  // weight rows of block nb: gate/up nb 0 -> gate columns 32 wn, nb 1 -> the same up columns
+  // (LDS rows 128 + ...); down: 64 wn + 32 nb
+  auto brow = [&](int nb) { return STAGE == 0 ? nb * 128 + wn * 32 + frow : wn * 64 + nb * 32 + frow; };
+  // weight-scale row of block nb: gate/up: gate (0) or up (1); down: column block of 64 wn + 32 nb
+  const int ws_row0 = STAGE == 0 ? 0 : (wn * 64) / 128, ws_row1 = STAGE == 0 ? 1 : (wn * 64 + 32) / 128;
+
+#pragma unroll
+  for (int s = 0; s < SNSTAGE - 1; ++s)
+    if (s < KB) issue(s, s);
+
+  for (int kb = 0; kb < KB; ++kb) {
+    if (kb + 1 < KB) dma_wait<SVM>();  // step kb has landed (one later stage may still be in flight)
+    else dma_wait<0>();
+    __builtin_amdgcn_s_barrier();  // ... in every wave; every wave is done with step kb - 1
+    __builtin_amdgcn_sched_barrier(0);
+    if (kb + SNSTAGE - 1 < KB) issue((kb + SNSTAGE - 1) % SNSTAGE, kb + SNSTAGE - 1);
+    const uint8_t* sa = smem + (kb % SNSTAGE) * SSTAGE;
+    const uint8_t* sb = sa + SABYTES;
+    const float* ss = reinterpret_cast<const float*>(sb + SBBYTES);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {  // 64-byte k slices: logical chunks 4 ks + 2 (l / 32) and +1
+      const int c0 = 4 * ks + 2 * fh;
+      i32x8 af[2], bf[2];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) {
+        const int row = wm * 64 + mi * 32 + frow;
+        const u32x4 lo = lds16(sa, row, c0), hi = lds16(sa, row, c0 + 1);
+        af[mi] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      }
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const u32x4 lo = lds16(sb, brow(nb), c0), hi = lds16(sb, brow(nb), c0 + 1);
+        bf[nb] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      }
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          if (ks == 0) blk[mi][nb] = mfma_32x32x64_fp8(af[mi], bf[nb], f32x16{});
+          else blk[mi][nb] = mfma_32x32x64_fp8(af[mi], bf[nb], blk[mi][nb]);
+        }
+    }
+    // promote this scale block: acc += blk * (row scale * weight-block scale)
+    const float ws0 = s_ws[ws_row0 * SMAXKB + kb], ws1 = s_ws[ws_row1 * SMAXKB + kb];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {  // items 4 q .. 4 q + 3 are 4 consecutive rows
+        const f32x4 rs = *reinterpret_cast<const f32x4*>(ss + wm * 64 + mi * 32 + 8 * q + 4 * fh);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[mi][0][4 * q + j] += blk[mi][0][4 * q + j] * (rs[j] * ws0);
+          acc[mi][1][4 * q + j] += blk[mi][1][4 * q + j] * (rs[j] * ws1);
+        }
+      }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  if (STAGE == 1) {
+    uint16_t* out = static_cast<uint16_t*>(g.out);
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = tc.row0 + wm * 64 + mi * 32 + item_row(r);
+        if (row >= tc.row_end) continue;
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          out[(size_t)row * NCOLS + n0 + wn * 64 + nb * 32 + frow] = (uint16_t)f32_to_bf16(acc[mi][nb][r]);
+      }
+    return;
+  }
+
+  // gate/up epilogue: h = silu(g) * u, quantised per row over the tile's 128 columns
+  __syncthreads();  // the ring is free: s_amax is aliased onto it
+  float* s_amax = reinterpret_cast<float*>(smem);  // [wn][tile row]
+  float h[2][16];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      h[mi][r] = silu(acc[mi][0][r]) * acc[mi][1][r];
+      float m = fabsf(h[mi][r]);
+#pragma unroll
+      for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));  // the 32 lanes of this row
+      if (frow == 0) s_amax[wn * SBM + wm * 64 + mi * 32 + item_row(r)] = m;
+    }
+  __syncthreads();
+  uint8_t* out = static_cast<uint8_t*>(g.out);
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int trow = wm * 64 + mi * 32 + item_row(r);
+      const int row = tc.row0 + trow;
+      const float amax =
+          fmaxf(fmaxf(s_amax[trow], s_amax[SBM + trow]), fmaxf(s_amax[2 * SBM + trow], s_amax[3 * SBM + trow]));
+      const float inv = amax > 0.f ? 448.0f / amax : 1.0f;
+      if (row < tc.row_end) {
+        out[(size_t)row * NCOLS + n0 + wn * 32 + frow] = (uint8_t)f32_to_e4m3(h[mi][r] * inv);
+        if (wn == 0 && frow == 0) g.out_scales[(size_t)row * NT + tc.n_tile] = amax > 0.f ? amax / 448.0f : 1.0f;
+      }
+    }
+}
+
+template <int STAGE>
+hipError_t launch_stream(const GroupedGemmArgs& g, int groups, int rows, int nt, hipStream_t s) {
+  static bool configured = false;
+  if (!configured) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_grouped_gemm_fp8_stream<STAGE>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, SLDS);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  k_grouped_gemm_fp8_stream<STAGE><<<grouped_grid(rows, groups, SBM, nt), 512, SLDS, s>>>(g);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_grouped_gemm_fp8(const GroupedGemmArgs& g, hipStream_t s) {
   const int groups = g.shared ? 1 : g.E;
   const int rows = g.shared ? g.N : g.P;
   if (rows == 0) return hipSuccess;
+  // up to ~256 rows per group: weight streaming dominates (routed experts); larger groups are
+  // MFMA-heavy and take the register-staged kernel
+  const int kd = g.stage == 0 ? g.H : g.I;
+  if (rows <= 256L * groups && kd <= 128 * SMAXKB && (g.stage == 0 || g.H % SBNB == 0))
+    return g.stage == 0 ? launch_stream<0>(g, groups, rows, g.I / (SBNB / 2), s)
+                        : launch_stream<1>(g, groups, rows, g.H / SBNB, s);
   if (g.stage == 0) {
     const unsigned grid = grouped_grid(rows, groups, BM, g.I / BN);
     k_grouped_gemm_fp8<0><<<grid, 256, 0, s>>>(g);
