@@ -103,7 +103,7 @@ void compute_layout(const moe_config_t* c, moe_workspace_layout_t* L) {
   L->sorted_ids = take(P * 4);
   L->inv_perm = take(P * 4);
   const int slices = moe::router_slices((int)N, (int)H, (int)R);
-  const size_t hist_bytes = (size_t)moe::permute_chunks((int)P) * R * 4;
+  const size_t hist_bytes = ((size_t)moe::permute_chunks((int)P) + 1) * R * 4;  // chunk histograms + bucket totals
   const size_t part_bytes = slices > 1 ? (size_t)slices * N * R * 4 : 0;
   L->scratch = take(hist_bytes > part_bytes ? hist_bytes : part_bytes);
   L->xq = fp8 ? take(N * H) : none;

@@ -24,7 +24,7 @@ hipError_t launch_topk_sort_small(const float* part, int slices, float* logits, 
                                   int32_t* inv_perm, int N, int R, int E, int K, int scoring, int renormalize,
                                   float routed_scale, hipStream_t s);
 
-// a3: stable counting sort by expert; hist is [permute_chunks(P) * R] int32 scratch
+// a3: stable counting sort by expert; hist is [(permute_chunks(P) + 1) * R] int32 scratch
 int permute_chunks(int P);
 hipError_t launch_permute(const int32_t* ids, int P, int R, int32_t* counts, int32_t* offsets, int32_t* sorted_ids,
                           int32_t* inv_perm, int32_t* hist, hipStream_t s);

@@ -2,12 +2,15 @@
 // forward_prefill.rs page, moe_sort_by_expert: sorted_token_ids, expert_offsets
 // and token_to_perm (here sorted_ids, offsets and inv_perm).
 //
-// Three passes over chunks of kChunk expanded rows:
-//   count   - per-chunk histograms in LDS                    (one block per chunk)
-//   scan    - per-bucket exclusive prefix over chunks, then over buckets -> counts,
-//             offsets, and each chunk's starting cursor per bucket (one block)
-//   scatter - each wave ranks its 256 rows in order with ballots, so equal ids keep
-//             ascending expanded index (stable), and writes both permutations.
+// Three passes over chunks of kChunk expanded rows (one wave per 64 rows):
+//   count   - per-chunk histograms in LDS                        (one block per chunk)
+//   scan    - per bucket, the exclusive prefix of its counts over the chunks and the
+//             bucket total (one wave per bucket, a DPP scan across the chunks)
+//   scatter - every block turns the bucket totals into bucket offsets (a block scan;
+//             block 0 also writes counts and offsets), then each wave ranks its 64 rows:
+//             the lanes holding the same id are found with one ballot per id bit, so a
+//             row's rank among equal ids below it is a popcount, and equal ids keep
+//             ascending expanded index (stable).
 // Every step is integer arithmetic with a fixed order, so the result is the same
 // on every run.
 #include "common.h"
@@ -15,8 +18,9 @@
 
 namespace moe {
 
-constexpr int kChunk = 1024;     // expanded rows per chunk (4 waves x 256)
+constexpr int kChunk = 256;        // expanded rows per chunk (4 waves x 64)
 constexpr int kMaxBuckets = 1024;  // router width limit
+constexpr int kIdBits = 10;        // ids < kMaxBuckets
 
 int permute_chunks(int P) { return (P + kChunk - 1) / kChunk; }
 
@@ -25,109 +29,129 @@ __global__ __launch_bounds__(256) void k_perm_count(const int32_t* __restrict__ 
   __shared__ int h[kMaxBuckets];
   for (int r = threadIdx.x; r < R; r += 256) h[r] = 0;
   __syncthreads();
-  const int base = blockIdx.x * kChunk;
-#pragma unroll
-  for (int i = 0; i < kChunk / 256; ++i) {
-    int idx = base + i * 256 + threadIdx.x;
-    if (idx < P) {
-      const int id = ids[idx];
-      if ((unsigned)id < (unsigned)R) atomicAdd(&h[id], 1);  // an id outside [0, R) is dropped, never written
-    }
+  const int idx = blockIdx.x * kChunk + threadIdx.x;
+  if (idx < P) {
+    const int id = ids[idx];
+    if ((unsigned)id < (unsigned)R) atomicAdd(&h[id], 1);  // an id outside [0, R) is dropped, never written
   }
   __syncthreads();
   for (int r = threadIdx.x; r < R; r += 256) hist[(size_t)blockIdx.x * R + r] = h[r];
 }
 
-__global__ __launch_bounds__(1024) void k_perm_scan(int32_t* __restrict__ hist, int C, int R,
-                                                    int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
-  __shared__ int s[kMaxBuckets];
-  const int r = threadIdx.x;
-  int total = 0;
-  if (r < R)
-    for (int c = 0; c < C; ++c) {
-      int v = hist[(size_t)c * R + r];
-      hist[(size_t)c * R + r] = total;  // rows of bucket r in chunks before c
-      total += v;
+// inclusive wave scan (lane order)
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x % kWave;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int x = __shfl_up(v, o, kWave);
+    if (lane >= o) v += x;
+  }
+  return v;
+}
+
+// hist[c][r] <- rows of bucket r in chunks before c; totals[r] <- rows of bucket r
+__global__ __launch_bounds__(256) void k_perm_scan(int32_t* __restrict__ hist, int C, int R,
+                                                   int32_t* __restrict__ totals) {
+  const int lane = threadIdx.x % kWave;
+  const int r = blockIdx.x * 4 + threadIdx.x / kWave;
+  if (r >= R) return;  // the whole wave leaves
+  int carry = 0;
+  for (int c0 = 0; c0 < C; c0 += 4 * kWave) {  // four batches of 64 chunks in flight
+    int v[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int c = c0 + b * kWave + lane;
+      v[b] = c < C ? hist[(size_t)c * R + r] : 0;
     }
-  s[r] = r < R ? total : 0;
-  __syncthreads();
-  for (int off = 1; off < kMaxBuckets; off <<= 1) {
-    int v = r >= off ? s[r - off] : 0;
-    __syncthreads();
-    s[r] += v;
-    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int c = c0 + b * kWave + lane;
+      const int incl = wave_incl_scan(v[b]);
+      if (c < C) hist[(size_t)c * R + r] = carry + incl - v[b];
+      carry += __shfl(incl, kWave - 1, kWave);
+    }
   }
-  if (r < R) {
-    int excl = s[r] - total;
-    counts[r] = total;
-    offsets[r] = excl;
-    for (int c = 0; c < C; ++c) hist[(size_t)c * R + r] += excl;
-  }
-  if (r == R - 1) offsets[R] = s[r];  // rows with a valid id (P when every id is in range)
+  if (lane == 0) totals[r] = carry;
 }
 
 __global__ __launch_bounds__(256) void k_perm_scatter(const int32_t* __restrict__ ids, int P, int R,
-                                                      const int32_t* __restrict__ chunk_base,
+                                                      const int32_t* __restrict__ chunk_prefix,
+                                                      const int32_t* __restrict__ totals,
+                                                      int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                       int32_t* __restrict__ sorted_ids,
                                                       int32_t* __restrict__ inv_perm) {
-  __shared__ int cur[4][kMaxBuckets];
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  for (int i = threadIdx.x; i < 4 * kMaxBuckets; i += 256) (&cur[0][0])[i] = 0;
-  __syncthreads();
-  const int wbase = blockIdx.x * kChunk + wave * 256;
-  int my_id[4];
+  __shared__ int s_base[kMaxBuckets];  // bucket offsets, then this chunk's cursors
+  __shared__ int s_wcnt[4][kMaxBuckets];  // rows per bucket in each wave, then per-wave cursors
+  __shared__ int s_wsum[4];
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+
+  // bucket offsets: exclusive scan of the totals (each thread owns 4 consecutive buckets)
+  int t4[4], local = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int idx = wbase + i * 64 + lane;
-    const int id = idx < P ? ids[idx] : -1;
-    my_id[i] = (unsigned)id < (unsigned)R ? id : -1;
-    if (my_id[i] >= 0) atomicAdd(&cur[wave][my_id[i]], 1);
+  for (int j = 0; j < 4; ++j) {
+    const int r = tid * 4 + j;
+    t4[j] = r < R ? totals[r] : 0;
+    local += t4[j];
   }
+  const int incl = wave_incl_scan(local);
+  if (lane == kWave - 1) s_wsum[wave] = incl;
+  for (int i = tid; i < 4 * kMaxBuckets; i += 256) (&s_wcnt[0][0])[i] = 0;
   __syncthreads();
-  // per-wave starting cursors: chunk base + rows of the same bucket in earlier waves
-  for (int r = threadIdx.x; r < R; r += 256) {
-    int run = chunk_base[(size_t)blockIdx.x * R + r];
+  int run = incl - local;
+  for (int w = 0; w < wave; ++w) run += s_wsum[w];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = tid * 4 + j;
+    if (r < R) {
+      s_base[r] = run + chunk_prefix[(size_t)blockIdx.x * R + r];
+      if (blockIdx.x == 0) {
+        counts[r] = t4[j];
+        offsets[r] = run;
+        if (r == R - 1) offsets[R] = run + t4[j];  // rows with a valid id (P when every id is in range)
+      }
+    }
+    run += t4[j];
+  }
+
+  // this wave's row and its id
+  const int idx = blockIdx.x * kChunk + tid;
+  const int id = idx < P ? ids[idx] : -1;
+  const int v = (unsigned)id < (unsigned)R ? id : -1;
+  if (v >= 0) atomicAdd(&s_wcnt[wave][v], 1);
+  __syncthreads();
+  // per-wave cursors: the chunk cursor plus the rows of the same bucket in earlier waves
+  for (int r = tid; r < R; r += 256) {
+    int cur = s_base[r];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      int c = cur[w][r];
-      cur[w][r] = run;
-      run += c;
+      const int c = s_wcnt[w][r];
+      s_wcnt[w][r] = cur;
+      cur += c;
     }
   }
   __syncthreads();
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  // lanes holding the same id: agree on every id bit (invalid rows have no valid id)
+  uint64_t same = __ballot(v >= 0);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int idx = wbase + i * 64 + lane;
-    const int v = my_id[i];
-    uint64_t pending = __ballot(v >= 0);
-    while (pending) {  // one pass per distinct id in this group of 64 rows (wave-uniform)
-      const int leader = __ffsll((unsigned long long)pending) - 1;
-      const int lv = __builtin_amdgcn_readlane(v, leader);
-      const uint64_t same = __ballot(v == lv);
-      if (v == lv) {
-        const int pos = cur[wave][lv] + __popcll(same & lt_mask);
-        sorted_ids[pos] = idx;
-        inv_perm[idx] = pos;
-      }
-      __builtin_amdgcn_wave_barrier();
-      if (lane == leader) cur[wave][lv] += __popcll(same);
-      __builtin_amdgcn_wave_barrier();
-      pending &= ~same;
-    }
+  for (int b = 0; b < kIdBits; ++b) {
+    const uint64_t ones = __ballot(v >= 0 && ((v >> b) & 1));
+    same &= ((v >> b) & 1) ? ones : ~ones;
+  }
+  if (v >= 0) {
+    const uint64_t lt_mask = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    const int pos = s_wcnt[wave][v] + __popcll(same & lt_mask);
+    sorted_ids[pos] = idx;
+    inv_perm[idx] = pos;
   }
 }
 
 hipError_t launch_permute(const int32_t* ids, int P, int R, int32_t* counts, int32_t* offsets, int32_t* sorted_ids,
                           int32_t* inv_perm, int32_t* hist, hipStream_t s) {
   const int C = permute_chunks(P);
-  if (C > 0) {
-    k_perm_count<<<C, 256, 0, s>>>(ids, P, R, hist);
-  }
-  k_perm_scan<<<1, 1024, 0, s>>>(hist, C, R, counts, offsets);
-  if (C > 0) {
-    k_perm_scatter<<<C, 256, 0, s>>>(ids, P, R, hist, sorted_ids, inv_perm);
-  }
+  int32_t* totals = hist + (size_t)C * R;  // R more ints after the chunk histograms
+  if (C > 0) k_perm_count<<<C, 256, 0, s>>>(ids, P, R, hist);
+  k_perm_scan<<<(R + 3) / 4, 256, 0, s>>>(hist, C, R, totals);
+  k_perm_scatter<<<C > 0 ? C : 1, 256, 0, s>>>(ids, P, R, hist, totals, counts, offsets, sorted_ids, inv_perm);
   return hipGetLastError();
 }
 

@@ -179,6 +179,33 @@ def test_stages_match_oracle(name):
     assert_close(f64(out), res.out_f64, BF16_TOL, "unpermute-reduce output")
 
 
+@pytest.mark.parametrize("P,R,K", [(100_003, 1024, 1), (65_536, 7, 4), (2_560, 384, 10), (257, 128, 1), (1, 1, 1)])
+def test_permute_bit_exact_many_chunks(P, R, K):
+    """The stable sort by expert, bit for bit against numpy's stable argsort, at
+    sizes spanning many 256-row chunks, the widest router (1024 buckets, every id
+    bit in use), a ragged last chunk, a single row and a single bucket.  Ids are
+    Zipf-skewed so that some buckets are long and many are empty."""
+    print(f"\n[case] permute P={P} R={R} K={K}", flush=True)
+    N = (P + K - 1) // K
+    rng = np.random.default_rng(1000 + R)
+    w = 1.0 / np.arange(1, R + 1) ** 1.1
+    flat = rng.choice(R, size=N * K, p=w / w.sum()).astype(np.int32)
+    cfg = moe.make_config(N, 128, R, R, K, 128)
+    ids = torch.from_numpy(flat.reshape(N, K)).cuda()
+    Pn = N * K
+    counts, offsets = _alloc((R,), torch.int32), _alloc((R + 1,), torch.int32)
+    sorted_ids, inv_perm = _alloc((Pn,), torch.int32), _alloc((Pn,), torch.int32)
+    ws = _alloc(moe.moe_workspace_size(cfg), torch.uint8)
+    moe.moe_permute(cfg, ids, counts, offsets, sorted_ids, inv_perm, ws)
+    torch.cuda.synchronize()
+    c_, o_, s_, i_ = (t.cpu().numpy() for t in (counts, offsets, sorted_ids, inv_perm))
+    ref_c = np.bincount(flat, minlength=R)
+    assert np.array_equal(c_, ref_c)
+    assert np.array_equal(o_, np.concatenate([[0], np.cumsum(ref_c)]))
+    assert np.array_equal(s_, np.argsort(flat, kind="stable"))
+    assert np.array_equal(i_[s_], np.arange(Pn))
+
+
 # ============================================================================ fp8 stages
 
 def _dequant_dev(q: torch.Tensor, sc: torch.Tensor) -> np.ndarray:
