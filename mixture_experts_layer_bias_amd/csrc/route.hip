@@ -361,7 +361,7 @@ int router_slices(int N, int H, int R) {
   if (N <= RG_MAXN) return 1;  // the GEMV router writes whole logits
   const long tiles = (long)((N + RT_BM - 1) / RT_BM) * ((R + RT_BN - 1) / RT_BN);
   int S = 1;
-  while (tiles * S < 256 && S < 16 && (H / 128) % (2 * S) == 0) S *= 2;  // topk adds at most 16 planes
+  while (tiles * S < 1024 && S < 16 && (H / 128) % (2 * S) == 0) S *= 2;  // topk adds at most 16 planes
   return S;
 }
 
