@@ -33,11 +33,17 @@ SMALL = {
     "many_tiles_300tok": W("tiles", 300, 256, 8, 8, 2, 384, 256, "softmax", True, 1.0, "bf16", False, seed=8),
     # several 256-column gate/up and 512-column down tiles, ragged row tiles per expert
     "wide_tiles_200tok": W("wide", 200, 1024, 8, 8, 2, 512, 0, "softmax", True, 1.0, "bf16", False, seed=12),
+    # the widest router (1024 columns, 24 of them identity experts) and the largest top-K (32), softmax + bias
+    "max_width_k32": W("kmax", 40, 256, 1000, 1024, 32, 128, 0, "softmax", False, 1.0, "bf16", True, seed=13),
+    # one token (single-token decode) with a shared expert, sigmoid + bias, scaled weights
+    "single_token_shared": W("one_tok", 1, 512, 64, 64, 8, 256, 128, "sigmoid", True, 2.5, "bf16", True, seed=14),
 }
 FP8_SMALL = {
     "fp8_sigmoid_bias_shared": W("fp8s", 33, 512, 8, 8, 2, 256, 128, "sigmoid", True, 2.5, "fp8", True, seed=9),
     "fp8_ragged_70tok_e16_top4": W("fp8r", 70, 256, 16, 16, 4, 384, 0, "softmax", True, 1.0, "fp8", False, seed=10),
     "fp8_300tok_shared": W("fp8t", 300, 384, 8, 8, 3, 256, 256, "sigmoid", True, 2.5, "fp8", True, seed=11),
+    # H = 8320: beyond the streaming kernel's K limit (8192), 65 scale groups per token
+    "fp8_wide_hidden_8320": W("fp8h", 20, 8320, 4, 4, 2, 128, 0, "sigmoid", True, 2.5, "fp8", True, seed=15),
 }
 
 
