@@ -482,10 +482,11 @@ hipError_t launch_grouped_gemm_fp8(const GroupedGemmArgs& g, hipStream_t s) {
   const int groups = g.shared ? 1 : g.E;
   const int rows = g.shared ? g.N : g.P;
   if (rows == 0) return hipSuccess;
-  // up to ~256 rows per group: weight streaming dominates (routed experts); larger groups are
-  // MFMA-heavy and take the register-staged kernel
+  // up to ~256 rows per group weight streaming dominates (routed experts); the shared expert's
+  // gate/up (every token, one group) also runs faster on the streaming kernel, its down stage on
+  // the register-staged one
   const int kd = g.stage == 0 ? g.H : g.I;
-  if (rows <= 256L * groups && kd <= 128 * SMAXKB && (g.stage == 0 || g.H % SBNB == 0))
+  if ((rows <= 256L * groups || (g.shared && g.stage == 0)) && kd <= 128 * SMAXKB && (g.stage == 0 || g.H % SBNB == 0))
     return g.stage == 0 ? launch_stream<0>(g, groups, rows, g.I / (SBNB / 2), s)
                         : launch_stream<1>(g, groups, rows, g.H / SBNB, s);
   if (g.stage == 0) {
