@@ -235,13 +235,8 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_decode(GroupedGemmArgs 
 
 template <int STAGE>
 hipError_t launch_decode(const GroupedGemmArgs& g, int groups, int rows, int nt, hipStream_t s) {
-  static bool configured = false;
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_grouped_gemm_decode<STAGE>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, DC_NSTAGE * DC_STAGE);
-    if (e != hipSuccess) return e;
-    configured = true;
-  }
+  const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&k_grouped_gemm_decode<STAGE>), DC_NSTAGE * DC_STAGE);
+  if (e != hipSuccess) return e;
   k_grouped_gemm_decode<STAGE>
       <<<grouped_grid(rows, groups, DecodeShape<STAGE>::BM, nt), 256, DC_NSTAGE * DC_STAGE, s>>>(g);
   return hipGetLastError();

@@ -465,13 +465,8 @@ __global__ __launch_bounds__(512, 1) void k_grouped_gemm_fp8_stream(GroupedGemmA
 
 template <int STAGE>
 hipError_t launch_stream(const GroupedGemmArgs& g, int groups, int rows, int nt, hipStream_t s) {
-  static bool configured = false;
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_grouped_gemm_fp8_stream<STAGE>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, SLDS);
-    if (e != hipSuccess) return e;
-    configured = true;
-  }
+  const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&k_grouped_gemm_fp8_stream<STAGE>), SLDS);
+  if (e != hipSuccess) return e;
   k_grouped_gemm_fp8_stream<STAGE><<<grouped_grid(rows, groups, SBM, nt), 512, SLDS, s>>>(g);
   return hipGetLastError();
 }

@@ -7,6 +7,10 @@
 
 namespace moe {
 
+// Raise a kernel's dynamic LDS limit to `bytes` on the current device, once per (kernel, device);
+// thread-safe.  Kernels that use more than the default dynamic LDS call this before each launch.
+hipError_t ensure_dynamic_lds(const void* kernel, int bytes);
+
 // a1 + a2: router logits (split over `slices` parts of H, each writing an [N, R]
 // partial plane) and top-K selection (adds the planes in order; when slices > 1
 // it also writes the summed logits to `logits`)
