@@ -34,8 +34,8 @@ MEASURED_TRAFFIC = {
                     "mixture_experts_layer_bias_amd/csrc/dma.h",
                     "mixture_experts_layer_bias_amd/csrc/gemm_common.h",
                     "mixture_experts_layer_bias_amd/csrc/common.h"],
-        "sha256": "ce42f5a540ac3494055cff0a5ffb616880b2485479bdd6127561eaf2002c9905",
-        "fetch_kib": 93346.44, "write_kib": 48.46, "fetch_scale": 2.0, "write_scale": 1.0,
+        "sha256": "34c2f6889cfb2b1e742eb932b7bd36c91efef8017150cc4d193da1811e258142",
+        "fetch_kib": 93344.48, "write_kib": 48.55, "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
 
