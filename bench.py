@@ -6,9 +6,12 @@ over one batch of seeded synthetic tokens, with every input resident in HBM.
 Prints one JSON line.  The default workload is the decode layer (4 tokens,
 H 2048, 128 experts, top-8, I 768); --workload picks another.
 
-The dominant kernel (the routed gate/up grouped GEMM) is timed with HIP events
-recorded on the stream the library launches on, over the same kind of steps,
-and reported against the binding roofline.  The oracle (float64 numpy on the
+The dominant kernel is timed with HIP events recorded on the stream the
+library launches on, over the same kind of steps, and reported against the
+binding roofline: for a decode batch with bf16 weights and no shared expert,
+the one launch that runs the routed gate/up GEMM, the down GEMM and the
+unpermute-reduce (through moe_experts_forward); otherwise the routed gate/up
+grouped GEMM.  The oracle (float64 numpy on the
 host cores) is timed on a bounded sample of the same workload.
 """
 import argparse
@@ -33,6 +36,7 @@ MEASURED_TRAFFIC = {
         "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_decode.hip",
                     "mixture_experts_layer_bias_amd/csrc/dma.h",
                     "mixture_experts_layer_bias_amd/csrc/gemm_common.h",
+                    "mixture_experts_layer_bias_amd/csrc/unpermute.h",
                     "mixture_experts_layer_bias_amd/csrc/common.h"],
         "sha256": "34c2f6889cfb2b1e742eb932b7bd36c91efef8017150cc4d193da1811e258142",
         "fetch_kib": 93344.48, "write_kib": 48.55, "fetch_scale": 2.0, "write_scale": 1.0,
@@ -116,7 +120,8 @@ def main():
         w = moe.weights_from_stacked(dl.router, dl.bias, dl.gate, dl.up, dl.down, dl.gate_s, dl.up_s, dl.down_s,
                                      dl.sh_gate, dl.sh_up, dl.sh_down, dl.sh_gate_s, dl.sh_up_s, dl.sh_down_s)
         layers.append((dl, w))
-    ws = torch.empty(moe.moe_workspace_size(cfg), dtype=torch.uint8, device=dev)
+    # zeroed once: the decode experts path keeps its counters in the workspace and leaves them zero
+    ws = torch.zeros(moe.moe_workspace_size(cfg), dtype=torch.uint8, device=dev)
     out = torch.empty((N, H), dtype=torch.bfloat16, device=dev)
     L = moe.moe_workspace_layout(cfg)
     stream = torch.cuda.current_stream()
@@ -176,46 +181,60 @@ def main():
     e_t = float(np.mean(touched))
     p_r = float(np.mean(rows_real))
 
-    # ---- dominant kernel: the routed gate/up grouped GEMM, timed with events on the launch stream.
-    # The stage calls below reuse moe_forward's own intermediates in the workspace.
+    # ---- dominant kernel, timed with events on the launch stream.  The calls below reuse
+    # moe_forward's own routing and intermediates in the workspace (refreshed before every launch).
+    # A decode batch (bf16 weights, a few rows per touched expert, no shared expert) runs its experts
+    # as one launch: routed gate/up + SwiGLU, down and the unpermute-reduce.  Otherwise the routed
+    # gate/up grouped GEMM dominates.
+    P = N * K
+    one_launch = not fp8 and Is == 0 and P <= min(8 * E, 512) and H % 128 == 0 and I % 64 == 0
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     a_off = L["xq"] if fp8 else None
+    base = ws.data_ptr()
     for i in range(args.warmup + args.steps):
         dl, w = layers[i % n_layers]
         moe.moe_forward(cfg, w, dl.x, out, ws, stream)  # refreshes ids / offsets / quantised x for this batch
-        sid = ws.data_ptr() + L["sorted_ids"]
-        offs = L["offsets"] + ws.data_ptr()
-        a = dl.x if not fp8 else ws.data_ptr() + a_off
-        a_sc = None if not fp8 else ws.data_ptr() + L["x_scales"]
-        h = ws.data_ptr() + L["h"]
-        hs = None if not fp8 else ws.data_ptr() + L["h_scales"]
         if i >= args.warmup:
             ev[i - args.warmup][0].record(stream)
-        moe.moe_grouped_gemm(cfg, moe.MOE_STAGE_GATE_UP, moe.MOE_GROUP_ROUTED, w, a, a_sc, sid, offs, h, hs, ws,
-                             stream)
+        if one_launch:
+            moe.moe_experts_forward(cfg, w, dl.x, base + L["topk_ids"], base + L["topk_w"], base + L["offsets"],
+                                    base + L["sorted_ids"], base + L["inv_perm"], out, ws, stream)
+        else:
+            a = dl.x if not fp8 else base + a_off
+            a_sc = None if not fp8 else base + L["x_scales"]
+            hs = None if not fp8 else base + L["h_scales"]
+            moe.moe_grouped_gemm(cfg, moe.MOE_STAGE_GATE_UP, moe.MOE_GROUP_ROUTED, w, a, a_sc,
+                                 base + L["sorted_ids"], base + L["offsets"], base + L["h"], hs, ws, stream)
         if i >= args.warmup:
             ev[i - args.warmup][1].record(stream)
     torch.cuda.synchronize()
     k_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
-    # algorithmic bytes / flops of one gate/up launch
-    gu_weight_bytes = e_t * 2 * I * H * wbytes + (e_t * 2 * (I // 128) * (H // 128) * 4 if fp8 else 0)
-    gu_bytes = gu_weight_bytes + N * H * wbytes + p_r * I * wbytes
-    gu_flops = 4.0 * p_r * H * I
+    if one_launch:
+        # touched experts' gate, up and down weights, x read, out written (h and y are intermediates)
+        k_bytes = e_t * 3 * I * H * wbytes + 2 * N * H * 2
+        k_flops = 6.0 * p_r * H * I
+        k_name = "routed gate/up + SwiGLU, down, unpermute-reduce (one launch)"
+    else:
+        # touched experts' gate and up weights (+ block scales), x read, h written
+        k_bytes = (e_t * 2 * I * H * wbytes + (e_t * 2 * (I // 128) * (H // 128) * 4 if fp8 else 0)
+                   + N * H * wbytes + p_r * I * wbytes)
+        k_flops = 4.0 * p_r * H * I
+        k_name = "grouped gate/up + SwiGLU (routed)"
     # whole layer
     layer_flops = 2.0 * N * H * R + 6.0 * p_r * H * I + 6.0 * N * H * Is
     layer_bytes_alg = (e_t * 3 * I * H * wbytes + R * H * 2 + 2 * N * H * 2 + 3 * Is * H * wbytes)
-    ai = gu_flops / gu_bytes
+    ai = k_flops / k_bytes
     ridge = MFMA_PEAK_TFLOPS[wl.weight_dtype] * 1e12 / (HBM_PEAK_GBS * 1e9)
     if ai < ridge:
-        roof = {"bound": "hbm", "achieved": gu_bytes / (k_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+        roof = {"bound": "hbm", "achieved": k_bytes / (k_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     else:
-        roof = {"bound": "mfma", "achieved": gu_flops / (k_ms * 1e-3) / 1e12,
+        roof = {"bound": "mfma", "achieved": k_flops / (k_ms * 1e-3) / 1e12,
                 "peak": MFMA_PEAK_TFLOPS[wl.weight_dtype], "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = measured_traffic(wl.name)  # bytes per launch (HBM, counters), or null
-    roof["alg_bytes"] = gu_bytes
-    roof["kernel"] = "grouped gate/up + SwiGLU (routed)"
+    roof["alg_bytes"] = k_bytes
+    roof["kernel"] = k_name
     roof["kernel_us"] = k_ms * 1e3
 
     result = {

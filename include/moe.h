@@ -93,7 +93,7 @@ typedef struct {
   const float* sh_down_s; /* [H/128, Is/128] */
 } moe_weights_t;
 
-/* Bytes of device workspace that moe_forward and moe_permute need for `cfg`
+/* Bytes of device workspace that moe_forward, moe_experts_forward and moe_permute need for `cfg`
  * (a function of the sizes only; 256-byte aligned pieces). */
 moe_status_t moe_workspace_size(const moe_config_t* cfg, size_t* bytes);
 
@@ -185,12 +185,31 @@ moe_status_t moe_unpermute_reduce(const moe_config_t* cfg, const void* y_sorted,
 moe_status_t moe_forward(const moe_config_t* cfg, const moe_weights_t* w, const void* x, void* out, void* ws,
                          size_t ws_bytes, void* stream);
 
+/* The expert half of the layer for a routing computed elsewhere (moe_route_topk
+ * and moe_permute, or moe_forward's own): [quantise] -> gate/up (+ shared) ->
+ * down (+ shared) -> unpermute-reduce with the blends.  Same result as
+ * composing moe_quantize_fp8, moe_grouped_gemm and moe_unpermute_reduce.
+ * forward_prefill.rs page, run_routed_grouped_gemm, run_shared_expert_prefill
+ * and moe_unpermute_reduce_indexed; forward.rs page, apply_zero_expert.
+ * x [N, H] bf16; topk_ids, topk_w [N, K]; offsets [R + 1], sorted_ids [P],
+ * inv_perm [P] as moe_permute writes them; out [N, H] bf16.
+ * ws: at least moe_workspace_size(cfg) bytes.  With bf16 weights and a few rows
+ * per touched expert (decode) the routed GEMMs and the reduce run as one launch
+ * whose tiles wait on counters in the workspace's `sync` piece: that piece must
+ * hold zeros when the call starts.  Zero it once (e.g. zero the whole
+ * workspace after allocating it); every call of this library leaves it zero. */
+moe_status_t moe_experts_forward(const moe_config_t* cfg, const moe_weights_t* w, const void* x,
+                                 const int32_t* topk_ids, const float* topk_w, const int32_t* offsets,
+                                 const int32_t* sorted_ids, const int32_t* inv_perm, void* out, void* ws,
+                                 size_t ws_bytes, void* stream);
+
 /* Offsets of the intermediates inside the moe_forward workspace, so a caller
  * can inspect them after moe_forward (all in bytes from the workspace start;
- * a piece that the config does not use has offset SIZE_MAX). */
+ * a piece that the config does not use has offset SIZE_MAX).  `sync` holds the
+ * counters of the one-launch decode experts path (see moe_experts_forward). */
 typedef struct {
   size_t logits, topk_ids, topk_w, zero_w, counts, offsets, sorted_ids, inv_perm;
-  size_t xq, x_scales, h, h_scales, y, shared_h, shared_h_scales, shared_y, scratch, total;
+  size_t xq, x_scales, h, h_scales, y, shared_h, shared_h_scales, shared_y, scratch, sync, total;
 } moe_workspace_layout_t;
 moe_status_t moe_workspace_layout(const moe_config_t* cfg, moe_workspace_layout_t* layout);
 

@@ -28,7 +28,8 @@ MOE_STAGE_GATE_UP, MOE_STAGE_DOWN = 0, 1
 MOE_GROUP_ROUTED, MOE_GROUP_SHARED = 0, 1
 
 EXPORTED = ["moe_workspace_size", "moe_workspace_layout", "moe_route_topk", "moe_permute", "moe_quantize_fp8",
-            "moe_grouped_gemm", "moe_unpermute_reduce", "moe_forward", "moe_status_str", "moe_last_error"]
+            "moe_grouped_gemm", "moe_unpermute_reduce", "moe_forward", "moe_experts_forward", "moe_status_str",
+            "moe_last_error"]
 
 
 class MoeError(RuntimeError):
@@ -54,7 +55,7 @@ class moe_weights_t(ctypes.Structure):
 class moe_workspace_layout_t(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "logits", "topk_ids", "topk_w", "zero_w", "counts", "offsets", "sorted_ids", "inv_perm", "xq", "x_scales",
-        "h", "h_scales", "y", "shared_h", "shared_h_scales", "shared_y", "scratch", "total")]
+        "h", "h_scales", "y", "shared_h", "shared_h_scales", "shared_y", "scratch", "sync", "total")]
 
 
 _lib = None
@@ -78,6 +79,7 @@ def lib() -> ctypes.CDLL:
             "moe_grouped_gemm": [cfgp, i32, i32, ctypes.POINTER(moe_weights_t), vp, vp, vp, vp, vp, vp, vp, sz, vp],
             "moe_unpermute_reduce": [cfgp, vp, vp, vp, vp, vp, vp, vp, vp],
             "moe_forward": [cfgp, ctypes.POINTER(moe_weights_t), vp, vp, vp, sz, vp],
+            "moe_experts_forward": [cfgp, ctypes.POINTER(moe_weights_t), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -238,6 +240,15 @@ def moe_unpermute_reduce(cfg, y_sorted, inv_perm, topk_ids, topk_w, x, shared_y,
 def moe_forward(cfg, weights: LayerWeights, x, out, ws, stream=None) -> None:
     _check(lib().moe_forward(ctypes.byref(cfg), ctypes.byref(weights.struct), _ptr(x, "x", 2), _ptr(out, "out", 2),
                              _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_experts_forward(cfg, weights: LayerWeights, x, topk_ids, topk_w, offsets, sorted_ids, inv_perm, out, ws,
+                        stream=None) -> None:
+    _check(lib().moe_experts_forward(ctypes.byref(cfg), ctypes.byref(weights.struct), _ptr(x, "x", 2),
+                                     _ptr(topk_ids, "topk_ids", 4), _ptr(topk_w, "topk_w", 4),
+                                     _ptr(offsets, "offsets", 4), _ptr(sorted_ids, "sorted_ids", 4),
+                                     _ptr(inv_perm, "inv_perm", 4), _ptr(out, "out", 2), _ptr(ws, "ws"),
+                                     ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def weights_from_stacked(router_w, correction_bias, gate, up, down, gate_s=None, up_s=None, down_s=None,

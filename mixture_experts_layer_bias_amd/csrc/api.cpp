@@ -126,6 +126,7 @@ void compute_layout(const moe_config_t* c, moe_workspace_layout_t* L) {
   const size_t hist_bytes = ((size_t)moe::permute_chunks((int)P) + 1) * R * 4;  // chunk histograms + bucket totals
   const size_t part_bytes = slices > 1 ? (size_t)slices * N * R * 4 : 0;
   L->scratch = take(hist_bytes > part_bytes ? hist_bytes : part_bytes);
+  L->sync = take((size_t)moe::decode_fused_counters(c->num_experts, (int)H) * 4);
   L->xq = fp8 ? take(N * H) : none;
   L->x_scales = fp8 ? take(N * (H / 128) * 4) : none;
   L->h = take(P * I * (fp8 ? 1 : 2));
@@ -203,6 +204,61 @@ moe_status_t run_gemm(const moe_config_t* c, const moe::GroupedGemmArgs& g, hipS
     MOE_HIP(moe::launch_grouped_gemm_fp8(g, s));
   }
   return MOE_OK;
+}
+
+// Whether the decode experts path (routed gate/up, down and the reduce in one launch) applies.
+bool experts_fused(const moe_config_t* c) {
+  if (c->weight_dtype != MOE_WEIGHTS_BF16) return false;
+  const moe_weights_t none{};  // the fit is a function of the sizes only
+  const moe::GroupedGemmArgs gu = gemm_args(c, MOE_STAGE_GATE_UP, MOE_GROUP_ROUTED, &none, nullptr, nullptr,
+                                            nullptr, nullptr, nullptr, nullptr);
+  const moe::GroupedGemmArgs dn = gemm_args(c, MOE_STAGE_DOWN, MOE_GROUP_ROUTED, &none, nullptr, nullptr, nullptr,
+                                            nullptr, nullptr, nullptr);
+  return moe::decode_gemm_fits(gu) && moe::decode_gemm_fits(dn);
+}
+
+// The expert half of the layer given the routing: [quantise] -> gate/up (+ shared) -> down
+// (+ shared) -> unpermute-reduce.  With `fused` (the counters piece of the workspace holds zeros)
+// the routed GEMMs and the reduce run as one launch, after the shared expert, whose output the
+// reduce reads; that launch leaves the counters zero again.
+moe_status_t run_experts(const moe_config_t* cfg, const moe_weights_t* w, const void* x, const int32_t* ids,
+                         const float* tw, const int32_t* offsets, const int32_t* sorted_ids, const int32_t* inv_perm,
+                         void* out, const moe_workspace_layout_t& L, char* base, bool fused, hipStream_t s) {
+  const moe_config_t& c = *cfg;
+  auto at = [&](size_t off) -> void* { return off == SIZE_MAX ? nullptr : base + off; };
+  const bool fp8 = c.weight_dtype == MOE_WEIGHTS_FP8_E4M3;
+  if (fp8)
+    MOE_HIP(moe::launch_quant_fp8(static_cast<const uint16_t*>(x), static_cast<uint8_t*>(at(L.xq)),
+                                  static_cast<float*>(at(L.x_scales)), c.num_tokens, c.hidden, s));
+  const void* a = fp8 ? at(L.xq) : x;
+  const float* a_scales = fp8 ? static_cast<const float*>(at(L.x_scales)) : nullptr;
+  const moe::GroupedGemmArgs gu = gemm_args(cfg, MOE_STAGE_GATE_UP, MOE_GROUP_ROUTED, w, a, a_scales, sorted_ids,
+                                            offsets, at(L.h), static_cast<float*>(at(L.h_scales)));
+  const moe::GroupedGemmArgs dn = gemm_args(cfg, MOE_STAGE_DOWN, MOE_GROUP_ROUTED, w, at(L.h),
+                                            static_cast<float*>(at(L.h_scales)), sorted_ids, offsets, at(L.y), nullptr);
+  const moe::GroupedGemmArgs sh_gu = gemm_args(cfg, MOE_STAGE_GATE_UP, MOE_GROUP_SHARED, w, a, a_scales, nullptr,
+                                               nullptr, at(L.shared_h), static_cast<float*>(at(L.shared_h_scales)));
+  const moe::GroupedGemmArgs sh_dn = gemm_args(cfg, MOE_STAGE_DOWN, MOE_GROUP_SHARED, w, at(L.shared_h),
+                                               static_cast<float*>(at(L.shared_h_scales)), nullptr, nullptr,
+                                               at(L.shared_y), nullptr);
+  const moe::ReduceArgs red{inv_perm, ids, tw, static_cast<const uint16_t*>(x),
+                            static_cast<const uint16_t*>(at(L.shared_y)), static_cast<uint16_t*>(out),
+                            c.num_tokens, c.hidden, c.top_k, c.num_experts};
+  if (fused) {
+    if (c.shared_inter > 0) {
+      MOE_RET(run_gemm(cfg, sh_gu, s));
+      MOE_RET(run_gemm(cfg, sh_dn, s));
+    }
+    MOE_HIP(moe::launch_decode_fused(gu, dn, red, static_cast<int32_t*>(at(L.sync)), s));
+    return ok();
+  }
+  MOE_RET(run_gemm(cfg, gu, s));
+  if (c.shared_inter > 0) MOE_RET(run_gemm(cfg, sh_gu, s));
+  MOE_RET(run_gemm(cfg, dn, s));
+  if (c.shared_inter > 0) MOE_RET(run_gemm(cfg, sh_dn, s));
+  MOE_HIP(moe::launch_unpermute_reduce(static_cast<const uint16_t*>(at(L.y)), red.inv_perm, red.ids, red.w, red.x,
+                                       red.shared_y, red.out, red.N, red.H, red.K, red.E, s));
+  return ok();
 }
 
 moe_status_t launch_route(const moe_config_t* c, const void* x, const void* router_w, const float* bias,
@@ -405,51 +461,50 @@ moe_status_t moe_forward(const moe_config_t* cfg, const moe_weights_t* w, const 
   const bool fp8 = c.weight_dtype == MOE_WEIGHTS_FP8_E4M3;
   const int P = c.num_tokens * c.top_k;
 
-  if (moe::topk_sort_small_fits(c.num_tokens, c.top_k)) {
-    // small batch: router GEMM, then top-K and the sort in one block
+  int32_t* sync = static_cast<int32_t*>(at(L.sync));
+  // small batch: router GEMM, then top-K and the sort in one block, which also zeroes the counters
+  // of the one-launch decode experts path
+  const bool small = moe::topk_sort_small_fits(c.num_tokens, c.top_k);
+  const bool fused = small && experts_fused(cfg);
+  if (small) {
     const int slices = moe::router_slices(c.num_tokens, c.hidden, c.router_width);
     float* part = slices > 1 ? reinterpret_cast<float*>(hist) : logits;
     MOE_HIP(moe::launch_router_logits(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w->router_w),
                                       part, c.num_tokens, c.hidden, c.router_width, slices, s));
     MOE_HIP(moe::launch_topk_sort_small(part, slices, logits, w->correction_bias, ids, tw, zw, counts, offsets,
-                                        sorted_ids, inv_perm, c.num_tokens, c.router_width, c.num_experts, c.top_k,
-                                        c.scoring, c.renormalize, c.routed_scale, s));
+                                        sorted_ids, inv_perm, fused ? sync : nullptr,
+                                        moe::decode_fused_counters(c.num_experts, c.hidden), c.num_tokens,
+                                        c.router_width, c.num_experts, c.top_k, c.scoring, c.renormalize,
+                                        c.routed_scale, s));
   } else {
     MOE_RET(launch_route(cfg, x, w->router_w, w->correction_bias, logits, ids, tw, zw, reinterpret_cast<float*>(hist),
                          s));
     MOE_HIP(moe::launch_permute(ids, P, c.router_width, counts, offsets, sorted_ids, inv_perm, hist, s));
   }
-  const void* a = x;
-  const float* a_scales = nullptr;
-  if (fp8) {
-    MOE_HIP(moe::launch_quant_fp8(static_cast<const uint16_t*>(x), static_cast<uint8_t*>(at(L.xq)),
-                                  static_cast<float*>(at(L.x_scales)), c.num_tokens, c.hidden, s));
-    a = at(L.xq);
-    a_scales = static_cast<const float*>(at(L.x_scales));
-  }
-  MOE_RET(run_gemm(cfg,
-                   gemm_args(cfg, MOE_STAGE_GATE_UP, MOE_GROUP_ROUTED, w, a, a_scales, sorted_ids, offsets, at(L.h),
-                             static_cast<float*>(at(L.h_scales))),
-                   s));
-  if (c.shared_inter > 0)
-    MOE_RET(run_gemm(cfg,
-                     gemm_args(cfg, MOE_STAGE_GATE_UP, MOE_GROUP_SHARED, w, a, a_scales, nullptr, nullptr,
-                               at(L.shared_h), static_cast<float*>(at(L.shared_h_scales))),
-                     s));
-  MOE_RET(run_gemm(cfg,
-                   gemm_args(cfg, MOE_STAGE_DOWN, MOE_GROUP_ROUTED, w, at(L.h), static_cast<float*>(at(L.h_scales)),
-                             sorted_ids, offsets, at(L.y), nullptr),
-                   s));
-  if (c.shared_inter > 0)
-    MOE_RET(run_gemm(cfg,
-                     gemm_args(cfg, MOE_STAGE_DOWN, MOE_GROUP_SHARED, w, at(L.shared_h),
-                               static_cast<float*>(at(L.shared_h_scales)), nullptr, nullptr, at(L.shared_y), nullptr),
-                     s));
-  MOE_HIP(moe::launch_unpermute_reduce(static_cast<const uint16_t*>(at(L.y)), inv_perm, ids, tw,
-                                       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(at(L.shared_y)),
-                                       static_cast<uint16_t*>(out), c.num_tokens, c.hidden, c.top_k, c.num_experts,
-                                       s));
-  return ok();
+  return run_experts(cfg, w, x, ids, tw, offsets, sorted_ids, inv_perm, out, L, base, fused, s);
+}
+
+moe_status_t moe_experts_forward(const moe_config_t* cfg, const moe_weights_t* w, const void* x,
+                                 const int32_t* topk_ids, const float* topk_w, const int32_t* offsets,
+                                 const int32_t* sorted_ids, const int32_t* inv_perm, void* out, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  MOE_RET(check_config(cfg));
+  MOE_RET(check_weights(cfg, w));
+  moe_workspace_layout_t L;
+  compute_layout(cfg, &L);
+  MOE_CHECK(ws_bytes >= L.total, MOE_ERR_WORKSPACE, "workspace too small: need %zu bytes, have %zu", L.total,
+            ws_bytes);
+  if (cfg->num_tokens == 0) return ok();
+  MOE_RET(check_ptr(x, 16, "x"));
+  MOE_RET(check_ptr(topk_ids, 4, "topk_ids"));
+  MOE_RET(check_ptr(topk_w, 4, "topk_w"));
+  MOE_RET(check_ptr(offsets, 4, "offsets"));
+  MOE_RET(check_ptr(sorted_ids, 4, "sorted_ids"));
+  MOE_RET(check_ptr(inv_perm, 4, "inv_perm"));
+  MOE_RET(check_ptr(out, 16, "out"));
+  MOE_RET(check_ptr(ws, 256, "ws"));
+  return run_experts(cfg, w, x, topk_ids, topk_w, offsets, sorted_ids, inv_perm, out, L, static_cast<char*>(ws),
+                     experts_fused(cfg), static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

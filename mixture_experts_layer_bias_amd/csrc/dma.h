@@ -16,6 +16,13 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds((dma_gptr_t)src, (dma_lptr_t)lds_wave_base, 16, 0, 0);
 }
 
+// The same load at device scope (sc1): served from the device's coherence point rather than from
+// lines this CU or this XCD's L2 may still hold, so it sees data that another XCD has written
+// with device-scope stores.
+__device__ __forceinline__ void dma16_device_scope(const void* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((dma_gptr_t)src, (dma_lptr_t)lds_wave_base, 16, 0, 16);
+}
+
 // s_waitcnt vmcnt(N) lgkmcnt(0)
 template <int N>
 __device__ __forceinline__ void dma_wait() {

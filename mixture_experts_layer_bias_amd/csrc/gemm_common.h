@@ -28,11 +28,14 @@ struct TileCoord {
   int n_tile;
   int row0;     // first sorted row of the tile
   int row_end;  // end of the expert's segment
+  int m_tiles;  // row tiles over all groups (the tiles of one column tile)
 };
 
-// s_prefix must hold kMaxGroups + 1 ints in LDS.  Block of 256 threads.
-__device__ __forceinline__ TileCoord schedule_tile(const int32_t* __restrict__ offsets, int num_groups, int shared_rows,
-                                                   int BM, int NT, int* s_prefix, int* s_wsum) {
+// s_prefix must hold kMaxGroups + 1 ints in LDS.  Block of at least 256 threads.  `b` is the
+// block's tile slot (blockIdx.x unless one launch runs several grids of tiles).
+__device__ __forceinline__ TileCoord schedule_tile_at(const int32_t* __restrict__ offsets, int num_groups,
+                                                      int shared_rows, int BM, int NT, int* s_prefix, int* s_wsum,
+                                                      int b) {
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   // each thread owns 4 consecutive groups
   int cnt[4], local = 0;
@@ -65,10 +68,10 @@ __device__ __forceinline__ TileCoord schedule_tile(const int32_t* __restrict__ o
   if (tid == 0) s_prefix[num_groups] = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
   __syncthreads();
 
-  TileCoord tc{-1, 0, 0, 0, 0};
+  TileCoord tc{-1, 0, 0, 0, 0, s_prefix[num_groups]};
   const int T = s_prefix[num_groups] * NT;
   const int chunk = (T + 7) / 8;
-  const int b = blockIdx.x, local_idx = b / 8;
+  const int local_idx = b / 8;
   if (local_idx >= chunk) return tc;
   const int L = (b % 8) * chunk + local_idx;
   if (L >= T) return tc;
@@ -89,6 +92,11 @@ __device__ __forceinline__ TileCoord schedule_tile(const int32_t* __restrict__ o
   tc.row_end = shared_rows >= 0 ? shared_rows : offsets[e + 1];
   tc.row0 = seg0 + tc.m_tile * BM;
   return tc;
+}
+
+__device__ __forceinline__ TileCoord schedule_tile(const int32_t* __restrict__ offsets, int num_groups, int shared_rows,
+                                                   int BM, int NT, int* s_prefix, int* s_wsum) {
+  return schedule_tile_at(offsets, num_groups, shared_rows, BM, NT, s_prefix, s_wsum, blockIdx.x);
 }
 
 // Grid size for a grouped GEMM: an upper bound of the tile count, rounded up to 8.

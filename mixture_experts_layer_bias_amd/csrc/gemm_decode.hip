@@ -22,6 +22,7 @@
 #include "dma.h"
 #include "gemm_common.h"
 #include "kernels.h"
+#include "unpermute.h"
 
 namespace moe {
 
@@ -60,8 +61,75 @@ __device__ __forceinline__ void wait_stages(int stages_after) {
 
 __device__ __forceinline__ float silu_d(float g) { return g / (1.0f + __expf(-g)); }
 
-template <int STAGE>
-__global__ __launch_bounds__(256, 2) void k_grouped_gemm_decode(GroupedGemmArgs g) {
+// Bounded wait of a down tile for its expert's gate/up tiles (the fused launch).  The bound only
+// guarantees that every wave exits; gate/up tiles never wait, and all of them are dispatched
+// before the first down tile, so the count is reached long before it.
+constexpr int kDoneSpinLimit = 1 << 22;
+
+// 16 bytes of y (8 bf16) at device scope: y is written in the same launch by down tiles that may
+// run on other XCDs, whose L2s are not coherent with this one's
+__device__ __forceinline__ u32x4 ld16_device_scope(const uint16_t* p) {
+  const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+  u32x4 v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = __hip_atomic_load(q + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return v;
+}
+
+// The unpermute-reduce of output columns [c0, c0 + ncols) for every token, once every down tile
+// of those columns is complete: the same sums, in the same order, as the unpermute-reduce
+// kernel.  Slots are taken 8 at a time (loads of a batch in flight together, adds in slot order).
+__device__ void reduce_columns(const ReduceArgs& r, const uint16_t* y, int c0, int ncols) {
+  const int chunks = ncols / 8;
+  const u32x4 z4 = {0u, 0u, 0u, 0u};
+  for (int p = threadIdx.x; p < r.N * chunks; p += blockDim.x) {
+    const int t = p / chunks, c = c0 + (p % chunks) * 8;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float zero = 0.f;
+    for (int k0 = 0; k0 < r.K; k0 += 8) {
+      int rows[8];
+      float wk[8];
+      u32x4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int k = k0 + j;
+        rows[j] = -2;  // past K
+        wk[j] = 0.f;
+        if (k < r.K) {
+          const size_t tk = (size_t)t * r.K + k;
+          rows[j] = r.ids[tk] < r.E ? r.inv_perm[tk] : -1;
+          wk[j] = r.w[tk];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = rows[j] >= 0 ? ld16_device_scope(y + (size_t)rows[j] * r.H + c) : z4;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (rows[j] >= 0) acc_bf16x8(acc, wk[j], v[j]);
+        else if (rows[j] == -1) zero += wk[j];
+      }
+    }
+    const size_t xo = (size_t)t * r.H + c;
+    const u32x4 xv = zero != 0.f ? ld16(r.x + xo) : z4;
+    const u32x4 sv = r.shared_y ? ld16(r.shared_y + xo) : z4;
+    st16(r.out + xo, finish_bf16x8(acc, zero, xv, r.shared_y != nullptr, sv));
+  }
+}
+
+// One tile of a decode-shaped grouped GEMM.  `block` is the tile slot (blockIdx.x of a plain
+// launch).  FUSED (gate/up, down and the reduce in one launch; `done` holds E per-expert counts,
+// one count per down column tile and one count of reduced column tiles, all zero at the start):
+//   - a gate/up tile writes h with device-scope stores, waits until they are complete, then adds
+//     one to its expert's count;
+//   - a down tile waits until its expert's gate/up tiles are all counted, loads h at device scope,
+//     writes y with device-scope stores, waits for them and adds one to its column tile's count;
+//     the tile that brings that count to the number of row tiles reduces those columns, then
+//     counts them; the last to do so finds every other tile finished and zeroes all the counts
+//     for the next launch.
+// No cache-wide write-back or invalidate is needed on either side.
+template <int STAGE, bool FUSED>
+__device__ __forceinline__ void decode_tile(const GroupedGemmArgs& g, uint8_t* smem, int block, int32_t* done,
+                                            int gu_tiles_per_row_tile, const ReduceArgs* ra) {
   using S = DecodeShape<STAGE>;
   constexpr int BM = S::BM, BNB = S::BNB, ROWB = S::ROWB, WK = S::WK, WN = 4 / WK;
   constexpr int ABYTES = BM * ROWB;
@@ -74,7 +142,6 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_decode(GroupedGemmArgs 
   static_assert(ABYTES == 4096 && BNB * ROWB == 16384 && ABYTES + BNB * ROWB == DC_STAGE, "stage layout");
   static_assert(WK == 1 || 4 * BNB * BM * 4 <= DC_NSTAGE * DC_STAGE, "epilogue partial sums fit in the ring");
 
-  extern __shared__ __align__(16) uint8_t smem[];  // DC_NSTAGE * DC_STAGE bytes
   int* s_prefix = reinterpret_cast<int*>(smem);     // scheduler scratch, dead before the first load
   int* s_wsum = s_prefix + kMaxGroups + 1;
 
@@ -82,9 +149,26 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_decode(GroupedGemmArgs 
   const int NCOLS = STAGE == 0 ? g.I : g.H;
   const int COLS_PER_TILE = STAGE == 0 ? BNB / 2 : BNB;
   const int NT = NCOLS / COLS_PER_TILE;
-  const TileCoord tc = schedule_tile(g.offsets, g.shared ? 1 : g.E, g.shared ? g.N : -1, BM, NT, s_prefix, s_wsum);
-  if (tc.expert < 0) return;  // the same decision in every thread of the block
+  const TileCoord tc =
+      schedule_tile_at(g.offsets, g.shared ? 1 : g.E, g.shared ? g.N : -1, BM, NT, s_prefix, s_wsum, block);
+  if (tc.expert < 0) {  // the same decision in every thread of the block
+    // FUSED with no routed rows at all (every slot took an identity expert): no down tile counts,
+    // so the first NT slots reduce one column tile each
+    if (STAGE == 1 && FUSED && tc.m_tiles == 0 && block < NT) reduce_columns(*ra, nullptr, block * BNB, BNB);
+    return;
+  }
   __syncthreads();               // every wave is done with the scheduler scratch before the loads reuse it
+  if (STAGE == 1 && FUSED) {
+    if (threadIdx.x == 0) {
+      const int count = g.offsets[tc.expert + 1] - g.offsets[tc.expert];
+      const int need = gu_tiles_per_row_tile * ((count + DecodeShape<0>::BM - 1) / DecodeShape<0>::BM);
+      for (int it = 0; it < kDoneSpinLimit; ++it) {
+        if (__hip_atomic_load(done + tc.expert, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need) break;
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    __syncthreads();
+  }
 
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -130,7 +214,8 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_decode(GroupedGemmArgs 
     uint8_t* sa = smem + stage * DC_STAGE;
     uint8_t* sb = sa + ABYTES;
     const size_t koff = (size_t)kstep * ROWB;
-    dma16(a_ptr + koff, sa + wave * 1024);
+    if (STAGE == 1 && FUSED) dma16_device_scope(a_ptr + koff, sa + wave * 1024);
+    else dma16(a_ptr + koff, sa + wave * 1024);
 #pragma unroll
     for (int i = 0; i < 4; ++i) dma16(b_ptr[i] + koff, sb + (wave * 4 + i) * 1024);
   };
@@ -203,7 +288,9 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_decode(GroupedGemmArgs 
 #pragma unroll
           for (int j = 0; j < NTW; ++j) {
             const int col = n0 + wn * (BNB / WN) + j * 16 + frow;
-            out[(size_t)row * NCOLS + col] = (uint16_t)f32_to_bf16(acc[mi][j][r]);
+            uint16_t* dst = out + (size_t)row * NCOLS + col;
+            if (FUSED) __hip_atomic_store(dst, (uint16_t)f32_to_bf16(acc[mi][j][r]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            else *dst = (uint16_t)f32_to_bf16(acc[mi][j][r]);
           }
         }
       }
@@ -228,9 +315,58 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_decode(GroupedGemmArgs 
       const int row = o / OC, col = o % OC;
       if (tc.row0 + row >= tc.row_end) continue;
       const float v = STAGE == 0 ? silu_d(sum4(row, col)) * sum4(row, BNB / 2 + col) : sum4(row, col);
-      out[(size_t)(tc.row0 + row) * NCOLS + n0 + col] = (uint16_t)f32_to_bf16(v);
+      uint16_t* dst = out + (size_t)(tc.row0 + row) * NCOLS + n0 + col;
+      if (STAGE == 0 && FUSED) __hip_atomic_store(dst, (uint16_t)f32_to_bf16(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else *dst = (uint16_t)f32_to_bf16(v);
     }
   }
+  if (STAGE == 0 && FUSED) {
+    static_assert(STAGE != 0 || WK == 4, "the fused h stores are the partial-sum epilogue's");
+    dma_wait<0>();     // this wave's device-scope h stores are complete
+    __syncthreads();   // ... and every other wave's
+    if (threadIdx.x == 0) __hip_atomic_fetch_add(done + tc.expert, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (STAGE == 1 && FUSED) {
+    static_assert(STAGE != 1 || WK == 1, "the fused y stores are the whole-sum epilogue's");
+    dma_wait<0>();     // this wave's device-scope y stores are complete
+    __syncthreads();   // ... and every other wave's; the ring is free
+    int* s_last = reinterpret_cast<int*>(smem);
+    if (threadIdx.x == 0) {
+      const int before = __hip_atomic_fetch_add(done + g.E + tc.n_tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *s_last = before == tc.m_tiles - 1;
+    }
+    __syncthreads();
+    if (*s_last) {
+      reduce_columns(*ra, out, n0, BNB);
+      if (threadIdx.x == 0) {
+        const int before = __hip_atomic_fetch_add(done + g.E + NT, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last[1] = before == NT - 1;
+      }
+      __syncthreads();
+      if (s_last[1])
+        for (int i = threadIdx.x; i <= g.E + NT; i += 256)
+          __hip_atomic_store(done + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+template <int STAGE>
+__global__ __launch_bounds__(256, 2) void k_grouped_gemm_decode(GroupedGemmArgs g) {
+  extern __shared__ __align__(16) uint8_t smem[];  // DC_NSTAGE * DC_STAGE bytes
+  decode_tile<STAGE, false>(g, smem, blockIdx.x, nullptr, 0, nullptr);
+}
+
+// gate/up, down and the reduce of the routed experts in one launch: blocks [0, gu_blocks) take
+// gate/up tiles, the rest take down tiles, which wait for their expert's h (gu_blocks is a multiple
+// of 8, so a block keeps its XCD-aware tile order).  Workgroups are dispatched in order on each
+// XCD, so every gate/up tile is running or done before a down tile of the same XCD can occupy a
+// slot, and gate/up tiles never wait: every wait ends.
+__global__ __launch_bounds__(256, 2) void k_decode_fused(GroupedGemmArgs gu, GroupedGemmArgs dn, ReduceArgs r,
+                                                         int gu_blocks, int32_t* done) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int gu_nt = gu.I / (DecodeShape<0>::BNB / 2);
+  if ((int)blockIdx.x < gu_blocks) decode_tile<0, true>(gu, smem, blockIdx.x, done, gu_nt, nullptr);
+  else decode_tile<1, true>(dn, smem, blockIdx.x - gu_blocks, done, gu_nt, &r);
 }
 
 template <int STAGE>
@@ -243,6 +379,20 @@ hipError_t launch_decode(const GroupedGemmArgs& g, int groups, int rows, int nt,
 }
 
 }  // namespace
+
+int decode_fused_counters(int E, int H) { return E + H / DecodeShape<1>::BNB + 1; }
+
+hipError_t launch_decode_fused(const GroupedGemmArgs& gu, const GroupedGemmArgs& dn, const ReduceArgs& r,
+                               int32_t* done, hipStream_t s) {
+  const int rows = gu.P;
+  if (rows == 0) return hipSuccess;
+  const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&k_decode_fused), DC_NSTAGE * DC_STAGE);
+  if (e != hipSuccess) return e;
+  const unsigned gu_blocks = grouped_grid(rows, gu.E, DecodeShape<0>::BM, gu.I / (DecodeShape<0>::BNB / 2));
+  const unsigned dn_blocks = grouped_grid(rows, dn.E, DecodeShape<1>::BM, dn.H / DecodeShape<1>::BNB);
+  k_decode_fused<<<gu_blocks + dn_blocks, 256, DC_NSTAGE * DC_STAGE, s>>>(gu, dn, r, (int)gu_blocks, done);
+  return hipGetLastError();
+}
 
 bool decode_gemm_fits(const GroupedGemmArgs& g) {
   const int groups = g.shared ? 1 : g.E;

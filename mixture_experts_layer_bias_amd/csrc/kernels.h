@@ -23,10 +23,11 @@ hipError_t launch_topk(const float* part, int slices, float* logits, const float
 
 // a2 + a3 for small batches (N <= 64, N*K <= 1024): top-K and the stable sort in one block
 bool topk_sort_small_fits(int N, int K);
+// `done` ([done_len] int32, may be null) is zeroed for a following fused decode launch
 hipError_t launch_topk_sort_small(const float* part, int slices, float* logits, const float* bias, int32_t* ids,
                                   float* w, float* zero_w, int32_t* counts, int32_t* offsets, int32_t* sorted_ids,
-                                  int32_t* inv_perm, int N, int R, int E, int K, int scoring, int renormalize,
-                                  float routed_scale, hipStream_t s);
+                                  int32_t* inv_perm, int32_t* done, int done_len, int N, int R, int E, int K,
+                                  int scoring, int renormalize, float routed_scale, hipStream_t s);
 
 // a3: stable counting sort by expert; hist is [(permute_chunks(P) + 1) * R] int32 scratch
 int permute_chunks(int P);
@@ -65,6 +66,22 @@ hipError_t launch_grouped_gemm_bf16(const GroupedGemmArgs& g, hipStream_t s);
 // bf16 streaming kernel for a few rows per expert (decode)
 bool decode_gemm_fits(const GroupedGemmArgs& g);
 hipError_t launch_grouped_gemm_decode(const GroupedGemmArgs& g, hipStream_t s);
+// Operands of the unpermute-reduce step (see launch_unpermute_reduce).
+struct ReduceArgs {
+  const int32_t* inv_perm;   // [N, K] sorted row of each (token, slot)
+  const int32_t* ids;        // [N, K] expert ids (>= E: identity expert)
+  const float* w;            // [N, K] routing weights
+  const uint16_t* x;         // [N, H] layer input (identity experts)
+  const uint16_t* shared_y;  // [N, H] shared expert output or null
+  uint16_t* out;             // [N, H]
+  int N, H, K, E;
+};
+// Routed gate/up, down and the unpermute-reduce of a decode layer in one launch (the shared expert,
+// if any, must already be in r.shared_y).  done: decode_fused_counters(E, H) int32 that hold zeros when
+// the launch starts; the launch leaves them zero.
+int decode_fused_counters(int E, int H);
+hipError_t launch_decode_fused(const GroupedGemmArgs& gu, const GroupedGemmArgs& dn, const ReduceArgs& r,
+                               int32_t* done, hipStream_t s);
 
 hipError_t launch_grouped_gemm_fp8(const GroupedGemmArgs& g, hipStream_t s);
 

@@ -6,6 +6,7 @@
 // once to bf16.
 #include "common.h"
 #include "kernels.h"
+#include "unpermute.h"
 
 namespace moe {
 
@@ -46,32 +47,9 @@ __global__ __launch_bounds__(256) void k_unpermute_reduce(const uint16_t* __rest
     const u32x4 sv = shared_y ? ld16(shared_y + xrow + c) : z4;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < KB; ++k) {
-      if (k >= K || rows[k] < 0) continue;
-      const float wv = wk[k];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc[2 * j] += wv * bf16_to_f32(v[k][j] & 0xFFFFu);
-        acc[2 * j + 1] += wv * bf16_to_f32(v[k][j] >> 16);
-      }
-    }
-    if (zero != 0.f) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc[2 * j] += zero * bf16_to_f32(xv[j] & 0xFFFFu);
-        acc[2 * j + 1] += zero * bf16_to_f32(xv[j] >> 16);
-      }
-    }
-    if (shared_y) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc[2 * j] += bf16_to_f32(sv[j] & 0xFFFFu);
-        acc[2 * j + 1] += bf16_to_f32(sv[j] >> 16);
-      }
-    }
-    u32x4 o;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = pack_bf16x2(acc[2 * j], acc[2 * j + 1]);
+    for (int k = 0; k < KB; ++k)
+      if (k < K && rows[k] >= 0) acc_bf16x8(acc, wk[k], v[k]);
+    const u32x4 o = finish_bf16x8(acc, zero, xv, shared_y != nullptr, sv);
     st16(out + xrow + c, o);
   }
 }

@@ -304,8 +304,9 @@ __global__ __launch_bounds__(1024) void k_topk_sort_small(const float* __restric
                                                          float* __restrict__ zero_w, int32_t* __restrict__ counts,
                                                          int32_t* __restrict__ offsets,
                                                          int32_t* __restrict__ sorted_ids,
-                                                         int32_t* __restrict__ inv_perm, int N, int R, int E, int K,
-                                                         int scoring, int renorm, float scale) {
+                                                         int32_t* __restrict__ inv_perm, int32_t* __restrict__ done,
+                                                         int done_len, int N, int R, int E, int K, int scoring,
+                                                         int renorm, float scale) {
   __shared__ float p_lds[16][MAXJ * 64];
   __shared__ __align__(16) int s_ids[1024];
   __shared__ int s_off[1024];  // bucket counts, then bucket offsets
@@ -313,6 +314,8 @@ __global__ __launch_bounds__(1024) void k_topk_sort_small(const float* __restric
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int P = N * K;
   if (tid < R) s_off[tid] = 0;
+  if (done)
+    for (int i = tid; i < done_len; i += 1024) done[i] = 0;
   for (int t = wave; t < N; t += 16) {
     const int my_id = topk_token<MAXJ>(part, nslices, logits, bias, ids, w, zero_w, p_lds[wave], t, N, R, E, K,
                                        scoring, renorm, scale);
@@ -408,14 +411,15 @@ bool topk_sort_small_fits(int N, int K) { return N <= 64 && N * K <= 1024; }
 
 hipError_t launch_topk_sort_small(const float* part, int slices, float* logits, const float* bias, int32_t* ids,
                                   float* w, float* zero_w, int32_t* counts, int32_t* offsets, int32_t* sorted_ids,
-                                  int32_t* inv_perm, int N, int R, int E, int K, int scoring, int renormalize,
-                                  float routed_scale, hipStream_t s) {
+                                  int32_t* inv_perm, int32_t* done, int done_len, int N, int R, int E, int K,
+                                  int scoring, int renormalize, float routed_scale, hipStream_t s) {
   if (N == 0) return hipSuccess;
   const int maxj = (R + 63) / 64;
 #define MOE_SMALL_CASE(J)                                                                                      \
   case J:                                                                                                      \
     k_topk_sort_small<J><<<1, 1024, 0, s>>>(part, slices, logits, bias, ids, w, zero_w, counts, offsets,        \
-                                            sorted_ids, inv_perm, N, R, E, K, scoring, renormalize, routed_scale); \
+                                            sorted_ids, inv_perm, done, done_len, N, R, E, K, scoring,            \
+                                            renormalize, routed_scale);                                          \
     break;
   switch (maxj <= 2 ? maxj : (maxj <= 4 ? 4 : (maxj <= 6 ? 6 : 16))) {
     MOE_SMALL_CASE(1)

@@ -37,6 +37,8 @@ SMALL = {
     "max_width_k32": W("kmax", 40, 256, 1000, 1024, 32, 128, 0, "softmax", False, 1.0, "bf16", True, seed=13),
     # one token (single-token decode) with a shared expert, sigmoid + bias, scaled weights
     "single_token_shared": W("one_tok", 1, 512, 64, 64, 8, 256, 128, "sigmoid", True, 2.5, "bf16", True, seed=14),
+    # decode-sized batch with identity experts (8 of 24 router columns) and no renormalisation
+    "decode_zero_experts": W("zdec", 6, 512, 16, 24, 6, 256, 0, "softmax", False, 1.0, "bf16", True, seed=17),
 }
 FP8_SMALL = {
     "fp8_sigmoid_bias_shared": W("fp8s", 33, 512, 8, 8, 2, 256, 128, "sigmoid", True, 2.5, "fp8", True, seed=9),
@@ -356,6 +358,70 @@ def test_forward_is_deterministic():
     b, _ = run_forward(cfg, w, dl.x)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_decode_forward_is_deterministic():
+    """The decode layer (one launch for the routed GEMMs and the reduce, whose tiles count each other
+    down): repeated calls give the same bits."""
+    wl = SMALL["decode"]
+    dl = mi.device.device_layer(wl)
+    cfg, w = config_of(wl), weights_of(dl)
+    ref, ws = run_forward(cfg, w, dl.x)
+    out = torch.empty_like(ref)
+    for i in range(20):
+        out.fill_(0)
+        moe.moe_forward(cfg, w, dl.x, out, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"call {i}"
+
+
+@pytest.mark.parametrize("name", ["decode", "tiny", "single_token_shared", "decode_zero_experts",
+                                  "many_tiles_300tok", "fp8_sigmoid_bias_shared"])
+def test_experts_forward_matches_forward(name):
+    """moe_experts_forward on moe_forward's own routing gives moe_forward's bits, on two calls in a
+    row over one workspace (the decode path's counters are back at zero after each call)."""
+    wl = SMALL.get(name) or FP8_SMALL[name]
+    print(f"\n[case] experts forward {name}", flush=True)
+    dl = mi.device.device_layer(wl)
+    cfg, w = config_of(wl), weights_of(dl)
+    ref, ws = run_forward(cfg, w, dl.x)
+    L = moe.moe_workspace_layout(cfg)
+    N, K, R = wl.num_tokens, wl.top_k, wl.router_width
+    piece = lambda k, n, dt: ws[L[k]:L[k] + 4 * n].view(dt).clone()
+    ids, tw = piece("topk_ids", N * K, torch.int32), piece("topk_w", N * K, torch.float32)
+    offsets = piece("offsets", R + 1, torch.int32)
+    sid, inv = piece("sorted_ids", N * K, torch.int32), piece("inv_perm", N * K, torch.int32)
+    ws2 = torch.zeros_like(ws)
+    nsync = (min(v for v in L.values() if L["sync"] < v < 2**63) - L["sync"]) // 4  # up to the next piece
+    for i in range(2):
+        out = torch.zeros_like(ref)
+        moe.moe_experts_forward(cfg, w, dl.x, ids, tw, offsets, sid, inv, out, ws2)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"call {i}"
+        assert int(ws2[L["sync"]:].view(torch.int32)[:nsync].abs().sum()) == 0, f"counters after call {i}"
+
+
+def test_decode_every_slot_an_identity_expert():
+    """A correction bias that puts every top-K pick on an identity expert: no routed rows at all, so
+    out = zero_accum * x + the shared expert."""
+    wl = W("allzero", 4, 256, 8, 16, 4, 128, 128, "sigmoid", True, 2.5, "bf16", True, seed=16)
+    print("\n[case] decode, every slot an identity expert", flush=True)
+    dl = mi.device.device_layer(wl)
+    host = mi.host_inputs(wl)
+    bias = host.bias.copy()
+    bias[wl.num_experts:] += np.float32(100.0)
+    w = moe.weights_from_stacked(dl.router, torch.from_numpy(bias).cuda(), dl.gate, dl.up, dl.down,
+                                 sh_gate=dl.sh_gate, sh_up=dl.sh_up, sh_down=dl.sh_down)
+    cfg = config_of(wl)
+    out, ws = run_forward(cfg, w, dl.x)
+    torch.cuda.synchronize()
+    res = ow.run(wl, inputs=mi.HostInputs(wl, host.x, host.router, bias))
+    assert (res.ids >= wl.num_experts).all()
+    L = moe.moe_workspace_layout(cfg)
+    N, K = wl.num_tokens, wl.top_k
+    gids = ws[L["topk_ids"]:L["topk_ids"] + 4 * N * K].view(torch.int32).cpu().numpy().reshape(N, K)
+    same = check_routing(gids, res, K)
+    assert_close(f64(out)[same], res.out_f64[same], BF16_TOL, "all-identity output")
 
 
 def test_zero_tokens_is_a_no_op():
