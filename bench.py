@@ -38,8 +38,8 @@ MEASURED_TRAFFIC = {
                     "mixture_experts_layer_bias_amd/csrc/gemm_common.h",
                     "mixture_experts_layer_bias_amd/csrc/unpermute.h",
                     "mixture_experts_layer_bias_amd/csrc/common.h"],
-        "sha256": "34c2f6889cfb2b1e742eb932b7bd36c91efef8017150cc4d193da1811e258142",
-        "fetch_kib": 93344.48, "write_kib": 48.55, "fetch_scale": 2.0, "write_scale": 1.0,
+        "sha256": "a33cd0fd93e5018d274c2b424763a39939a95022c38ff4136abafee7d3773d78",
+        "fetch_kib": 140118.35, "write_kib": 253.78, "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
 

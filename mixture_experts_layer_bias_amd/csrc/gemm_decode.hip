@@ -7,14 +7,14 @@
 //
 // With one to a few rows per expert the layer is bound by reading the touched
 // experts' weights from HBM, so the kernel is built to keep many bytes in
-// flight: a 4-stage LDS ring filled by direct global -> LDS loads
-// (global_load_lds_dwordx4, 16 bytes per lane) of whole row segments, three K
-// steps of loads ahead of the MFMAs, and two blocks per CU (the ring is the
-// block's only LDS; the tile scheduler's scratch and the epilogue's partial
-// sums are aliased onto it).  Each weight row is read in 256-byte segments
-// where K is long (gate/up), which streams faster than 128-byte ones.  Chunk c
-// of LDS row r is stored at 16-byte slot c ^ (r % (segment / 16)), since the
-// loads write rows unpadded in lane order.
+// flight: a 3- or 4-stage LDS ring filled by direct global -> LDS loads
+// (global_load_lds_dwordx4, 16 bytes per lane) of whole row segments, two or
+// three K steps of loads ahead of the MFMAs, and two blocks per CU (the ring is
+// the block's only LDS; the tile scheduler's scratch and the epilogue's partial
+// sums are aliased onto it).  Each weight row is read in 512-byte segments
+// where K is long (gate/up), which streams faster than 256- or 128-byte ones.
+// Chunk c of LDS row r is stored at 16-byte slot c ^ (r % (segment / 16)),
+// since the loads write rows unpadded in lane order.
 //
 // Waits are explicit (vmcnt of this wave's own loads, then a plain s_barrier):
 // a __syncthreads would wait for every stage still in flight.
@@ -28,34 +28,46 @@ namespace moe {
 
 namespace {
 
-// Tile shapes.  Both move 20 KB per stage (A: BM x ROWB = 4 KB, one load instruction per
-// wave; B: BNB x ROWB = 16 KB, four per wave), so the ring and the waits are shared.
-//   gate/up (K = H, long): 16 rows x 64 weight rows x 256-byte segments; wave w computes the
-//     32-wide k slice w of every step for the whole tile (partial sums added in the epilogue).
-//   down (K = I, short):   32 rows x 128 weight rows x 128-byte segments (half as many tiles,
-//     so a decode layer's tiles are all resident); wave w owns weight rows 32w .. 32w+31.
-constexpr int DC_STAGE = 20480;
-constexpr int DC_NSTAGE = 4;  // 80 KB: two blocks per CU
-constexpr int DC_VM = 5;      // load instructions per wave per stage
-
+// Tile shapes.  A stage holds BM x ROWB bytes of A (AI load instructions per wave) and
+// BNB x ROWB bytes of B (BI per wave); NSTAGE stages make the ring.
+//   gate/up (K = H, long): 16 rows x 32 weight rows (16 gate, 16 up) x 512-byte segments,
+//     3 x 24 KB stages; wave w computes 32-wide k slices 2w and 2w+1 of every step for the whole
+//     tile (partial sums added in the epilogue).
+//   down (K = I, short):   32 rows x 128 weight rows x 128-byte segments, 4 x 20 KB stages (half
+//     as many tiles, so a decode layer's down tiles are all resident at once); wave w owns weight
+//     rows 32w .. 32w+31.
+// Both rings fit twice in a CU's LDS (two blocks per CU).
 template <int STAGE>
 struct DecodeShape;
 template <>
 struct DecodeShape<0> {
-  static constexpr int BM = 16, BNB = 64, ROWB = 256, WK = 4;
+  static constexpr int BM = 16, BNB = 32, ROWB = 512, WK = 4, NSTAGE = 3, AI = 2, BI = 4;
 };
 template <>
 struct DecodeShape<1> {
-  static constexpr int BM = 32, BNB = 128, ROWB = 128, WK = 1;
+  static constexpr int BM = 32, BNB = 128, ROWB = 128, WK = 1, NSTAGE = 4, AI = 1, BI = 4;
 };
+template <int STAGE>
+constexpr int dc_stage_bytes() {
+  return (DecodeShape<STAGE>::BM + DecodeShape<STAGE>::BNB) * DecodeShape<STAGE>::ROWB;
+}
+template <int STAGE>
+constexpr int dc_ring_bytes() {
+  return DecodeShape<STAGE>::NSTAGE * dc_stage_bytes<STAGE>();
+}
+constexpr int DC_LDS = dc_ring_bytes<0>() > dc_ring_bytes<1>() ? dc_ring_bytes<0>() : dc_ring_bytes<1>();
+static_assert(2 * DC_LDS <= 160 * 1024, "two blocks per CU");
 
-// wait until at most `stages_after` later stages (DC_VM loads each) are still in flight
+// wait until at most `stages_after` later stages (VM loads each) are still in flight
+template <int NSTAGE, int VM>
 __device__ __forceinline__ void wait_stages(int stages_after) {
-  static_assert(DC_NSTAGE == 4, "one case per possible count of later stages");
-  switch (stages_after) {
-    case 0: dma_wait<0>(); break;
-    case 1: dma_wait<1 * DC_VM>(); break;
-    default: dma_wait<2 * DC_VM>(); break;
+  static_assert(NSTAGE == 3 || NSTAGE == 4, "one case per possible count of later stages");
+  if (NSTAGE == 3 || stages_after == 1) {
+    if (stages_after == 0) dma_wait<0>();
+    else dma_wait<VM>();
+  } else {
+    if (stages_after == 0) dma_wait<0>();
+    else dma_wait<2 * VM>();
   }
 }
 
@@ -132,6 +144,8 @@ __device__ __forceinline__ void decode_tile(const GroupedGemmArgs& g, uint8_t* s
                                             int gu_tiles_per_row_tile, const ReduceArgs* ra) {
   using S = DecodeShape<STAGE>;
   constexpr int BM = S::BM, BNB = S::BNB, ROWB = S::ROWB, WK = S::WK, WN = 4 / WK;
+  constexpr int NSTAGE = S::NSTAGE, AI = S::AI, BI = S::BI, VM = AI + BI;
+  constexpr int SBYTES = dc_stage_bytes<STAGE>();
   constexpr int ABYTES = BM * ROWB;
   constexpr int LPR = ROWB / 16;          // lanes per row in one load instruction
   constexpr int RPI = 64 / LPR;           // rows per load instruction
@@ -139,8 +153,8 @@ __device__ __forceinline__ void decode_tile(const GroupedGemmArgs& g, uint8_t* s
   constexpr int MT = BM / 16;             // 16-row MFMA blocks
   constexpr int NTW = BNB / WN / 16;      // 16-wide weight blocks per wave
   constexpr int SUBW = NSUB / WK;         // k slices per wave per step
-  static_assert(ABYTES == 4096 && BNB * ROWB == 16384 && ABYTES + BNB * ROWB == DC_STAGE, "stage layout");
-  static_assert(WK == 1 || 4 * BNB * BM * 4 <= DC_NSTAGE * DC_STAGE, "epilogue partial sums fit in the ring");
+  static_assert(ABYTES == AI * 4 * 1024 && BNB * ROWB == BI * 4 * 1024, "one 1 KB load per wave instruction");
+  static_assert(WK == 1 || 4 * BNB * BM * 4 <= NSTAGE * SBYTES, "epilogue partial sums fit in the ring");
 
   int* s_prefix = reinterpret_cast<int*>(smem);     // scheduler scratch, dead before the first load
   int* s_wsum = s_prefix + kMaxGroups + 1;
@@ -186,23 +200,24 @@ __device__ __forceinline__ void decode_tile(const GroupedGemmArgs& g, uint8_t* s
 
   // Load sources.  One instruction writes RPI rows x ROWB bytes; lane l covers row l / LPR
   // of its group and 16-byte slot l % LPR, i.e. logical chunk (l % LPR) ^ (row % LPR).
-  // A: wave w fills tile rows RPI w ..; B: instruction i of wave w fills weight rows
-  // RPI (4w + i) .. (gate/up: the first BNB / 2 rows gate, the rest up).
+  // A: instruction i of wave w fills tile rows RPI (AI w + i) ..; B: instruction i of wave w
+  // fills weight rows RPI (BI w + i) .. (gate/up: the first BNB / 2 rows gate, the rest up).
   const int prow = lane / LPR, pslot = lane % LPR;
-  const uint8_t* a_ptr;
-  {
-    const int trow = wave * RPI + prow;
+  const uint8_t* a_ptr[AI];
+#pragma unroll
+  for (int i = 0; i < AI; ++i) {
+    const int trow = (wave * AI + i) * RPI + prow;
     int p = tc.row0 + trow;
     if (p >= tc.row_end) p = tc.row_end - 1;  // rows past the segment are computed, never stored
     long arow;
     if (STAGE == 0) arow = g.shared ? p : g.sorted_ids[p] / g.K;
     else arow = p;
-    a_ptr = static_cast<const uint8_t*>(g.a) + (size_t)arow * row_bytes + ((pslot ^ (trow % LPR)) << 4);
+    a_ptr[i] = static_cast<const uint8_t*>(g.a) + (size_t)arow * row_bytes + ((pslot ^ (trow % LPR)) << 4);
   }
-  const uint8_t* b_ptr[4];
+  const uint8_t* b_ptr[BI];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int trow = (wave * 4 + i) * RPI + prow;
+  for (int i = 0; i < BI; ++i) {
+    const int trow = (wave * BI + i) * RPI + prow;
     const uint8_t* base;
     if (STAGE == 0)
       base = trow < BNB / 2 ? wa + (size_t)(n0 + trow) * row_bytes : wb + (size_t)(n0 + trow - BNB / 2) * row_bytes;
@@ -211,13 +226,16 @@ __device__ __forceinline__ void decode_tile(const GroupedGemmArgs& g, uint8_t* s
     b_ptr[i] = base + ((pslot ^ (trow % LPR)) << 4);
   }
   auto issue = [&](int stage, int kstep) {
-    uint8_t* sa = smem + stage * DC_STAGE;
+    uint8_t* sa = smem + stage * SBYTES;
     uint8_t* sb = sa + ABYTES;
     const size_t koff = (size_t)kstep * ROWB;
-    if (STAGE == 1 && FUSED) dma16_device_scope(a_ptr + koff, sa + wave * 1024);
-    else dma16(a_ptr + koff, sa + wave * 1024);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(b_ptr[i] + koff, sb + (wave * 4 + i) * 1024);
+    for (int i = 0; i < AI; ++i) {
+      if (STAGE == 1 && FUSED) dma16_device_scope(a_ptr[i] + koff, sa + (wave * AI + i) * 1024);
+      else dma16(a_ptr[i] + koff, sa + (wave * AI + i) * 1024);
+    }
+#pragma unroll
+    for (int i = 0; i < BI; ++i) dma16(b_ptr[i] + koff, sb + (wave * BI + i) * 1024);
   };
   auto lds_chunk = [&](const uint8_t* base, int row, int chunk) {
     return *reinterpret_cast<const u32x4*>(base + row * ROWB + ((chunk ^ (row % LPR)) << 4));
@@ -241,16 +259,16 @@ __device__ __forceinline__ void decode_tile(const GroupedGemmArgs& g, uint8_t* s
     for (int j = 0; j < NTW; ++j) acc[mi][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
-  for (int s = 0; s < DC_NSTAGE - 1; ++s)
+  for (int s = 0; s < NSTAGE - 1; ++s)
     if (s < nk) issue(s, s);
 
   for (int k = 0; k < nk; ++k) {
     const int later = nk - 1 - k;  // stages issued after step k (capped by the ring depth)
-    wait_stages(later < DC_NSTAGE - 2 ? later : DC_NSTAGE - 2);
+    wait_stages<NSTAGE, VM>(later < NSTAGE - 2 ? later : NSTAGE - 2);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    if (k + DC_NSTAGE - 1 < nk) issue((k + DC_NSTAGE - 1) % DC_NSTAGE, k + DC_NSTAGE - 1);
-    const uint8_t* sa = smem + (k % DC_NSTAGE) * DC_STAGE;
+    if (k + NSTAGE - 1 < nk) issue((k + NSTAGE - 1) % NSTAGE, k + NSTAGE - 1);
+    const uint8_t* sa = smem + (k % NSTAGE) * SBYTES;
     const uint8_t* sb = sa + ABYTES;
 #pragma unroll
     for (int u = 0; u < SUBW; ++u) {
@@ -352,7 +370,7 @@ __device__ __forceinline__ void decode_tile(const GroupedGemmArgs& g, uint8_t* s
 
 template <int STAGE>
 __global__ __launch_bounds__(256, 2) void k_grouped_gemm_decode(GroupedGemmArgs g) {
-  extern __shared__ __align__(16) uint8_t smem[];  // DC_NSTAGE * DC_STAGE bytes
+  extern __shared__ __align__(16) uint8_t smem[];  // dc_ring_bytes<STAGE>() bytes
   decode_tile<STAGE, false>(g, smem, blockIdx.x, nullptr, 0, nullptr);
 }
 
@@ -371,10 +389,10 @@ __global__ __launch_bounds__(256, 2) void k_decode_fused(GroupedGemmArgs gu, Gro
 
 template <int STAGE>
 hipError_t launch_decode(const GroupedGemmArgs& g, int groups, int rows, int nt, hipStream_t s) {
-  const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&k_grouped_gemm_decode<STAGE>), DC_NSTAGE * DC_STAGE);
+  constexpr int lds = dc_ring_bytes<STAGE>();
+  const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&k_grouped_gemm_decode<STAGE>), lds);
   if (e != hipSuccess) return e;
-  k_grouped_gemm_decode<STAGE>
-      <<<grouped_grid(rows, groups, DecodeShape<STAGE>::BM, nt), 256, DC_NSTAGE * DC_STAGE, s>>>(g);
+  k_grouped_gemm_decode<STAGE><<<grouped_grid(rows, groups, DecodeShape<STAGE>::BM, nt), 256, lds, s>>>(g);
   return hipGetLastError();
 }
 
@@ -386,11 +404,11 @@ hipError_t launch_decode_fused(const GroupedGemmArgs& gu, const GroupedGemmArgs&
                                int32_t* done, hipStream_t s) {
   const int rows = gu.P;
   if (rows == 0) return hipSuccess;
-  const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&k_decode_fused), DC_NSTAGE * DC_STAGE);
+  const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&k_decode_fused), DC_LDS);
   if (e != hipSuccess) return e;
   const unsigned gu_blocks = grouped_grid(rows, gu.E, DecodeShape<0>::BM, gu.I / (DecodeShape<0>::BNB / 2));
   const unsigned dn_blocks = grouped_grid(rows, dn.E, DecodeShape<1>::BM, dn.H / DecodeShape<1>::BNB);
-  k_decode_fused<<<gu_blocks + dn_blocks, 256, DC_NSTAGE * DC_STAGE, s>>>(gu, dn, r, (int)gu_blocks, done);
+  k_decode_fused<<<gu_blocks + dn_blocks, 256, DC_LDS, s>>>(gu, dn, r, (int)gu_blocks, done);
   return hipGetLastError();
 }
 
@@ -399,8 +417,9 @@ bool decode_gemm_fits(const GroupedGemmArgs& g) {
   const int rows = g.shared ? g.N : g.P;
   const bool few_rows = rows <= 8L * groups && rows <= 512;  // about one row tile per touched expert
   if (!few_rows) return false;
-  return g.stage == 0 ? (g.H % 128 == 0 && g.I % (DecodeShape<0>::BNB / 2) == 0)
-                      : (g.I % 64 == 0 && g.H % DecodeShape<1>::BNB == 0);
+  // whole K steps (ROWB / 2 elements) and whole column tiles
+  return g.stage == 0 ? (g.H % (DecodeShape<0>::ROWB / 2) == 0 && g.I % (DecodeShape<0>::BNB / 2) == 0)
+                      : (g.I % (DecodeShape<1>::ROWB / 2) == 0 && g.H % DecodeShape<1>::BNB == 0);
 }
 
 hipError_t launch_grouped_gemm_decode(const GroupedGemmArgs& g, hipStream_t s) {
