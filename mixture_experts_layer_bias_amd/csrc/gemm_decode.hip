@@ -61,13 +61,14 @@ static_assert(2 * DC_LDS <= 160 * 1024, "two blocks per CU");
 // wait until at most `stages_after` later stages (VM loads each) are still in flight
 template <int NSTAGE, int VM>
 __device__ __forceinline__ void wait_stages(int stages_after) {
-  static_assert(NSTAGE == 3 || NSTAGE == 4, "one case per possible count of later stages");
-  if (NSTAGE == 3 || stages_after == 1) {
-    if (stages_after == 0) dma_wait<0>();
-    else dma_wait<VM>();
-  } else {
-    if (stages_after == 0) dma_wait<0>();
-    else dma_wait<2 * VM>();
+  static_assert(NSTAGE >= 2 && NSTAGE <= 7, "one case per possible count of later stages");
+  switch (stages_after) {
+    case 0: dma_wait<0>(); break;
+    case 1: dma_wait<VM>(); break;
+    case 2: dma_wait<(NSTAGE > 3 ? 2 * VM : VM)>(); break;
+    case 3: dma_wait<(NSTAGE > 4 ? 3 * VM : VM)>(); break;
+    case 4: dma_wait<(NSTAGE > 5 ? 4 * VM : VM)>(); break;
+    default: dma_wait<(NSTAGE > 6 ? 5 * VM : VM)>(); break;
   }
 }
 
