@@ -24,7 +24,7 @@ HOST_LIB = os.path.join(_HERE, "libmoe_inputs_host.so")
 DEV_LIB = os.path.join(_HERE, "libmoe_inputs_dev.so")
 
 TAG_X, TAG_ROUTER, TAG_BIAS, TAG_GATE, TAG_UP, TAG_DOWN = 1, 2, 3, 4, 5, 6
-TAG_SH_GATE, TAG_SH_UP, TAG_SH_DOWN, TAG_PERM = 7, 8, 9, 10
+TAG_SH_GATE, TAG_SH_UP, TAG_SH_DOWN, TAG_PERM, TAG_SH_EXPERT_GATE = 7, 8, 9, 10, 11
 
 SIGMA_X = 1.0
 SIGMA_W = 0.02
@@ -43,7 +43,7 @@ class Workload:
     top_k: int  # K
     inter: int  # I
     shared_inter: int  # Is, 0 = no shared expert
-    scoring: str  # "softmax" | "sigmoid"
+    scoring: str  # "softmax" | "sigmoid" | "sqrtsoftplus"
     renormalize: bool
     routed_scale: float
     weight_dtype: str  # "bf16" | "fp8"
@@ -51,6 +51,7 @@ class Workload:
     zipf_s: float = 0.0  # > 0: skewed router column (prefill workload)
     zipf_tau: float = 0.0
     seed: int = 0
+    shared_gated: bool = False  # the shared expert has a sigmoid gate (one weight row [H])
 
     def with_tokens(self, n: int) -> "Workload":
         return dataclasses.replace(self, num_tokens=n)
@@ -254,6 +255,13 @@ def host_shared(wl: Workload, layer: int = 0):
                 host_bf16((H, Is), seed, TAG_SH_DOWN, 0, SIGMA_W))
     return (host_e4m3(Is, H, seed, TAG_SH_GATE, 0, SIGMA_W), host_e4m3(Is, H, seed, TAG_SH_UP, 0, SIGMA_W),
             host_e4m3(H, Is, seed, TAG_SH_DOWN, 0, SIGMA_W))
+
+
+def host_shared_gate(wl: Workload, layer: int = 0) -> Optional[np.ndarray]:
+    """The shared expert's gate row [H] (bf16 bits, N(0, SIGMA_W)), or None."""
+    if wl.shared_inter == 0 or not wl.shared_gated:
+        return None
+    return host_bf16((wl.hidden,), wl.seed + layer, TAG_SH_EXPERT_GATE, 0, SIGMA_W)
 
 
 # ----------------------------------------------------------------------------- device fills (torch)

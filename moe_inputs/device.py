@@ -12,8 +12,9 @@ from typing import Optional
 import numpy as np
 import torch
 
-from . import (SIGMA_BIAS, SIGMA_W, SIGMA_X, TAG_BIAS, TAG_DOWN, TAG_GATE, TAG_ROUTER, TAG_SH_DOWN, TAG_SH_GATE,
-               TAG_SH_UP, TAG_UP, TAG_X, Workload, dev_bf16, dev_e4m3, dev_f32, zipf_router_column)
+from . import (SIGMA_BIAS, SIGMA_W, SIGMA_X, TAG_BIAS, TAG_DOWN, TAG_GATE, TAG_ROUTER, TAG_SH_DOWN,
+               TAG_SH_EXPERT_GATE, TAG_SH_GATE, TAG_SH_UP, TAG_UP, TAG_X, Workload, dev_bf16, dev_e4m3, dev_f32,
+               zipf_router_column)
 
 
 @dataclasses.dataclass
@@ -34,6 +35,7 @@ class DeviceLayer:
     sh_gate_s: Optional[torch.Tensor] = None
     sh_up_s: Optional[torch.Tensor] = None
     sh_down_s: Optional[torch.Tensor] = None
+    sh_expert_gate: Optional[torch.Tensor] = None  # [H] bf16, the shared expert's sigmoid gate row
 
 
 def _mat(rows, cols, seed, tag, sub, fp8, device):
@@ -84,6 +86,9 @@ def device_layer(wl: Workload, layer: int = 0, device: str = "cuda", x_only: boo
         lay.sh_gate, lay.sh_gate_s = _mat(Is, H, seed, TAG_SH_GATE, 0, fp8, device)
         lay.sh_up, lay.sh_up_s = _mat(Is, H, seed, TAG_SH_UP, 0, fp8, device)
         lay.sh_down, lay.sh_down_s = _mat(H, Is, seed, TAG_SH_DOWN, 0, fp8, device)
+        if wl.shared_gated:
+            lay.sh_expert_gate = torch.empty((H,), dtype=torch.bfloat16, device=device)
+            dev_bf16(lay.sh_expert_gate, seed, TAG_SH_EXPERT_GATE, 0, SIGMA_W)
     return lay
 
 

@@ -9,12 +9,16 @@ engines; no page prints kernel source or numbers for this path):
   ``MoeLayer::forward_prefill`` and its steps: gate GEMM, top-K, sort by
   expert (``moe_sort_by_expert`` and its four outputs), grouped gate/up GEMM,
   activation, grouped down GEMM, ``moe_unpermute_reduce_indexed`` and the
-  shared-expert blend (weight 1 without a shared_expert_gate).
+  shared-expert blend: output += sigmoid(input . shared_expert_gate) * shared,
+  weight 1 when the layer has no shared_expert_gate.
 * "spark_model/layers/moe/forward.rs", ``MoeLayer::forward``: the top-K
   scoring arms (softmax; sigmoid + correction bias for selection with
   unbiased, renormalised, scaled weights; softmax + correction bias with the
-  zero-computation experts folded into ``zero_accum``) and the doc comment of
-  ``MoeLayer::apply_zero_expert`` (out[t,:] += zero_accum[t] * x[t,:]).
+  zero-computation experts folded into ``zero_accum``; the DeepSeek-V4
+  sqrtsoftplus + correction bias arm: scores = sqrtsoftplus(gate_logits),
+  indices = topk(scores + bias), weights = scores[indices] / their sum) and the
+  doc comment of ``MoeLayer::apply_zero_expert`` (out[t,:] += zero_accum[t] *
+  x[t,:]).
 * "spark_model/layers/moe/forward_batched.rs", ``MoeLayer::forward_batched``:
   the router width R differs from the expert count E only when the router also
   scores the zero-computation experts.
@@ -25,7 +29,10 @@ the selection score go to the lower router column, slots ordered by
 descending selection score; the sort is stable in the expanded index t*K+k and
 ``sorted_token_ids`` stores that expanded index; h = silu(g)*u is rounded to
 the expert GEMM operand type (bf16, or e4m3 with per-128 scales) before the
-down projection, nothing else is rounded until the one final bf16 rounding.
+down projection, nothing else is rounded until the one final bf16 rounding;
+sqrtsoftplus(z) is sqrt(softplus(z)) = sqrt(ln(1 + e^z)) (the pages only name
+it); the shared-expert gate is one bf16 weight row [H] and its dot product with
+the token's bf16 input is exact in float64.
 """
 from __future__ import annotations
 
@@ -50,7 +57,7 @@ class MoeConfig:
     top_k: int  # num_experts_per_tok (K)
     inter: int  # moe_intermediate_size (I)
     shared_inter: int  # shared_expert_intermediate_size (0: none)
-    scoring: str  # scoring_func: "softmax" | "sigmoid"
+    scoring: str  # scoring_func: "softmax" | "sigmoid" | "sqrtsoftplus"
     renormalize: bool  # norm_topk_prob
     routed_scale: float  # routed_scaling_factor
     weight_dtype: str  # "bf16" | "fp8"
@@ -69,10 +76,14 @@ def router_logits(x_bits: np.ndarray, router_bits: np.ndarray) -> np.ndarray:
 
 
 def scores(logits: np.ndarray, scoring: str) -> np.ndarray:
-    """Router probabilities: softmax over all R columns, or the logistic sigmoid.
+    """Router scores: softmax over all R columns, the logistic sigmoid, or
+    sqrt(softplus).
 
     forward.rs page, ``MoeLayer::forward`` top-K arms (``moe_topk_softmax``;
-    the sigmoid + correction bias comment: scores = sigmoid(gate_logits)).
+    the sigmoid + correction bias comment: scores = sigmoid(gate_logits); the
+    DeepSeek-V4 comment: scores = sqrtsoftplus(gate_logits)).  softplus(z) =
+    ln(1 + e^z), written as max(z, 0) + ln(1 + e^-|z|) so that no exponential
+    overflows.
     """
     if scoring == "softmax":
         z = logits - logits.max(axis=1, keepdims=True)
@@ -80,6 +91,8 @@ def scores(logits: np.ndarray, scoring: str) -> np.ndarray:
         return e / e.sum(axis=1, keepdims=True)
     if scoring == "sigmoid":
         return 1.0 / (1.0 + np.exp(-logits))
+    if scoring == "sqrtsoftplus":
+        return np.sqrt(np.maximum(logits, 0.0) + np.log1p(np.exp(-np.abs(logits))))
     raise ValueError(f"unknown scoring {scoring!r}")
 
 
@@ -253,7 +266,8 @@ class OracleResult:
     weights: np.ndarray  # [n, K] float64
     zero_accum: np.ndarray  # [n] float64
     routed: np.ndarray  # [n, H] float64: sum_k w * y over real experts
-    shared: Optional[np.ndarray]  # [n, H] float64
+    shared: Optional[np.ndarray]  # [n, H] float64, the shared expert's output before its gate
+    shared_weight: np.ndarray  # [n] float64: sigmoid(x . shared_expert_gate), or 1
     out_f64: np.ndarray  # [n, H] float64 before the final rounding
     out_bits: np.ndarray  # [n, H] bf16 bits
 
@@ -261,19 +275,35 @@ class OracleResult:
 ExpertFn = Callable[[int], tuple]
 
 
+def shared_gate(x_bits: np.ndarray, gate_bits: Optional[np.ndarray]) -> np.ndarray:
+    """Per-token weight of the shared expert: sigmoid(x[t] . shared_expert_gate),
+    or 1 when the layer has no shared_expert_gate.
+
+    forward_prefill.rs page, the shared-expert blend comment.  gate_bits is the
+    gate's one weight row [H] (bf16); the dot product is float64.
+    """
+    if gate_bits is None:
+        return np.ones(x_bits.shape[0])
+    z = bf16_to_f64(x_bits) @ bf16_to_f64(gate_bits)
+    return 1.0 / (1.0 + np.exp(-z))
+
+
 def moe_forward(cfg: MoeConfig, x_bits: np.ndarray, router_bits: np.ndarray, bias: Optional[np.ndarray],
-                expert: ExpertFn, shared: Optional[tuple], tokens: Optional[np.ndarray] = None) -> OracleResult:
-    """out[t] = bf16( sum_{k: id<E} w[t,k] * y_{t,k} + zero_accum[t] * x[t] + shared[t] ).
+                expert: ExpertFn, shared: Optional[tuple], tokens: Optional[np.ndarray] = None,
+                shared_gate_bits: Optional[np.ndarray] = None) -> OracleResult:
+    """out[t] = bf16( sum_{k: id<E} w[t,k] * y_{t,k} + zero_accum[t] * x[t] + g[t] * shared[t] ),
+    with g[t] = sigmoid(x[t] . shared_expert_gate), or 1 without that gate.
 
     Every token is independent, so ``x_bits`` may hold any subset of the
     layer's rows (``tokens`` names them, for bookkeeping only).
     ``expert(e)`` returns routed expert e's weights (bf16 bit arrays
     (Wg, Wu, Wd), or fp8 ((codes, scales) x 3)), fetched only for experts some
-    row selects; ``shared`` is the shared expert in the same form or None.
+    row selects; ``shared`` is the shared expert in the same form or None,
+    ``shared_gate_bits`` its gate row [H] (bf16 bits) or None.
 
     Steps as on the forward_prefill.rs page: gate GEMM, top-K, grouped
     gate/up + SwiGLU, grouped down, unpermute + top-K-weighted reduce, shared
-    blend with weight 1; then the zero-computation experts' term of
+    blend (sigmoid-gated, or weight 1); then the zero-computation experts' term of
     ``MoeLayer::apply_zero_expert`` (forward.rs page).  Reading: the three
     terms are summed in float64 and rounded to bf16 once.
     """
@@ -305,7 +335,8 @@ def moe_forward(cfg: MoeConfig, x_bits: np.ndarray, router_bits: np.ndarray, bia
         else:
             sh = swiglu_expert_fp8(xq, xs, *shared)
 
+    g = shared_gate(x_bits, shared_gate_bits)
     total = routed + zero_accum[:, None] * x64
     if sh is not None:
-        total = total + sh
-    return OracleResult(tokens, logits, p, ids, gap, w, zero_accum, routed, sh, total, f64_to_bf16(total))
+        total = total + g[:, None] * sh
+    return OracleResult(tokens, logits, p, ids, gap, w, zero_accum, routed, sh, g, total, f64_to_bf16(total))

@@ -38,7 +38,8 @@ def run(wl: mi.Workload, tokens: Optional[np.ndarray] = None, layer: int = 0,
             expert_cache[e] = mi.host_expert(wl, e, layer)
         return expert_cache[e]
 
-    return moe_forward(config_of(wl), x, router, bias, expert, mi.host_shared(wl, layer), tokens=tokens)
+    return moe_forward(config_of(wl), x, router, bias, expert, mi.host_shared(wl, layer), tokens=tokens,
+                       shared_gate_bits=mi.host_shared_gate(wl, layer))
 
 
 @functools.lru_cache(maxsize=8)

@@ -85,6 +85,32 @@ def test_sigmoid_is_expit():
     assert np.allclose(om.scores(lg, "sigmoid"), expit(lg), rtol=1e-14)
 
 
+def test_sqrtsoftplus_is_sqrt_of_torch_softplus_with_closed_forms():
+    """sqrt(softplus(z)) against torch's softplus in float64, over a range that
+    overflows a naive exp; closed forms at 0 and in both tails."""
+    z = np.concatenate([np.linspace(-60.0, 60.0, 241), np.random.default_rng(31).standard_normal(200) * 4])
+    ref = torch.sqrt(torch.nn.functional.softplus(torch.from_numpy(z), threshold=1000.0)).numpy()
+    got = om.scores(z[None, :], "sqrtsoftplus")[0]
+    assert np.allclose(got, ref, rtol=1e-14, atol=0)
+    edge = om.scores(np.array([[0.0, 800.0, -800.0, 30.0, -30.0]]), "sqrtsoftplus")[0]
+    assert edge[0] == pytest.approx(math.sqrt(math.log(2.0)), rel=1e-15)
+    assert edge[1] == pytest.approx(math.sqrt(800.0), rel=1e-15)  # softplus(z) -> z
+    assert edge[2] == 0.0 or edge[2] < 1e-170  # softplus(z) -> e^z, so the score -> e^(z/2)
+    assert edge[3] == pytest.approx(math.sqrt(30.0 + math.exp(-30.0)), rel=1e-15)
+    assert edge[4] == pytest.approx(math.exp(-15.0), rel=1e-12)
+
+
+def test_sqrtsoftplus_without_bias_selects_topk_of_logits_and_renormalises():
+    """sqrt(softplus) is increasing, so without a bias the K best scores are the K
+    best logits; renormalised weights sum to 1, then times the scale."""
+    lg = np.random.default_rng(32).standard_normal((40, 64)) * 3
+    p = om.scores(lg, "sqrtsoftplus")
+    ids, _ = om.select_topk(p, None, 6)
+    assert np.array_equal(ids, np.argsort(-lg, axis=1, kind="stable")[:, :6])
+    w, _ = om.routing_weights(p, ids, True, 2.0, 64)
+    assert np.allclose(w.sum(1), 2.0, rtol=1e-14)
+
+
 def test_topk_equals_full_sort_brute_force_with_ties():
     rng = np.random.default_rng(4)
     p = rng.integers(0, 6, size=(200, 12)).astype(np.float64) / 8.0  # many exact ties
@@ -215,7 +241,7 @@ def test_single_expert_top1_is_a_plain_swiglu_mlp():
     assert (res.ids == 0).all() and np.allclose(res.weights, 1.0)
 
 
-def _dense_brute_force(cfg, x_bits, router_bits, bias, experts, shared):
+def _dense_brute_force(cfg, x_bits, router_bits, bias, experts, shared, shared_gate_bits=None):
     """North-star brute force: a per-token loop over ALL experts, gates zeroed
     unless selected; written with Python loops and a full sort per token."""
     out = []
@@ -228,8 +254,10 @@ def _dense_brute_force(cfg, x_bits, router_bits, bias, experts, shared):
             m = max(logit)
             ex = [math.exp(v - m) for v in logit]
             p = [v / sum(ex) for v in ex]
-        else:
+        elif cfg.scoring == "sigmoid":
             p = [1 / (1 + math.exp(-v)) for v in logit]
+        else:  # sqrt(softplus), softplus(v) = ln(1 + e^v)
+            p = [math.sqrt(math.log1p(math.exp(v))) for v in logit]
         sel = [p[r] + (float(bias[r]) if bias is not None else 0.0) for r in range(R)]
         chosen = sorted(range(R), key=lambda r: (-sel[r], r))[:K]
         denom = sum(p[r] for r in chosen) if cfg.renormalize else 1.0
@@ -249,12 +277,16 @@ def _dense_brute_force(cfg, x_bits, router_bits, bias, experts, shared):
         for r in range(E, R):
             acc += gate[r] * X[t]
         if shared is not None:
+            gsh = 1.0
+            if shared_gate_bits is not None:
+                gv = codecs.bf16_to_f64(shared_gate_bits)
+                gsh = 1 / (1 + math.exp(-sum(float(X[t, i]) * float(gv[i]) for i in range(cfg.hidden))))
             if cfg.weight_dtype == "bf16":
                 sg, su, sd = (codecs.bf16_to_f64(w) for w in shared)
                 g, u = sg @ X[t], su @ X[t]
-                acc += sd @ codecs.bf16_to_f64(codecs.f64_to_bf16(g / (1 + np.exp(-g)) * u))
+                acc += gsh * (sd @ codecs.bf16_to_f64(codecs.f64_to_bf16(g / (1 + np.exp(-g)) * u)))
             else:
-                acc += _fp8_expert_blockwise(X[t], shared)
+                acc += gsh * _fp8_expert_blockwise(X[t], shared)
         out.append(acc)
     return np.array(out)
 
@@ -314,12 +346,21 @@ def _random_layer(rng, N, H, E, R, K, I, Is, scoring, renorm, scale, dtype, with
          with_bias=True),
     dict(N=3, H=256, E=4, R=4, K=2, I=128, Is=128, scoring="sigmoid", renorm=True, scale=2.5, dtype="fp8",
          with_bias=True),
+    dict(N=6, H=32, E=8, R=8, K=3, I=16, Is=0, scoring="sqrtsoftplus", renorm=True, scale=1.5, dtype="bf16",
+         with_bias=True),
+    dict(N=5, H=32, E=6, R=9, K=3, I=16, Is=24, scoring="sqrtsoftplus", renorm=False, scale=1.0, dtype="bf16",
+         with_bias=True, gated=True),
+    dict(N=3, H=256, E=4, R=4, K=2, I=128, Is=128, scoring="softmax", renorm=True, scale=1.0, dtype="fp8",
+         with_bias=False, gated=True),
 ])
 def test_oracle_equals_dense_brute_force(case):
     rng = np.random.default_rng(13)
+    case = dict(case)
+    gated = case.pop("gated", False)
     cfg, x, wr, bias, experts, shared = _random_layer(rng, **case)
-    res = om.moe_forward(cfg, x, wr, bias, lambda e: experts[e], shared)
-    ref = _dense_brute_force(cfg, x, wr, bias, experts, shared)
+    gate = _bf16(rng.standard_normal(cfg.hidden) * 0.2) if gated else None
+    res = om.moe_forward(cfg, x, wr, bias, lambda e: experts[e], shared, shared_gate_bits=gate)
+    ref = _dense_brute_force(cfg, x, wr, bias, experts, shared, gate)
     assert np.allclose(res.out_f64, ref, rtol=1e-11, atol=1e-12 * np.abs(ref).max())
     assert np.array_equal(res.out_bits, codecs.f64_to_bf16(ref)) or np.abs(
         codecs.bf16_to_f64(res.out_bits) - codecs.bf16_to_f64(codecs.f64_to_bf16(ref))).max() <= \
@@ -361,6 +402,28 @@ def test_zero_routed_down_leaves_the_shared_expert():
     g, u = X @ sg.T, X @ su.T
     ref = codecs.bf16_to_f64(codecs.f64_to_bf16(torch.nn.functional.silu(torch.from_numpy(g)).numpy() * u)) @ sd.T
     assert np.allclose(res.out_f64, ref, rtol=1e-12)
+
+
+def test_shared_gate_closed_forms():
+    """A zero gate row weighs the shared expert by sigmoid(0) = 1/2 exactly, which
+    equals the ungated layer with the shared W_down halved (exact in bf16).  For
+    one token, a gate row of 8 x (resp. -8 x) saturates the sigmoid to exactly 1
+    (resp. 0) in float64: the ungated layer, resp. the layer with no shared expert."""
+    rng = np.random.default_rng(33)
+    cfg, x, wr, bias, experts, shared = _random_layer(rng, 1, 64, 4, 4, 2, 16, 32, "softmax", True, 1.0, "bf16",
+                                                      False)
+    ex = lambda e: experts[e]
+    ungated = om.moe_forward(cfg, x, wr, bias, ex, shared)
+    half = (shared[0], shared[1], _bf16(codecs.bf16_to_f64(shared[2]) * 0.5))
+    a = om.moe_forward(cfg, x, wr, bias, ex, shared, shared_gate_bits=np.zeros(64, np.uint16))
+    b = om.moe_forward(cfg, x, wr, bias, ex, half)
+    assert np.array_equal(a.out_f64, b.out_f64) and (a.shared_weight == 0.5).all()
+    up = om.moe_forward(cfg, x, wr, bias, ex, shared, shared_gate_bits=_bf16(codecs.bf16_to_f64(x[0]) * 8))
+    assert np.array_equal(up.out_f64, ungated.out_f64)
+    cfg0 = om.MoeConfig(cfg.hidden, cfg.num_experts, cfg.router_width, cfg.top_k, cfg.inter, 0, cfg.scoring,
+                        cfg.renormalize, cfg.routed_scale, cfg.weight_dtype)
+    down = om.moe_forward(cfg, x, wr, bias, ex, shared, shared_gate_bits=_bf16(codecs.bf16_to_f64(x[0]) * -8))
+    assert np.array_equal(down.out_f64, om.moe_forward(cfg0, x, wr, bias, ex, None).out_f64)
 
 
 def test_routed_part_is_linear_in_w_down():
