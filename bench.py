@@ -118,7 +118,8 @@ def main():
     for l in range(n_layers):
         dl = mid.device_layer(wl, layer=l, device="cuda:0")
         w = moe.weights_from_stacked(dl.router, dl.bias, dl.gate, dl.up, dl.down, dl.gate_s, dl.up_s, dl.down_s,
-                                     dl.sh_gate, dl.sh_up, dl.sh_down, dl.sh_gate_s, dl.sh_up_s, dl.sh_down_s)
+                                     dl.sh_gate, dl.sh_up, dl.sh_down, dl.sh_gate_s, dl.sh_up_s, dl.sh_down_s,
+                                    sh_expert_gate=dl.sh_expert_gate)
         layers.append((dl, w))
     # zeroed once: the decode experts path keeps its counters in the workspace and leaves them zero
     ws = torch.zeros(moe.moe_workspace_size(cfg), dtype=torch.uint8, device=dev)

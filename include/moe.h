@@ -42,7 +42,7 @@ typedef enum {
   MOE_ERR_HIP = 4          /* a HIP runtime error from a launch */
 } moe_status_t;
 
-enum { MOE_SCORING_SOFTMAX = 0, MOE_SCORING_SIGMOID = 1 };
+enum { MOE_SCORING_SOFTMAX = 0, MOE_SCORING_SIGMOID = 1, MOE_SCORING_SQRTSOFTPLUS = 2 };
 enum { MOE_WEIGHTS_BF16 = 0, MOE_WEIGHTS_FP8_E4M3 = 1 };
 enum { MOE_STAGE_GATE_UP = 0, MOE_STAGE_DOWN = 1 };
 enum { MOE_GROUP_ROUTED = 0, MOE_GROUP_SHARED = 1 };
@@ -91,6 +91,8 @@ typedef struct {
   const float* sh_gate_s; /* fp8 only: [Is/128, H/128] */
   const float* sh_up_s;
   const float* sh_down_s; /* [H/128, Is/128] */
+  const void* sh_expert_gate; /* [H] bf16: the shared expert's sigmoid gate row, or NULL (weight 1);
+                                 must be NULL when Is == 0 */
 } moe_weights_t;
 
 /* Bytes of device workspace that moe_forward, moe_experts_forward and moe_permute need for `cfg`
@@ -102,9 +104,11 @@ moe_status_t moe_workspace_size(const moe_config_t* cfg, size_t* bytes);
  * forward_prefill.rs page, MoeLayer::forward_prefill gate GEMM and top-K steps;
  * forward.rs page, MoeLayer::forward top-K arms (moe_topk_softmax;
  * moe_topk_sigmoid with the correction bias used for selection only;
- * moe_topk_softmax_bias with the zero-expert fold into zero_accum).
+ * moe_topk_softmax_bias with the zero-expert fold into zero_accum;
+ * moe_topk_sqrtsoftplus, the DeepSeek-V4 arm: scores = sqrtsoftplus(logits)).
  *   logits[t,r] = sum_h x[t,h] * router_w[r,h]          (fp32 accumulation)
- *   p = softmax over all R columns, or sigmoid            (fp32)
+ *   p = softmax over all R columns, sigmoid, or sqrt(softplus) with
+ *       softplus(z) = ln(1 + e^z)                          (fp32)
  *   ids[t,0..K) = the K largest p + bias (bias 0 if NULL), slots in descending
  *                 order, exact ties to the lower column
  *   w[t,k] = p[ids] (unbiased); / sum_k when renormalize; * routed_scale
@@ -166,15 +170,18 @@ moe_status_t moe_grouped_gemm(const moe_config_t* cfg, int32_t stage, int32_t gr
 /* Unpermute with the top-K-weighted reduce, plus the shared-expert and
  * zero-computation-expert blends, rounded once to bf16.
  * forward_prefill.rs page, moe_unpermute_reduce_indexed and the shared blend
- * (weight 1 without a shared_expert_gate); forward.rs page,
- * MoeLayer::apply_zero_expert (out[t,:] += zero_accum[t] * x[t,:]).
+ * (output += sigmoid(input . shared_expert_gate) * shared, weight 1 without a
+ * shared_expert_gate); forward.rs page, MoeLayer::apply_zero_expert
+ * (out[t,:] += zero_accum[t] * x[t,:]).
+ *   g[t] = sigmoid(sum_h x[t,h] * shared_gate[h])  (fp32), or 1 if shared_gate is NULL
  *   out[t,:] = bf16( sum_{k: ids<E} w[t,k] * y_sorted[inv_perm[t*K+k], :]
- *                    + (sum_{k: ids>=E} w[t,k]) * x[t,:] + shared_y[t,:] )   (fp32 sum)
+ *                    + (sum_{k: ids>=E} w[t,k]) * x[t,:] + g[t] * shared_y[t,:] )   (fp32 sum)
  * y_sorted [P, H] bf16 (the DOWN output); inv_perm [P]; topk_ids, topk_w [N, K];
- * x [N, H] bf16; shared_y [N, H] bf16 or NULL; out [N, H] bf16. */
+ * x [N, H] bf16; shared_y [N, H] bf16 or NULL; shared_gate [H] bf16 or NULL (ignored
+ * without shared_y); out [N, H] bf16. */
 moe_status_t moe_unpermute_reduce(const moe_config_t* cfg, const void* y_sorted, const int32_t* inv_perm,
                                   const int32_t* topk_ids, const float* topk_w, const void* x,
-                                  const void* shared_y, void* out, void* stream);
+                                  const void* shared_y, const void* shared_gate, void* out, void* stream);
 
 /* The whole layer: route -> sort -> [quantise] -> gate/up (+ shared) -> down
  * (+ shared) -> unpermute-reduce, on one stream with no host synchronisation.

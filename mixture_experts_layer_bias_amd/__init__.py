@@ -22,7 +22,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, 1, 2, 3, 4
-MOE_SCORING_SOFTMAX, MOE_SCORING_SIGMOID = 0, 1
+MOE_SCORING_SOFTMAX, MOE_SCORING_SIGMOID, MOE_SCORING_SQRTSOFTPLUS = 0, 1, 2
 MOE_WEIGHTS_BF16, MOE_WEIGHTS_FP8_E4M3 = 0, 1
 MOE_STAGE_GATE_UP, MOE_STAGE_DOWN = 0, 1
 MOE_GROUP_ROUTED, MOE_GROUP_SHARED = 0, 1
@@ -49,7 +49,7 @@ class moe_config_t(ctypes.Structure):
 class moe_weights_t(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "router_w", "correction_bias", "gate_w", "up_w", "down_w", "gate_s", "up_s", "down_s",
-        "sh_gate_w", "sh_up_w", "sh_down_w", "sh_gate_s", "sh_up_s", "sh_down_s")]
+        "sh_gate_w", "sh_up_w", "sh_down_w", "sh_gate_s", "sh_up_s", "sh_down_s", "sh_expert_gate")]
 
 
 class moe_workspace_layout_t(ctypes.Structure):
@@ -77,7 +77,7 @@ def lib() -> ctypes.CDLL:
             "moe_permute": [cfgp, vp, vp, vp, vp, vp, vp, sz, vp],
             "moe_quantize_fp8": [cfgp, vp, vp, vp, vp],
             "moe_grouped_gemm": [cfgp, i32, i32, ctypes.POINTER(moe_weights_t), vp, vp, vp, vp, vp, vp, vp, sz, vp],
-            "moe_unpermute_reduce": [cfgp, vp, vp, vp, vp, vp, vp, vp, vp],
+            "moe_unpermute_reduce": [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
             "moe_forward": [cfgp, ctypes.POINTER(moe_weights_t), vp, vp, vp, sz, vp],
             "moe_experts_forward": [cfgp, ctypes.POINTER(moe_weights_t), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         }
@@ -111,7 +111,8 @@ def make_config(num_tokens: int, hidden: int, num_experts: int, router_width: in
                 shared_inter: int = 0, scoring: str = "softmax", renormalize: bool = True,
                 routed_scale: float = 1.0, weight_dtype: str = "bf16") -> moe_config_t:
     return moe_config_t(num_tokens, hidden, num_experts, router_width, top_k, inter, shared_inter,
-                        {"softmax": MOE_SCORING_SOFTMAX, "sigmoid": MOE_SCORING_SIGMOID}[scoring],
+                        {"softmax": MOE_SCORING_SOFTMAX, "sigmoid": MOE_SCORING_SIGMOID,
+                         "sqrtsoftplus": MOE_SCORING_SQRTSOFTPLUS}[scoring],
                         1 if renormalize else 0, routed_scale,
                         {"bf16": MOE_WEIGHTS_BF16, "fp8": MOE_WEIGHTS_FP8_E4M3}[weight_dtype])
 
@@ -168,6 +169,7 @@ class LayerWeights:
     sh_gate_s: Optional[object] = None
     sh_up_s: Optional[object] = None
     sh_down_s: Optional[object] = None
+    sh_expert_gate: Optional[object] = None  # [H] bf16: the shared expert's sigmoid gate row
 
     def __post_init__(self):
         import torch
@@ -185,7 +187,7 @@ class LayerWeights:
         s.correction_bias = _ptr(self.correction_bias, "correction_bias", 4, optional=True)
         for n, t in self._tables.items():
             setattr(s, n, None if t is None else t.data_ptr())
-        for n in ("sh_gate_w", "sh_up_w", "sh_down_w", "sh_gate_s", "sh_up_s", "sh_down_s"):
+        for n in ("sh_gate_w", "sh_up_w", "sh_down_w", "sh_gate_s", "sh_up_s", "sh_down_s", "sh_expert_gate"):
             setattr(s, n, _ptr(getattr(self, n), n, optional=True))
         self.struct = s
 
@@ -231,10 +233,12 @@ def moe_grouped_gemm(cfg, stage: int, group: int, weights: LayerWeights, a, a_sc
                                   0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 
-def moe_unpermute_reduce(cfg, y_sorted, inv_perm, topk_ids, topk_w, x, shared_y, out, stream=None) -> None:
+def moe_unpermute_reduce(cfg, y_sorted, inv_perm, topk_ids, topk_w, x, shared_y, out, shared_gate=None,
+                         stream=None) -> None:
     _check(lib().moe_unpermute_reduce(ctypes.byref(cfg), _ptr(y_sorted, "y_sorted", 2), _ptr(inv_perm, "inv_perm", 4),
                                       _ptr(topk_ids, "topk_ids", 4), _ptr(topk_w, "topk_w", 4), _ptr(x, "x", 2),
-                                      _ptr(shared_y, "shared_y", 2, True), _ptr(out, "out", 2), _stream(stream)))
+                                      _ptr(shared_y, "shared_y", 2, True), _ptr(shared_gate, "shared_gate", 2, True),
+                                      _ptr(out, "out", 2), _stream(stream)))
 
 
 def moe_forward(cfg, weights: LayerWeights, x, out, ws, stream=None) -> None:
@@ -253,7 +257,7 @@ def moe_experts_forward(cfg, weights: LayerWeights, x, topk_ids, topk_w, offsets
 
 def weights_from_stacked(router_w, correction_bias, gate, up, down, gate_s=None, up_s=None, down_s=None,
                          sh_gate=None, sh_up=None, sh_down=None, sh_gate_s=None, sh_up_s=None,
-                         sh_down_s=None) -> LayerWeights:
+                         sh_down_s=None, sh_expert_gate=None) -> LayerWeights:
     """LayerWeights over expert weights stacked as [E, I, H] / [E, H, I] tensors
     (and [E, ., .] block scales for fp8): the tables point at each expert's slice."""
     E = gate.shape[0]
@@ -262,4 +266,4 @@ def weights_from_stacked(router_w, correction_bias, gate, up, down, gate_s=None,
         return None if t is None else [t[e] for e in range(E)]
 
     return LayerWeights(router_w, correction_bias, split(gate), split(up), split(down), split(gate_s), split(up_s),
-                        split(down_s), sh_gate, sh_up, sh_down, sh_gate_s, sh_up_s, sh_down_s)
+                        split(down_s), sh_gate, sh_up, sh_down, sh_gate_s, sh_up_s, sh_down_s, sh_expert_gate)

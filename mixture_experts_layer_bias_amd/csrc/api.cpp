@@ -83,8 +83,9 @@ moe_status_t check_config(const moe_config_t* c) {
             c->router_width, c->num_experts);
   MOE_CHECK(c->top_k >= 1 && c->top_k <= c->router_width, MOE_ERR_INVALID, "top_k %d not in [1, router_width %d]",
             c->top_k, c->router_width);
-  MOE_CHECK(c->scoring == MOE_SCORING_SOFTMAX || c->scoring == MOE_SCORING_SIGMOID, MOE_ERR_INVALID,
-            "scoring %d is not a MOE_SCORING_* value", c->scoring);
+  MOE_CHECK(c->scoring == MOE_SCORING_SOFTMAX || c->scoring == MOE_SCORING_SIGMOID ||
+                c->scoring == MOE_SCORING_SQRTSOFTPLUS,
+            MOE_ERR_INVALID, "scoring %d is not a MOE_SCORING_* value", c->scoring);
   MOE_CHECK(c->weight_dtype == MOE_WEIGHTS_BF16 || c->weight_dtype == MOE_WEIGHTS_FP8_E4M3, MOE_ERR_INVALID,
             "weight_dtype %d is not a MOE_WEIGHTS_* value", c->weight_dtype);
   MOE_CHECK(std::isfinite(c->routed_scale), MOE_ERR_INVALID, "routed_scale is not finite");
@@ -160,6 +161,9 @@ moe_status_t check_weights(const moe_config_t* c, const moe_weights_t* w) {
       MOE_RET(check_ptr(w->sh_up_s, 4, "sh_up_s"));
       MOE_RET(check_ptr(w->sh_down_s, 4, "sh_down_s"));
     }
+    if (w->sh_expert_gate) MOE_RET(check_ptr(w->sh_expert_gate, 16, "sh_expert_gate"));
+  } else {
+    MOE_CHECK(w->sh_expert_gate == nullptr, MOE_ERR_INVALID, "sh_expert_gate is set but shared_inter is 0");
   }
   return MOE_OK;
 }
@@ -241,9 +245,17 @@ moe_status_t run_experts(const moe_config_t* cfg, const moe_weights_t* w, const 
   const moe::GroupedGemmArgs sh_dn = gemm_args(cfg, MOE_STAGE_DOWN, MOE_GROUP_SHARED, w, at(L.shared_h),
                                                static_cast<float*>(at(L.shared_h_scales)), nullptr, nullptr,
                                                at(L.shared_y), nullptr);
-  const moe::ReduceArgs red{inv_perm, ids, tw, static_cast<const uint16_t*>(x),
-                            static_cast<const uint16_t*>(at(L.shared_y)), static_cast<uint16_t*>(out),
-                            c.num_tokens, c.hidden, c.top_k, c.num_experts};
+  const moe::ReduceArgs red{inv_perm,
+                            ids,
+                            tw,
+                            static_cast<const uint16_t*>(x),
+                            static_cast<const uint16_t*>(at(L.shared_y)),
+                            c.shared_inter > 0 ? static_cast<const uint16_t*>(w->sh_expert_gate) : nullptr,
+                            static_cast<uint16_t*>(out),
+                            c.num_tokens,
+                            c.hidden,
+                            c.top_k,
+                            c.num_experts};
   if (fused) {
     if (c.shared_inter > 0) {
       MOE_RET(run_gemm(cfg, sh_gu, s));
@@ -256,8 +268,7 @@ moe_status_t run_experts(const moe_config_t* cfg, const moe_weights_t* w, const 
   if (c.shared_inter > 0) MOE_RET(run_gemm(cfg, sh_gu, s));
   MOE_RET(run_gemm(cfg, dn, s));
   if (c.shared_inter > 0) MOE_RET(run_gemm(cfg, sh_dn, s));
-  MOE_HIP(moe::launch_unpermute_reduce(static_cast<const uint16_t*>(at(L.y)), red.inv_perm, red.ids, red.w, red.x,
-                                       red.shared_y, red.out, red.N, red.H, red.K, red.E, s));
+  MOE_HIP(moe::launch_unpermute_reduce(static_cast<const uint16_t*>(at(L.y)), red, s));
   return ok();
 }
 
@@ -416,7 +427,7 @@ moe_status_t moe_grouped_gemm(const moe_config_t* cfg, int32_t stage, int32_t gr
 
 moe_status_t moe_unpermute_reduce(const moe_config_t* cfg, const void* y_sorted, const int32_t* inv_perm,
                                   const int32_t* topk_ids, const float* topk_w, const void* x,
-                                  const void* shared_y, void* out, void* stream) {
+                                  const void* shared_y, const void* shared_gate, void* out, void* stream) {
   MOE_RET(check_config(cfg));
   if (cfg->num_tokens == 0) return ok();
   MOE_RET(check_ptr(y_sorted, 16, "y_sorted"));
@@ -425,11 +436,20 @@ moe_status_t moe_unpermute_reduce(const moe_config_t* cfg, const void* y_sorted,
   MOE_RET(check_ptr(topk_w, 4, "topk_w"));
   MOE_RET(check_ptr(x, 16, "x"));
   if (shared_y) MOE_RET(check_ptr(shared_y, 16, "shared_y"));
+  if (shared_y && shared_gate) MOE_RET(check_ptr(shared_gate, 16, "shared_gate"));
   MOE_RET(check_ptr(out, 16, "out"));
-  MOE_HIP(moe::launch_unpermute_reduce(static_cast<const uint16_t*>(y_sorted), inv_perm, topk_ids, topk_w,
-                                       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(shared_y),
-                                       static_cast<uint16_t*>(out), cfg->num_tokens, cfg->hidden, cfg->top_k,
-                                       cfg->num_experts, static_cast<hipStream_t>(stream)));
+  const moe::ReduceArgs r{inv_perm,
+                          topk_ids,
+                          topk_w,
+                          static_cast<const uint16_t*>(x),
+                          static_cast<const uint16_t*>(shared_y),
+                          shared_y ? static_cast<const uint16_t*>(shared_gate) : nullptr,
+                          static_cast<uint16_t*>(out),
+                          cfg->num_tokens,
+                          cfg->hidden,
+                          cfg->top_k,
+                          cfg->num_experts};
+  MOE_HIP(moe::launch_unpermute_reduce(static_cast<const uint16_t*>(y_sorted), r, static_cast<hipStream_t>(stream)));
   return ok();
 }
 
@@ -458,9 +478,7 @@ moe_status_t moe_forward(const moe_config_t* cfg, const moe_weights_t* w, const 
   int32_t* sorted_ids = static_cast<int32_t*>(at(L.sorted_ids));
   int32_t* inv_perm = static_cast<int32_t*>(at(L.inv_perm));
   int32_t* hist = static_cast<int32_t*>(at(L.scratch));
-  const bool fp8 = c.weight_dtype == MOE_WEIGHTS_FP8_E4M3;
   const int P = c.num_tokens * c.top_k;
-
   int32_t* sync = static_cast<int32_t*>(at(L.sync));
   // small batch: router GEMM, then top-K and the sort in one block, which also zeroes the counters
   // of the one-launch decode experts path

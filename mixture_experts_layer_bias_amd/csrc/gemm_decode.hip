@@ -92,9 +92,21 @@ __device__ __forceinline__ u32x4 ld16_device_scope(const uint16_t* p) {
 // The unpermute-reduce of output columns [c0, c0 + ncols) for every token, once every down tile
 // of those columns is complete: the same sums, in the same order, as the unpermute-reduce
 // kernel.  Slots are taken 8 at a time (loads of a batch in flight together, adds in slot order).
-__device__ void reduce_columns(const ReduceArgs& r, const uint16_t* y, int c0, int ncols) {
+// With a shared-expert gate the tokens' shared weights are computed first into s_w (LDS, N
+// floats).  Called by every thread of the block.
+__device__ void reduce_columns(const ReduceArgs& r, const uint16_t* y, int c0, int ncols, float* s_w) {
   const int chunks = ncols / 8;
   const u32x4 z4 = {0u, 0u, 0u, 0u};
+  const bool gated = r.shared_y && r.shared_gate;  // the same in every thread
+  if (gated) {
+    __syncthreads();  // the caller's last LDS reads are done before s_w is written
+    const int nw = blockDim.x / kWave, wv = threadIdx.x / kWave;
+    for (int t = wv; t < r.N; t += nw) {
+      const float g = shared_gate_weight(r.x + (size_t)t * r.H, r.shared_gate, r.H);
+      if (threadIdx.x % kWave == 0) s_w[t] = g;
+    }
+    __syncthreads();
+  }
   for (int p = threadIdx.x; p < r.N * chunks; p += blockDim.x) {
     const int t = p / chunks, c = c0 + (p % chunks) * 8;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -125,7 +137,7 @@ __device__ void reduce_columns(const ReduceArgs& r, const uint16_t* y, int c0, i
     const size_t xo = (size_t)t * r.H + c;
     const u32x4 xv = zero != 0.f ? ld16(r.x + xo) : z4;
     const u32x4 sv = r.shared_y ? ld16(r.shared_y + xo) : z4;
-    st16(r.out + xo, finish_bf16x8(acc, zero, xv, r.shared_y != nullptr, sv));
+    st16(r.out + xo, finish_bf16x8(acc, zero, xv, r.shared_y != nullptr, sv, gated ? s_w[t] : 1.0f));
   }
 }
 
@@ -169,7 +181,8 @@ __device__ __forceinline__ void decode_tile(const GroupedGemmArgs& g, uint8_t* s
   if (tc.expert < 0) {  // the same decision in every thread of the block
     // FUSED with no routed rows at all (every slot took an identity expert): no down tile counts,
     // so the first NT slots reduce one column tile each
-    if (STAGE == 1 && FUSED && tc.m_tiles == 0 && block < NT) reduce_columns(*ra, nullptr, block * BNB, BNB);
+    if (STAGE == 1 && FUSED && tc.m_tiles == 0 && block < NT)
+      reduce_columns(*ra, nullptr, block * BNB, BNB, reinterpret_cast<float*>(smem) + kMaxGroups + 16);
     return;
   }
   __syncthreads();               // every wave is done with the scheduler scratch before the loads reuse it
@@ -356,7 +369,7 @@ __device__ __forceinline__ void decode_tile(const GroupedGemmArgs& g, uint8_t* s
     }
     __syncthreads();
     if (*s_last) {
-      reduce_columns(*ra, out, n0, BNB);
+      reduce_columns(*ra, out, n0, BNB, reinterpret_cast<float*>(smem) + 16);
       if (threadIdx.x == 0) {
         const int before = __hip_atomic_fetch_add(done + g.E + NT, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last[1] = before == NT - 1;

@@ -73,6 +73,7 @@ struct ReduceArgs {
   const float* w;            // [N, K] routing weights
   const uint16_t* x;         // [N, H] layer input (identity experts)
   const uint16_t* shared_y;  // [N, H] shared expert output or null
+  const uint16_t* shared_gate;  // [H] bf16 sigmoid gate row of the shared expert, or null (weight 1)
   uint16_t* out;             // [N, H]
   int N, H, K, E;
 };
@@ -85,9 +86,7 @@ hipError_t launch_decode_fused(const GroupedGemmArgs& gu, const GroupedGemmArgs&
 
 hipError_t launch_grouped_gemm_fp8(const GroupedGemmArgs& g, hipStream_t s);
 
-// a7: unpermute + weighted reduce + identity-expert and shared blends
-hipError_t launch_unpermute_reduce(const uint16_t* y_sorted, const int32_t* inv_perm, const int32_t* ids,
-                                   const float* w, const uint16_t* x, const uint16_t* shared_y, uint16_t* out, int N,
-                                   int H, int K, int E, hipStream_t s);
+// unpermute + weighted reduce + identity-expert and (gated) shared blends
+hipError_t launch_unpermute_reduce(const uint16_t* y_sorted, const ReduceArgs& r, hipStream_t s);
 
 }  // namespace moe

@@ -5,7 +5,8 @@
 // zero-computation experts).  Scoring and selection: forward.rs page,
 // MoeLayer::forward top-K arms (softmax; sigmoid + correction bias for
 // selection, unbiased weights renormalised then scaled; softmax + correction
-// bias with the zero-expert fold).
+// bias with the zero-expert fold; the DeepSeek-V4 sqrtsoftplus + correction
+// bias arm, weighted like the sigmoid one).
 #include "common.h"
 #include "kernels.h"
 
@@ -216,11 +217,17 @@ __device__ __forceinline__ int topk_token(const float* __restrict__ part, int ns
     s = wave_sum(s);
 #pragma unroll
     for (int j = 0; j < MAXJ; ++j) p[j] = p[j] / s;
-  } else {
+  } else if (scoring == 1) {
 #pragma unroll
     for (int j = 0; j < MAXJ; ++j) {
       int r = lane + 64 * j;
       p[j] = r < R ? 1.0f / (1.0f + expf(-v[j])) : 0.f;
+    }
+  } else {  // sqrt(softplus(z)), softplus(z) = ln(1 + e^z) = max(z, 0) + ln(1 + e^-|z|)
+#pragma unroll
+    for (int j = 0; j < MAXJ; ++j) {
+      int r = lane + 64 * j;
+      p[j] = r < R ? sqrtf(fmaxf(v[j], 0.f) + log1pf(expf(-fabsf(v[j])))) : 0.f;
     }
   }
   float sel[MAXJ];

@@ -26,7 +26,8 @@ def config_of(wl: mi.Workload):
 
 def weights_of(dl):
     return moe.weights_from_stacked(dl.router, dl.bias, dl.gate, dl.up, dl.down, dl.gate_s, dl.up_s, dl.down_s,
-                                    dl.sh_gate, dl.sh_up, dl.sh_down, dl.sh_gate_s, dl.sh_up_s, dl.sh_down_s)
+                                    dl.sh_gate, dl.sh_up, dl.sh_down, dl.sh_gate_s, dl.sh_up_s, dl.sh_down_s,
+                                    sh_expert_gate=dl.sh_expert_gate)
 
 
 def bits(t: torch.Tensor) -> np.ndarray:

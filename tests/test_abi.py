@@ -55,6 +55,12 @@ def test_bad_configs_are_refused(kw, status, needle):
 
 
 def test_bad_enum_values_are_refused():
+    moe.moe_workspace_size(_cfg(scoring="sqrtsoftplus"))  # the third scoring function is accepted
+    c = _cfg()
+    c.scoring = 3
+    with pytest.raises(moe.MoeError) as e:
+        moe.moe_workspace_size(c)
+    assert e.value.status == moe.MOE_ERR_INVALID
     c = _cfg()
     c.scoring = 7
     with pytest.raises(moe.MoeError) as e:
@@ -92,7 +98,8 @@ def test_null_and_misaligned_pointers_are_refused():
     st = lib.moe_route_topk(ctypes.byref(c), _fake() + 2, _fake(), None, _fake(), _fake(), _fake(), None, _fake(256),
                             moe.moe_workspace_size(c), None)
     assert st == moe.MOE_ERR_INVALID and b"aligned" in lib.moe_last_error()
-    st = lib.moe_unpermute_reduce(ctypes.byref(c), _fake(), None, _fake(), _fake(), _fake(), None, _fake(), None)
+    st = lib.moe_unpermute_reduce(ctypes.byref(c), _fake(), None, _fake(), _fake(), _fake(), None, None, _fake(),
+                                  None)
     assert st == moe.MOE_ERR_INVALID and b"inv_perm" in lib.moe_last_error()
 
 
@@ -106,9 +113,21 @@ def test_forward_refuses_small_workspace_and_missing_weights():
     st = lib.moe_forward(ctypes.byref(c), ctypes.byref(w), _fake(), _fake(), _fake(), need - 1, None)
     assert st == moe.MOE_ERR_WORKSPACE
     assert f"need {need} bytes, have {need - 1}".encode() in lib.moe_last_error()
+    w.sh_expert_gate = _fake() + 2
+    st = lib.moe_forward(ctypes.byref(c), ctypes.byref(w), _fake(), _fake(), _fake(), need, None)
+    assert st == moe.MOE_ERR_INVALID and b"sh_expert_gate" in lib.moe_last_error()
+    w.sh_expert_gate = None
     w.sh_up_w = None
     st = lib.moe_forward(ctypes.byref(c), ctypes.byref(w), _fake(), _fake(), _fake(), need, None)
     assert st == moe.MOE_ERR_INVALID and b"sh_up_w" in lib.moe_last_error()
+    # a shared-expert gate without a shared expert
+    c0 = _cfg(shared_inter=0)
+    w0 = moe.moe_weights_t()
+    for n in ("router_w", "gate_w", "up_w", "down_w", "sh_expert_gate"):
+        setattr(w0, n, _fake())
+    st = lib.moe_forward(ctypes.byref(c0), ctypes.byref(w0), _fake(), _fake(), _fake(),
+                         moe.moe_workspace_size(c0), None)
+    assert st == moe.MOE_ERR_INVALID and b"sh_expert_gate" in lib.moe_last_error()
 
 
 def test_grouped_gemm_argument_checks():

@@ -39,6 +39,14 @@ SMALL = {
     "single_token_shared": W("one_tok", 1, 512, 64, 64, 8, 256, 128, "sigmoid", True, 2.5, "bf16", True, seed=14),
     # decode-sized batch with identity experts (8 of 24 router columns) and no renormalisation
     "decode_zero_experts": W("zdec", 6, 512, 16, 24, 6, 256, 0, "softmax", False, 1.0, "bf16", True, seed=17),
+    # sqrt(softplus) scoring + correction bias, renormalised and scaled
+    "sqrtsoftplus_bias": W("ssp", 37, 256, 16, 16, 4, 128, 0, "sqrtsoftplus", True, 1.5, "bf16", True, seed=18),
+    # decode batch (one launch for the experts): sqrt(softplus) + bias, identity experts, gated shared expert
+    "decode_sqrtsoftplus_gated_shared": W("gsd", 3, 512, 32, 40, 6, 256, 128, "sqrtsoftplus", True, 2.0, "bf16",
+                                          True, seed=19, shared_gated=True),
+    # many tokens, softmax, sigmoid-gated shared expert
+    "gated_shared_150tok": W("gsp", 150, 256, 8, 8, 2, 128, 256, "softmax", True, 1.0, "bf16", False, seed=20,
+                             shared_gated=True),
 }
 FP8_SMALL = {
     "fp8_sigmoid_bias_shared": W("fp8s", 33, 512, 8, 8, 2, 256, 128, "sigmoid", True, 2.5, "fp8", True, seed=9),
@@ -46,6 +54,9 @@ FP8_SMALL = {
     "fp8_300tok_shared": W("fp8t", 300, 384, 8, 8, 3, 256, 256, "sigmoid", True, 2.5, "fp8", True, seed=11),
     # H = 8320: beyond the streaming kernel's K limit (8192), 65 scale groups per token
     "fp8_wide_hidden_8320": W("fp8h", 20, 8320, 4, 4, 2, 128, 0, "sigmoid", True, 2.5, "fp8", True, seed=15),
+    # sqrt(softplus) + bias with a gated fp8 shared expert
+    "fp8_sqrtsoftplus_gated_shared": W("fp8g", 40, 256, 8, 8, 2, 128, 128, "sqrtsoftplus", True, 2.5, "fp8", True,
+                                       seed=21, shared_gated=True),
 }
 
 
@@ -182,7 +193,8 @@ def test_stages_match_oracle(name):
     y_in = from_bits(om.f64_to_bf16(y_ref))
     moe.moe_unpermute_reduce(cfg, y_in, torch.from_numpy(oinv).cuda(), torch.from_numpy(res.ids).cuda(),
                              torch.from_numpy(res.weights.astype(np.float32)).cuda(), dl.x,
-                             None if shared_y is None else from_bits(om.f64_to_bf16(res.shared)), out)
+                             None if shared_y is None else from_bits(om.f64_to_bf16(res.shared)), out,
+                             shared_gate=dl.sh_expert_gate)
     torch.cuda.synchronize()
     assert_close(f64(out), res.out_f64, BF16_TOL, "unpermute-reduce output")
 
@@ -345,7 +357,7 @@ def test_forward_matches_oracle_and_composed_stages(name):
         moe.moe_grouped_gemm(cfg, 0, 1, w, a, a_sc, None, None, shh, shs)
         moe.moe_grouped_gemm(cfg, 1, 1, w, shh, shs, None, None, shy)
     out2 = torch.empty_like(out)
-    moe.moe_unpermute_reduce(cfg, y, inv, ids, tw, dl.x, shy, out2)
+    moe.moe_unpermute_reduce(cfg, y, inv, ids, tw, dl.x, shy, out2, shared_gate=dl.sh_expert_gate)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
 
@@ -376,7 +388,8 @@ def test_decode_forward_is_deterministic():
 
 
 @pytest.mark.parametrize("name", ["decode", "tiny", "single_token_shared", "decode_zero_experts",
-                                  "many_tiles_300tok", "fp8_sigmoid_bias_shared"])
+                                  "decode_sqrtsoftplus_gated_shared", "many_tiles_300tok",
+                                  "fp8_sigmoid_bias_shared"])
 def test_experts_forward_matches_forward(name):
     """moe_experts_forward on moe_forward's own routing gives moe_forward's bits, on two calls in a
     row over one workspace (the decode path's counters are back at zero after each call)."""
