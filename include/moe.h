@@ -65,6 +65,12 @@ typedef struct {
   int32_t renormalize;  /* nonzero: divide the K weights by their sum */
   float routed_scale;   /* multiplies the (renormalised) weights */
   int32_t weight_dtype; /* MOE_WEIGHTS_*: type of the expert (routed and shared) weights */
+  int32_t row_invariant; /* 0 or 1.  1: every token's output bits are independent of the batch it
+                            comes in (forward_prefill.rs page, prefill_row_invariant: a prompt's rows
+                            get the same bits in a cold pass and in a short replay of its tail).  The
+                            same kernels and sum orders then run at every N (the router split fixed by
+                            H, the general grouped GEMMs, the separate reduce), at the cost of the
+                            decode-shaped kernels' speed.  0: the fastest kernels for each N. */
 } moe_config_t;
 
 /* Weights of one layer.  The router is always bf16.  Routed experts are reached

@@ -43,7 +43,7 @@ class moe_config_t(ctypes.Structure):
     _fields_ = [("num_tokens", ctypes.c_int32), ("hidden", ctypes.c_int32), ("num_experts", ctypes.c_int32),
                 ("router_width", ctypes.c_int32), ("top_k", ctypes.c_int32), ("inter", ctypes.c_int32),
                 ("shared_inter", ctypes.c_int32), ("scoring", ctypes.c_int32), ("renormalize", ctypes.c_int32),
-                ("routed_scale", ctypes.c_float), ("weight_dtype", ctypes.c_int32)]
+                ("routed_scale", ctypes.c_float), ("weight_dtype", ctypes.c_int32), ("row_invariant", ctypes.c_int32)]
 
 
 class moe_weights_t(ctypes.Structure):
@@ -109,12 +109,13 @@ def _check(status: int) -> None:
 
 def make_config(num_tokens: int, hidden: int, num_experts: int, router_width: int, top_k: int, inter: int,
                 shared_inter: int = 0, scoring: str = "softmax", renormalize: bool = True,
-                routed_scale: float = 1.0, weight_dtype: str = "bf16") -> moe_config_t:
+                routed_scale: float = 1.0, weight_dtype: str = "bf16", row_invariant: bool = False) -> moe_config_t:
     return moe_config_t(num_tokens, hidden, num_experts, router_width, top_k, inter, shared_inter,
                         {"softmax": MOE_SCORING_SOFTMAX, "sigmoid": MOE_SCORING_SIGMOID,
                          "sqrtsoftplus": MOE_SCORING_SQRTSOFTPLUS}[scoring],
                         1 if renormalize else 0, routed_scale,
-                        {"bf16": MOE_WEIGHTS_BF16, "fp8": MOE_WEIGHTS_FP8_E4M3}[weight_dtype])
+                        {"bf16": MOE_WEIGHTS_BF16, "fp8": MOE_WEIGHTS_FP8_E4M3}[weight_dtype],
+                        1 if row_invariant else 0)
 
 
 def config_with_tokens(cfg: moe_config_t, n: int) -> moe_config_t:

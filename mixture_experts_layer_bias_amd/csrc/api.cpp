@@ -89,6 +89,8 @@ moe_status_t check_config(const moe_config_t* c) {
   MOE_CHECK(c->weight_dtype == MOE_WEIGHTS_BF16 || c->weight_dtype == MOE_WEIGHTS_FP8_E4M3, MOE_ERR_INVALID,
             "weight_dtype %d is not a MOE_WEIGHTS_* value", c->weight_dtype);
   MOE_CHECK(std::isfinite(c->routed_scale), MOE_ERR_INVALID, "routed_scale is not finite");
+  MOE_CHECK(c->row_invariant == 0 || c->row_invariant == 1, MOE_ERR_INVALID, "row_invariant %d is not 0 or 1",
+            c->row_invariant);
   MOE_CHECK(c->hidden > 0 && c->inter > 0 && c->shared_inter >= 0, MOE_ERR_INVALID,
             "hidden %d, inter %d must be > 0 and shared_inter %d >= 0", c->hidden, c->inter, c->shared_inter);
   MOE_CHECK(c->router_width <= 1024, MOE_ERR_UNSUPPORTED, "router_width %d > 1024", c->router_width);
@@ -123,7 +125,7 @@ void compute_layout(const moe_config_t* c, moe_workspace_layout_t* L) {
   L->offsets = take((R + 1) * 4);
   L->sorted_ids = take(P * 4);
   L->inv_perm = take(P * 4);
-  const int slices = moe::router_slices((int)N, (int)H, (int)R);
+  const int slices = moe::router_slices((int)N, (int)H, (int)R, c->row_invariant != 0);
   const size_t hist_bytes = ((size_t)moe::permute_chunks((int)P) + 1) * R * 4;  // chunk histograms + bucket totals
   const size_t part_bytes = slices > 1 ? (size_t)slices * N * R * 4 : 0;
   L->scratch = take(hist_bytes > part_bytes ? hist_bytes : part_bytes);
@@ -198,6 +200,7 @@ moe::GroupedGemmArgs gemm_args(const moe_config_t* c, int stage, int group, cons
   g.sh_down_s = w->sh_down_s;
   g.out = out;
   g.out_scales = out_scales;
+  g.row_invariant = c->row_invariant;
   return g;
 }
 
@@ -212,7 +215,7 @@ moe_status_t run_gemm(const moe_config_t* c, const moe::GroupedGemmArgs& g, hipS
 
 // Whether the decode experts path (routed gate/up, down and the reduce in one launch) applies.
 bool experts_fused(const moe_config_t* c) {
-  if (c->weight_dtype != MOE_WEIGHTS_BF16) return false;
+  if (c->weight_dtype != MOE_WEIGHTS_BF16 || c->row_invariant) return false;
   const moe_weights_t none{};  // the fit is a function of the sizes only
   const moe::GroupedGemmArgs gu = gemm_args(c, MOE_STAGE_GATE_UP, MOE_GROUP_ROUTED, &none, nullptr, nullptr,
                                             nullptr, nullptr, nullptr, nullptr);
@@ -274,10 +277,11 @@ moe_status_t run_experts(const moe_config_t* cfg, const moe_weights_t* w, const 
 
 moe_status_t launch_route(const moe_config_t* c, const void* x, const void* router_w, const float* bias,
                           float* logits, int32_t* ids, float* tw, float* zw, float* scratch, hipStream_t s) {
-  const int slices = moe::router_slices(c->num_tokens, c->hidden, c->router_width);
+  const bool inv = c->row_invariant != 0;
+  const int slices = moe::router_slices(c->num_tokens, c->hidden, c->router_width, inv);
   float* part = slices > 1 ? scratch : logits;
   MOE_HIP(moe::launch_router_logits(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(router_w), part,
-                                    c->num_tokens, c->hidden, c->router_width, slices, s));
+                                    c->num_tokens, c->hidden, c->router_width, slices, inv, s));
   MOE_HIP(moe::launch_topk(part, slices, logits, bias, ids, tw, zw, c->num_tokens, c->router_width, c->num_experts,
                            c->top_k, c->scoring, c->renormalize, c->routed_scale, s));
   return MOE_OK;
@@ -485,10 +489,11 @@ moe_status_t moe_forward(const moe_config_t* cfg, const moe_weights_t* w, const 
   const bool small = moe::topk_sort_small_fits(c.num_tokens, c.top_k);
   const bool fused = small && experts_fused(cfg);
   if (small) {
-    const int slices = moe::router_slices(c.num_tokens, c.hidden, c.router_width);
+    const bool inv = c.row_invariant != 0;
+    const int slices = moe::router_slices(c.num_tokens, c.hidden, c.router_width, inv);
     float* part = slices > 1 ? reinterpret_cast<float*>(hist) : logits;
     MOE_HIP(moe::launch_router_logits(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w->router_w),
-                                      part, c.num_tokens, c.hidden, c.router_width, slices, s));
+                                      part, c.num_tokens, c.hidden, c.router_width, slices, inv, s));
     MOE_HIP(moe::launch_topk_sort_small(part, slices, logits, w->correction_bias, ids, tw, zw, counts, offsets,
                                         sorted_ids, inv_perm, fused ? sync : nullptr,
                                         moe::decode_fused_counters(c.num_experts, c.hidden), c.num_tokens,

@@ -167,7 +167,7 @@ hipError_t launch_grouped_gemm_bf16(const GroupedGemmArgs& g, hipStream_t s) {
   const int groups = g.shared ? 1 : g.E;
   const int rows = g.shared ? g.N : g.P;
   if (rows == 0) return hipSuccess;
-  if (decode_gemm_fits(g)) return launch_grouped_gemm_decode(g, s);
+  if (!g.row_invariant && decode_gemm_fits(g)) return launch_grouped_gemm_decode(g, s);
   if (g.stage == 0) {
     k_grouped_gemm_bf16<0><<<grouped_grid(rows, groups, BM, g.I / BN), 256, 0, s>>>(g);
   } else {

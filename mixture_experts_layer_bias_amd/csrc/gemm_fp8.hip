@@ -481,7 +481,8 @@ hipError_t launch_grouped_gemm_fp8(const GroupedGemmArgs& g, hipStream_t s) {
   // gate/up (every token, one group) also runs faster on the streaming kernel, its down stage on
   // the register-staged one
   const int kd = g.stage == 0 ? g.H : g.I;
-  if ((rows <= 256L * groups || (g.shared && g.stage == 0)) && kd <= 128 * SMAXKB && (g.stage == 0 || g.H % SBNB == 0))
+  if (!g.row_invariant && (rows <= 256L * groups || (g.shared && g.stage == 0)) && kd <= 128 * SMAXKB &&
+      (g.stage == 0 || g.H % SBNB == 0))
     return g.stage == 0 ? launch_stream<0>(g, groups, rows, g.I / (SBNB / 2), s)
                         : launch_stream<1>(g, groups, rows, g.H / SBNB, s);
   if (g.stage == 0) {

@@ -14,9 +14,10 @@ hipError_t ensure_dynamic_lds(const void* kernel, int bytes);
 // a1 + a2: router logits (split over `slices` parts of H, each writing an [N, R]
 // partial plane) and top-K selection (adds the planes in order; when slices > 1
 // it also writes the summed logits to `logits`)
-int router_slices(int N, int H, int R);
+// row_invariant: the MFMA kernel at every N with a split that depends on H only (no GEMV)
+int router_slices(int N, int H, int R, bool row_invariant);
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* router_w, float* part, int N, int H, int R,
-                                int slices, hipStream_t s);
+                                int slices, bool row_invariant, hipStream_t s);
 hipError_t launch_topk(const float* part, int slices, float* logits, const float* bias, int32_t* ids, float* w,
                        float* zero_w, int N, int R, int E, int K, int scoring, int renormalize, float routed_scale,
                        hipStream_t s);
@@ -61,6 +62,7 @@ struct GroupedGemmArgs {
   const float* sh_down_s;
   void* out;           // gate/up: h [rows, I] (bf16 or e4m3); down: y [rows, H] bf16
   float* out_scales;   // fp8 gate/up only: [rows, I/128]
+  int row_invariant;   // 1: only the kernels whose per-row arithmetic is the same at any row count
 };
 hipError_t launch_grouped_gemm_bf16(const GroupedGemmArgs& g, hipStream_t s);
 // bf16 streaming kernel for a few rows per expert (decode)

@@ -367,7 +367,12 @@ __global__ __launch_bounds__(1024) void k_topk_sort_small(const float* __restric
   }
 }
 
-int router_slices(int N, int H, int R) {
+int router_slices(int N, int H, int R, bool row_invariant) {
+  if (row_invariant) {  // a function of H only: the largest power of two <= 16 dividing H / 128
+    int S = 1;
+    while (S < 16 && (H / 128) % (2 * S) == 0) S *= 2;
+    return S;
+  }
   if (N <= RG_MAXN) return 1;  // the GEMV router writes whole logits
   const long tiles = (long)((N + RT_BM - 1) / RT_BM) * ((R + RT_BN - 1) / RT_BN);
   int S = 1;
@@ -376,9 +381,9 @@ int router_slices(int N, int H, int R) {
 }
 
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* router_w, float* part, int N, int H, int R,
-                                int slices, hipStream_t s) {
+                                int slices, bool row_invariant, hipStream_t s) {
   if (N == 0) return hipSuccess;
-  if (N <= RG_MAXN) {
+  if (N <= RG_MAXN && !row_invariant) {
     const unsigned blocks = (unsigned)((R + 3) / 4);
     if (N <= 4) k_router_gemv<4, 4><<<blocks, 256, 0, s>>>(x, router_w, part, N, H, R);
     else k_router_gemv<8, 2><<<blocks, 256, 0, s>>>(x, router_w, part, N, H, R);

@@ -70,6 +70,12 @@ def test_bad_enum_values_are_refused():
     c.weight_dtype = 5
     with pytest.raises(moe.MoeError):
         moe.moe_workspace_size(c)
+    moe.moe_workspace_size(_cfg(row_invariant=True))
+    c = _cfg()
+    c.row_invariant = 2
+    with pytest.raises(moe.MoeError) as e:
+        moe.moe_workspace_size(c)
+    assert e.value.status == moe.MOE_ERR_INVALID and "row_invariant" in e.value.message
 
 
 def test_workspace_size_and_layout():

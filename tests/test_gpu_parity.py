@@ -414,6 +414,34 @@ def test_experts_forward_matches_forward(name):
         assert int(ws2[L["sync"]:].view(torch.int32)[:nsync].abs().sum()) == 0, f"counters after call {i}"
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_row_invariant_mode_gives_each_token_the_same_bits_in_any_batch(dtype):
+    """With row_invariant set, a token's output bits do not depend on the batch it comes in: the
+    rows of a 200-token batch equal those of a 5-token tail, a single token and the first 100
+    tokens run on their own (the short batches would otherwise take the decode-shaped kernels).
+    The whole batch also matches the oracle."""
+    wl = W("rinv", 200, 512, 16, 20, 4, 256, 128, "sigmoid", True, 2.0, dtype, True, seed=22, shared_gated=True)
+    print(f"\n[case] row-invariant {dtype}", flush=True)
+    dl = mi.device.device_layer(wl)
+    w = weights_of(dl)
+    mk = lambda n: moe.make_config(n, wl.hidden, wl.num_experts, wl.router_width, wl.top_k, wl.inter,
+                                   wl.shared_inter, wl.scoring, wl.renormalize, wl.routed_scale, dtype,
+                                   row_invariant=True)
+    full, _ = run_forward(mk(200), w, dl.x)
+    for lo, hi in [(195, 200), (7, 8), (0, 100)]:
+        part, _ = run_forward(mk(hi - lo), w, dl.x[lo:hi].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(part.view(torch.int16), full[lo:hi].view(torch.int16)), f"tokens {lo}:{hi}"
+    res = ow.run(wl)
+    L = moe.moe_workspace_layout(mk(200))
+    ws = torch.empty(moe.moe_workspace_size(mk(200)), dtype=torch.uint8, device="cuda")
+    moe.moe_forward(mk(200), w, dl.x, full, ws)
+    torch.cuda.synchronize()
+    gids = ws[L["topk_ids"]:L["topk_ids"] + 4 * 200 * 4].view(torch.int32).cpu().numpy().reshape(200, 4)
+    same = check_routing(gids, res, 4)
+    assert_close(f64(full)[same], res.out_f64[same], _tol(wl), "row-invariant output")
+
+
 def test_decode_every_slot_an_identity_expert():
     """A correction bias that puts every top-K pick on an identity expert: no routed rows at all, so
     out = zero_accum * x + the shared expert."""
