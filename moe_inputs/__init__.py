@@ -46,7 +46,7 @@ class Workload:
     scoring: str  # "softmax" | "sigmoid" | "sqrtsoftplus"
     renormalize: bool
     routed_scale: float
-    weight_dtype: str  # "bf16" | "fp8"
+    weight_dtype: str  # "bf16" | "fp8" | "mxfp4"
     has_bias: bool
     zipf_s: float = 0.0  # > 0: skewed router column (prefill workload)
     zipf_tau: float = 0.0
@@ -113,7 +113,8 @@ def _host_lib():
         lib.mi_host_fill_bf16.argtypes = [vp, u64, u64, u64, u32, u32, f32]
         lib.mi_host_fill_f32.argtypes = [vp, u64, u64, u64, u32, u32, f32]
         lib.mi_host_fill_e4m3.argtypes = [vp, vp, u32, u32, u64, u32, u32, f32]
-        for f in (lib.mi_host_fill_bf16, lib.mi_host_fill_f32, lib.mi_host_fill_e4m3):
+        lib.mi_host_fill_mxfp4.argtypes = [vp, vp, u32, u32, u64, u32, u32, f32]
+        for f in (lib.mi_host_fill_bf16, lib.mi_host_fill_f32, lib.mi_host_fill_e4m3, lib.mi_host_fill_mxfp4):
             f.restype = None
         _host = lib
     return _host
@@ -129,7 +130,8 @@ def _dev_lib():
         lib.mi_dev_fill_bf16.argtypes = [vp, u64, u64, u64, u32, u32, f32, vp]
         lib.mi_dev_fill_f32.argtypes = [vp, u64, u64, u64, u32, u32, f32, vp]
         lib.mi_dev_fill_e4m3.argtypes = [vp, vp, u32, u32, u64, u32, u32, f32, vp]
-        for f in (lib.mi_dev_fill_bf16, lib.mi_dev_fill_f32, lib.mi_dev_fill_e4m3):
+        lib.mi_dev_fill_mxfp4.argtypes = [vp, vp, u32, u32, u64, u32, u32, f32, vp]
+        for f in (lib.mi_dev_fill_bf16, lib.mi_dev_fill_f32, lib.mi_dev_fill_e4m3, lib.mi_dev_fill_mxfp4):
             f.restype = ctypes.c_int
         _dev = lib
     return _dev
@@ -155,6 +157,14 @@ def host_e4m3(rows: int, cols: int, seed: int, tag: int, sub: int, sigma: float)
     q = np.empty((rows, cols), dtype=np.uint8)
     s = np.empty(((rows + 127) // 128, (cols + 127) // 128), dtype=np.float32)
     _host_lib().mi_host_fill_e4m3(q.ctypes.data, s.ctypes.data, rows, cols, seed, tag, sub, sigma)
+    return q, s
+
+
+def host_mxfp4(rows: int, cols: int, seed: int, tag: int, sub: int, sigma: float):
+    """MXFP4 matrix: (packed E2M1 codes uint8 [rows, cols/2], E8M0 scale codes uint8 [rows, cols/32])."""
+    q = np.empty((rows, cols // 2), dtype=np.uint8)
+    s = np.empty((rows, cols // 32), dtype=np.uint8)
+    _host_lib().mi_host_fill_mxfp4(q.ctypes.data, s.ctypes.data, rows, cols, seed, tag, sub, sigma)
     return q, s
 
 
@@ -240,8 +250,8 @@ def host_expert(wl: Workload, e: int, layer: int = 0):
     if wl.weight_dtype == "bf16":
         return (host_bf16((I, H), seed, TAG_GATE, e, SIGMA_W), host_bf16((I, H), seed, TAG_UP, e, SIGMA_W),
                 host_bf16((H, I), seed, TAG_DOWN, e, SIGMA_W))
-    return (host_e4m3(I, H, seed, TAG_GATE, e, SIGMA_W), host_e4m3(I, H, seed, TAG_UP, e, SIGMA_W),
-            host_e4m3(H, I, seed, TAG_DOWN, e, SIGMA_W))
+    q = host_mxfp4 if wl.weight_dtype == "mxfp4" else host_e4m3
+    return (q(I, H, seed, TAG_GATE, e, SIGMA_W), q(I, H, seed, TAG_UP, e, SIGMA_W), q(H, I, seed, TAG_DOWN, e, SIGMA_W))
 
 
 def host_shared(wl: Workload, layer: int = 0):
@@ -253,8 +263,9 @@ def host_shared(wl: Workload, layer: int = 0):
     if wl.weight_dtype == "bf16":
         return (host_bf16((Is, H), seed, TAG_SH_GATE, 0, SIGMA_W), host_bf16((Is, H), seed, TAG_SH_UP, 0, SIGMA_W),
                 host_bf16((H, Is), seed, TAG_SH_DOWN, 0, SIGMA_W))
-    return (host_e4m3(Is, H, seed, TAG_SH_GATE, 0, SIGMA_W), host_e4m3(Is, H, seed, TAG_SH_UP, 0, SIGMA_W),
-            host_e4m3(H, Is, seed, TAG_SH_DOWN, 0, SIGMA_W))
+    q = host_mxfp4 if wl.weight_dtype == "mxfp4" else host_e4m3
+    return (q(Is, H, seed, TAG_SH_GATE, 0, SIGMA_W), q(Is, H, seed, TAG_SH_UP, 0, SIGMA_W),
+            q(H, Is, seed, TAG_SH_DOWN, 0, SIGMA_W))
 
 
 def host_shared_gate(wl: Workload, layer: int = 0) -> Optional[np.ndarray]:
@@ -282,6 +293,13 @@ def dev_f32(t, seed: int, tag: int, sub: int, sigma: float, stream=None, first: 
     import torch
     s = stream if stream is not None else torch.cuda.current_stream().cuda_stream
     _check(_dev_lib().mi_dev_fill_f32(t.data_ptr(), t.numel(), first, seed, tag, sub, sigma, s), "fill_f32")
+
+
+def dev_mxfp4(q, scales, rows: int, cols: int, seed: int, tag: int, sub: int, sigma: float, stream=None) -> None:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream().cuda_stream
+    _check(_dev_lib().mi_dev_fill_mxfp4(q.data_ptr(), scales.data_ptr(), rows, cols, seed, tag, sub, sigma, s),
+           "fill_mxfp4")
 
 
 def dev_e4m3(q, scales, rows: int, cols: int, seed: int, tag: int, sub: int, sigma: float, stream=None) -> None:

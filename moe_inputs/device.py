@@ -14,7 +14,7 @@ import torch
 
 from . import (SIGMA_BIAS, SIGMA_W, SIGMA_X, TAG_BIAS, TAG_DOWN, TAG_GATE, TAG_ROUTER, TAG_SH_DOWN,
                TAG_SH_EXPERT_GATE, TAG_SH_GATE, TAG_SH_UP, TAG_UP, TAG_X, Workload, dev_bf16, dev_e4m3, dev_f32,
-               zipf_router_column)
+               dev_mxfp4, zipf_router_column)
 
 
 @dataclasses.dataclass
@@ -39,6 +39,11 @@ class DeviceLayer:
 
 
 def _mat(rows, cols, seed, tag, sub, fp8, device):
+    if fp8 == "mxfp4":
+        q = torch.empty((rows, cols // 2), dtype=torch.uint8, device=device)
+        s = torch.empty((rows, cols // 32), dtype=torch.uint8, device=device)
+        dev_mxfp4(q, s, rows, cols, seed, tag, sub, SIGMA_W)
+        return q, s
     if not fp8:
         t = torch.empty((rows, cols), dtype=torch.bfloat16, device=device)
         dev_bf16(t, seed, tag, sub, SIGMA_W)
@@ -50,6 +55,12 @@ def _mat(rows, cols, seed, tag, sub, fp8, device):
 
 
 def _stack(E, rows, cols, seed, tag, fp8, device):
+    if fp8 == "mxfp4":
+        w = torch.empty((E, rows, cols // 2), dtype=torch.uint8, device=device)
+        s = torch.empty((E, rows, cols // 32), dtype=torch.uint8, device=device)
+        for e in range(E):
+            dev_mxfp4(w[e], s[e], rows, cols, seed, tag, e, SIGMA_W)
+        return w, s
     dt = torch.uint8 if fp8 else torch.bfloat16
     w = torch.empty((E, rows, cols), dtype=dt, device=device)
     s = torch.empty((E, (rows + 127) // 128, (cols + 127) // 128), dtype=torch.float32, device=device) if fp8 else None
@@ -64,7 +75,7 @@ def _stack(E, rows, cols, seed, tag, fp8, device):
 def device_layer(wl: Workload, layer: int = 0, device: str = "cuda", x_only: bool = False) -> DeviceLayer:
     seed = wl.seed + layer
     N, H, E, R, I, Is = wl.num_tokens, wl.hidden, wl.num_experts, wl.router_width, wl.inter, wl.shared_inter
-    fp8 = wl.weight_dtype == "fp8"
+    fp8 = {"bf16": False, "fp8": True, "mxfp4": "mxfp4"}[wl.weight_dtype]
     x = torch.empty((N, H), dtype=torch.bfloat16, device=device)
     dev_bf16(x, seed, TAG_X, 0, SIGMA_X)
     router = torch.empty((R, H), dtype=torch.bfloat16, device=device)

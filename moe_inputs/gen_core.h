@@ -21,6 +21,14 @@
  * e4m3 tensors          = per 128x128 block of value(): S = fp32(amax / 448),
  *                         code = e4m3fn_rne_satfinite(fp32(v / S)); a zero block
  *                         has S = 1.  (OCP FP8 E4M3: bias 7, max 448, no inf.)
+ * mxfp4 tensors         = per row, per 32 consecutive columns of value() (the OCP
+ *                         Microscaling Formats v1.0 recipe for MXFP4): shared
+ *                         exponent X = floor(log2(amax)) - 2 (2 = the largest
+ *                         E2M1 exponent), scale code = X + 127 (E8M0), element
+ *                         code = e2m1_rne_sat(v * 2^-X) (OCP FP4 E2M1: values
+ *                         0, 0.5, 1, 1.5, 2, 3, 4, 6; beyond 6 saturates); a
+ *                         zero block gets scale code 127 and zero codes.
+ *                         Two codes per byte, the even column in the low nibble.
  * mix64 is the SplitMix64 output function (Steele, Lea and Flood, "Fast
  * splittable pseudorandom number generators", OOPSLA 2014).
  */
@@ -123,5 +131,34 @@ MI_FN uint8_t mi_e4m3_rne_sat(float f) {
   if (code > 0x7Eu) code = 0x7Eu;
   return (uint8_t)(sign | code);
 }
+
+/* fp32 -> OCP FP4 E2M1 code (sign in bit 3), round to nearest with ties to the even code,
+ * finite values beyond 6 saturate to 6.  The magnitude codes 0..7 are 0, 0.5, 1, 1.5, 2, 3, 4, 6,
+ * so each threshold below is the midpoint of two neighbours, assigned to the even code. */
+MI_FN uint8_t mi_e2m1_rne_sat(float f) {
+  uint8_t sign = (uint8_t)((mi_f32_bits(f) >> 28) & 0x8u);
+  float a = f < 0.0f ? -f : f;
+  uint8_t c;
+  if (a <= 0.25f) c = 0;
+  else if (a < 0.75f) c = 1;
+  else if (a <= 1.25f) c = 2;
+  else if (a < 1.75f) c = 3;
+  else if (a <= 2.5f) c = 4;
+  else if (a < 3.5f) c = 5;
+  else if (a <= 5.0f) c = 6;
+  else c = 7;
+  return (uint8_t)(sign | c);
+}
+
+/* E8M0 scale code of a 32-element block with maximum magnitude amax (a normal fp32 value or 0) */
+MI_FN uint8_t mi_mx_scale_code(float amax) {
+  if (!(amax > 0.0f)) return 127u;
+  int e = (int)((mi_f32_bits(amax) >> 23) & 0xFFu) - 127; /* floor(log2(amax)) */
+  int code = e - 2 + 127;
+  return (uint8_t)(code < 0 ? 0 : (code > 254 ? 254 : code));
+}
+
+/* 2^-(code - 127) as fp32 (exact for the codes that occur here) */
+MI_FN float mi_mx_inv_scale(uint8_t code) { return mi_bits_f32((uint32_t)(254 - code) << 23); }
 
 #endif

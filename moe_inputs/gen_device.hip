@@ -45,6 +45,25 @@ __global__ void __launch_bounds__(256) mi_k_fill_e4m3(uint8_t* q, float* scales,
   }
 }
 
+// One thread per 32-element block of an MXFP4 matrix (same recipe as the host fill).
+__global__ void __launch_bounds__(256) mi_k_fill_mxfp4(uint8_t* q, uint8_t* scales, uint64_t nb, uint64_t key,
+                                                       float sigma) {
+  for (uint64_t b = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nb; b += (uint64_t)gridDim.x * blockDim.x) {
+    uint64_t e0 = b * 32;
+    float v[32], amax = 0.0f;
+    for (int j = 0; j < 32; ++j) {
+      v[j] = mi_value(key, e0 + (uint64_t)j, sigma);
+      amax = fmaxf(amax, fabsf(v[j]));
+    }
+    uint8_t sc = mi_mx_scale_code(amax);
+    float inv = mi_mx_inv_scale(sc);
+    scales[b] = sc;
+    for (int j = 0; j < 32; j += 2)
+      q[e0 / 2 + (uint64_t)(j / 2)] =
+          (uint8_t)(mi_e2m1_rne_sat(v[j] * inv) | (mi_e2m1_rne_sat(v[j + 1] * inv) << 4));
+  }
+}
+
 static unsigned grid_for(uint64_t n) {
   uint64_t g = (n + 255) / 256;
   return (unsigned)(g > 65536 ? 65536 : (g == 0 ? 1 : g));
@@ -61,6 +80,14 @@ extern "C" int mi_dev_fill_f32(void* out, uint64_t n, uint64_t first, uint64_t s
                                float sigma, hipStream_t stream) {
   if (n == 0) return 0;
   mi_k_fill_f32<<<grid_for(n), 256, 0, stream>>>((float*)out, n, first, mi_key(seed, tag, sub), sigma);
+  return (int)hipGetLastError();
+}
+
+extern "C" int mi_dev_fill_mxfp4(void* q, void* scales, uint32_t rows, uint32_t cols, uint64_t seed, uint32_t tag,
+                                 uint32_t sub, float sigma, hipStream_t stream) {
+  uint64_t nb = (uint64_t)rows * (cols / 32);
+  if (nb == 0) return 0;
+  mi_k_fill_mxfp4<<<grid_for(nb), 256, 0, stream>>>((uint8_t*)q, (uint8_t*)scales, nb, mi_key(seed, tag, sub), sigma);
   return (int)hipGetLastError();
 }
 

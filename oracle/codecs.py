@@ -1,4 +1,5 @@
-"""Number formats used by the oracle: bfloat16 and OCP FP8 E4M3 (e4m3fn).
+"""Number formats used by the oracle: bfloat16, OCP FP8 E4M3 (e4m3fn) and the
+OCP Microscaling MXFP4 weight format (FP4 E2M1 elements, E8M0 block scales).
 
 TEST INFRASTRUCTURE ONLY.  See ``oracle/__init__.py``.
 
@@ -82,3 +83,34 @@ def e4m3_encode(v: np.ndarray) -> np.ndarray:
     code = np.where(pick_hi, hi, lo).astype(np.uint8)
     code = np.where(a == _POS_VALUES[hi], hi, code).astype(np.uint8)
     return np.where(np.signbit(v), code | np.uint8(0x80), code).astype(np.uint8)
+
+
+# ----------------------------------------------------------------------------- MXFP4
+
+def e2m1_decode(codes: np.ndarray) -> np.ndarray:
+    """FP4 E2M1 codes (low 4 bits) -> float64, from the bit-field definition of the OCP
+    Microscaling Formats (MX) v1.0 spec: sign bit, 2 exponent bits with bias 1, 1
+    mantissa bit, exponent field 0 is subnormal (0 or 0.5); no infinities or NaN."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64) & 0xF
+    sign = np.where(c & 0x8, -1.0, 1.0)
+    exp = (c >> 1) & 0x3
+    man = c & 0x1
+    val = np.where(exp == 0, man * 0.5, (1.0 + man / 2.0) * np.ldexp(1.0, (exp - 1).astype(np.int64)))
+    return sign * val
+
+
+def e8m0_decode(codes: np.ndarray) -> np.ndarray:
+    """E8M0 scale codes -> 2^(code - 127) as float64 (255 is NaN)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    return np.where(c == 255, np.nan, np.ldexp(1.0, c - 127))
+
+
+def mxfp4_dequant(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """An MXFP4 matrix -> float64 (exact): packed [rows, cols/2] holds two E2M1 codes per byte
+    (the even column in the low nibble), scales [rows, cols/32] one E8M0 code per row and
+    32 consecutive columns."""
+    p = np.asarray(packed, dtype=np.uint8)
+    codes = np.empty((p.shape[0], p.shape[1] * 2), dtype=np.uint8)
+    codes[:, 0::2] = p & 0xF
+    codes[:, 1::2] = p >> 4
+    return e2m1_decode(codes) * np.repeat(e8m0_decode(scales), 32, axis=1)

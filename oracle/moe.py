@@ -41,7 +41,7 @@ from typing import Callable, Optional
 
 import numpy as np
 
-from .codecs import bf16_to_f64, e4m3_decode, e4m3_encode, f64_to_bf16
+from .codecs import bf16_to_f64, e4m3_decode, e4m3_encode, f64_to_bf16, mxfp4_dequant
 
 FP8_BLOCK = 128
 E4M3_MAX = 448.0
@@ -60,7 +60,7 @@ class MoeConfig:
     scoring: str  # scoring_func: "softmax" | "sigmoid" | "sqrtsoftplus"
     renormalize: bool  # norm_topk_prob
     routed_scale: float  # routed_scaling_factor
-    weight_dtype: str  # "bf16" | "fp8"
+    weight_dtype: str  # "bf16" | "fp8" | "mxfp4" (fp8 and mxfp4 experts take fp8 activations)
 
 
 # ----------------------------------------------------------------------------- routing
@@ -194,7 +194,11 @@ def dequant_rows(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
 
 
 def dequant_blocks(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
-    """A weight matrix of codes with one scale per 128x128 block -> float64 (exact)."""
+    """A weight matrix -> float64 (exact).  e4m3 codes with one fp32 scale per 128x128 block,
+    or MXFP4 (packed E2M1 codes with one E8M0 scale per row and 32 columns; the scales are
+    uint8 then)."""
+    if scales.dtype == np.uint8:
+        return mxfp4_dequant(codes, scales)
     s = np.repeat(np.repeat(scales.astype(np.float64), FP8_BLOCK, axis=0), FP8_BLOCK, axis=1)
     return e4m3_decode(codes) * s[: codes.shape[0], : codes.shape[1]]
 
@@ -316,7 +320,7 @@ def moe_forward(cfg: MoeConfig, x_bits: np.ndarray, router_bits: np.ndarray, bia
     w, zero_accum = routing_weights(p, ids, cfg.renormalize, cfg.routed_scale, E)
 
     x64 = bf16_to_f64(x_bits)
-    if cfg.weight_dtype == "fp8":
+    if cfg.weight_dtype != "bf16":  # fp8 and mxfp4 experts: e4m3 activations, per-128 scales
         xq, xs = quantize_fp8_groups(x64.astype(np.float32))
     routed = np.zeros((n, cfg.hidden), dtype=np.float64)
     for e in np.unique(ids[ids < E]):  # expert-major: fetch each touched expert once

@@ -70,6 +70,57 @@ def test_e4m3_roundtrip_every_code():
 
 # ============================================================================ routing
 
+# OCP Microscaling Formats (MX) v1.0, FP4 E2M1: the eight magnitudes of codes 0..7
+E2M1_MAGNITUDES = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def test_e2m1_decode_is_the_published_table():
+    got = codecs.e2m1_decode(np.arange(16, dtype=np.uint8))
+    assert list(got[:8]) == E2M1_MAGNITUDES
+    assert list(-got[8:]) == E2M1_MAGNITUDES and all(np.signbit(got[8:]))
+
+
+def test_e8m0_decode_is_a_power_of_two():
+    got = codecs.e8m0_decode(np.array([0, 1, 120, 127, 128, 254, 255], dtype=np.uint8))
+    assert list(got[:6]) == [2.0**-127, 2.0**-126, 2.0**-7, 1.0, 2.0, 2.0**127] and np.isnan(got[6])
+
+
+def _mx_quantize_reference(v: np.ndarray):
+    """An independent MXFP4 quantiser (numpy, per row and 32 columns): shared exponent
+    floor(log2(amax)) - 2, element = the nearest E2M1 value of v / 2^X with ties to the even
+    code, beyond 6 saturating; a zero block gets scale code 127."""
+    rows, cols = v.shape
+    mags = np.array(E2M1_MAGNITUDES)
+    codes = np.zeros((rows, cols), np.uint8)
+    scales = np.zeros((rows, cols // 32), np.uint8)
+    for r in range(rows):
+        for b in range(cols // 32):
+            blk = v[r, 32 * b:32 * b + 32].astype(np.float64)
+            amax = np.abs(blk).max()
+            x = int(np.floor(np.log2(amax))) - 2 if amax > 0 else 0
+            scales[r, b] = x + 127
+            for j, val in enumerate(blk / 2.0**x):
+                d = np.abs(mags - min(abs(val), 6.0))
+                best = [c for c in range(8) if d[c] == d.min()]
+                c = min(best, key=lambda c: (c % 2, c))  # ties to the even code
+                codes[r, 32 * b + j] = c | (8 if np.signbit(val) else 0)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return packed, scales
+
+
+def test_mxfp4_inputs_follow_the_recipe_and_round_trip():
+    """The generator's MXFP4 matrices equal an independent numpy quantisation of the same
+    fp32 values, and dequantise to within half an E2M1 step of them."""
+    rows, cols = 12, 96
+    v = mi.host_f32((rows * cols,), 3, mi.TAG_GATE, 5, mi.SIGMA_W).reshape(rows, cols)
+    q, s = mi.host_mxfp4(rows, cols, 3, mi.TAG_GATE, 5, mi.SIGMA_W)
+    rq, rs = _mx_quantize_reference(v)
+    assert np.array_equal(s, rs) and np.array_equal(q, rq)
+    w = codecs.mxfp4_dequant(q, s)
+    step = np.repeat(codecs.e8m0_decode(s), 32, axis=1)  # the E2M1 step is at most 2 units of 2^X
+    assert (np.abs(w - v) <= step + 1e-30).all()
+
+
 def test_softmax_is_torch_softmax_and_shift_invariant():
     lg = np.random.default_rng(2).standard_normal((7, 384)) * 3
     p = om.scores(lg, "softmax")
@@ -292,18 +343,33 @@ def _dense_brute_force(cfg, x_bits, router_bits, bias, experts, shared, shared_g
 
 
 def _fp8_expert_blockwise(xrow, w):
-    """One row through an fp8 expert, as sums over 128-blocks of (s_x*S_w) * code dot products."""
+    """One row through an fp8 or MXFP4 expert, as sums over 128-blocks of the activation:
+    s_x * S_w * (code dot product) for e4m3 weights with 128x128 block scales, or
+    s_x * sum over the four 32-column weight blocks of 2^(e - 127) * (code dot product) for
+    MXFP4 weights (E2M1 codes unpacked from their nibbles)."""
     (qg, sg), (qu, su), (qd, sd) = w
     xq, xs = om.quantize_fp8_groups(xrow[None, :].astype(np.float32))
 
     def gemv(codes, scales, aq, as_):
+        mx = scales.dtype == np.uint8
         out = np.zeros(codes.shape[0])
         for i in range(codes.shape[0]):
+            if mx:
+                wrow = np.empty(codes.shape[1] * 2, np.uint8)
+                wrow[0::2], wrow[1::2] = codes[i] & 0xF, codes[i] >> 4
             tot = 0.0
-            for b in range(codes.shape[1] // 128):
-                dot = float(np.dot(codecs.e4m3_decode(codes[i, b * 128:(b + 1) * 128]),
-                                   codecs.e4m3_decode(aq[0, b * 128:(b + 1) * 128])))
-                tot += float(as_[0, b]) * float(scales[i // 128, b]) * dot
+            for b in range(aq.shape[1] // 128):
+                a = codecs.e4m3_decode(aq[0, b * 128:(b + 1) * 128])
+                if mx:
+                    inner = 0.0
+                    for j in range(4):
+                        k0 = b * 128 + 32 * j
+                        inner += 2.0 ** (int(scales[i, k0 // 32]) - 127) * float(
+                            np.dot(codecs.e2m1_decode(wrow[k0:k0 + 32]), a[32 * j:32 * j + 32]))
+                    tot += float(as_[0, b]) * inner
+                else:
+                    dot = float(np.dot(codecs.e4m3_decode(codes[i, b * 128:(b + 1) * 128]), a))
+                    tot += float(as_[0, b]) * float(scales[i // 128, b]) * dot
             out[i] = tot
         return out
 
@@ -321,6 +387,8 @@ def _random_layer(rng, N, H, E, R, K, I, Is, scoring, renorm, scale, dtype, with
         w = rng.standard_normal((rows, cols)) * 0.05
         if dtype == "bf16":
             return _bf16(w)
+        if dtype == "mxfp4":
+            return _mx_quantize_reference(w.astype(np.float32))
         s = np.zeros(((rows + 127) // 128, (cols + 127) // 128), np.float32)
         q = np.zeros((rows, cols), np.uint8)
         for bi in range(s.shape[0]):
@@ -352,6 +420,8 @@ def _random_layer(rng, N, H, E, R, K, I, Is, scoring, renorm, scale, dtype, with
          with_bias=True, gated=True),
     dict(N=3, H=256, E=4, R=4, K=2, I=128, Is=128, scoring="softmax", renorm=True, scale=1.0, dtype="fp8",
          with_bias=False, gated=True),
+    dict(N=3, H=256, E=4, R=6, K=3, I=128, Is=128, scoring="sqrtsoftplus", renorm=True, scale=2.5, dtype="mxfp4",
+         with_bias=True, gated=True),
 ])
 def test_oracle_equals_dense_brute_force(case):
     rng = np.random.default_rng(13)
