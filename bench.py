@@ -24,7 +24,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}  # dense MFMA peaks
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "mxfp4": 5000.0}  # dense MFMA peaks (mxfp4: e4m3 x e2m1 MFMA)
 
 # HBM traffic of the dominant kernel per launch, from two rocprofv3 --pmc runs of this script
 # (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch averaged over the kernel's dispatches), each scaled by
@@ -104,8 +104,9 @@ def main():
     wl = mi.WORKLOADS[args.workload]
     N, H, E, R, K, I, Is = (wl.num_tokens, wl.hidden, wl.num_experts, wl.router_width, wl.top_k, wl.inter,
                             wl.shared_inter)
-    fp8 = wl.weight_dtype == "fp8"
-    wbytes = 1 if fp8 else 2
+    fp8 = wl.weight_dtype != "bf16"  # fp8 and mxfp4 experts take e4m3 activations
+    abytes = 1 if fp8 else 2  # activation and h element bytes
+    wbytes = {"bf16": 2, "fp8": 1, "mxfp4": 0.5 + 1 / 32}[wl.weight_dtype]  # mxfp4: codes + E8M0 per 32
     layer_bytes = 3 * E * I * H * wbytes
     # enough distinct weight copies that the touched experts of consecutive steps cannot be
     # served from the 256 MB Infinity Cache (at least ~8 GB of weights in rotation, at most 8 copies)
@@ -218,8 +219,8 @@ def main():
         k_name = "routed gate/up + SwiGLU, down, unpermute-reduce (one launch)"
     else:
         # touched experts' gate and up weights (+ block scales), x read, h written
-        k_bytes = (e_t * 2 * I * H * wbytes + (e_t * 2 * (I // 128) * (H // 128) * 4 if fp8 else 0)
-                   + N * H * wbytes + p_r * I * wbytes)
+        k_bytes = (e_t * 2 * I * H * wbytes + (e_t * 2 * (I // 128) * (H // 128) * 4 if wl.weight_dtype == "fp8" else 0)
+                   + N * H * abytes + p_r * I * abytes)
         k_flops = 4.0 * p_r * H * I
         k_name = "grouped gate/up + SwiGLU (routed)"
     # whole layer

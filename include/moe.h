@@ -43,7 +43,7 @@ typedef enum {
 } moe_status_t;
 
 enum { MOE_SCORING_SOFTMAX = 0, MOE_SCORING_SIGMOID = 1, MOE_SCORING_SQRTSOFTPLUS = 2 };
-enum { MOE_WEIGHTS_BF16 = 0, MOE_WEIGHTS_FP8_E4M3 = 1 };
+enum { MOE_WEIGHTS_BF16 = 0, MOE_WEIGHTS_FP8_E4M3 = 1, MOE_WEIGHTS_MXFP4 = 2 };
 enum { MOE_STAGE_GATE_UP = 0, MOE_STAGE_DOWN = 1 };
 enum { MOE_GROUP_ROUTED = 0, MOE_GROUP_SHARED = 1 };
 
@@ -80,6 +80,12 @@ typedef struct {
  * fp8:  the same matrices as e4m3 codes, plus one fp32 scale per 128x128 block:
  *       gate_s[e], up_s[e] -> [I/128, H/128]; down_s[e] -> [H/128, I/128]
  *       (dequantised weight = code * scale of its block).
+ * mxfp4 (OCP Microscaling MXFP4; the forward.rs page's MXFP4 / E8M0 expert arm):
+ *       each matrix [rows, K] as packed FP4 E2M1 codes [rows, K/2] uint8 (column 2j in
+ *       the low nibble of byte j) plus one E8M0 code per row and 32 columns,
+ *       [rows, K/32] uint8, passed in the *_s pointers (4-byte aligned); dequantised
+ *       weight = e2m1(code) * 2^(e8m0 - 127).  Activations and h are e4m3 with fp32
+ *       per-128 scales as on the fp8 path.
  * The shared expert, if Is > 0, is given directly (not through tables) with
  * Is in place of I.  Pointers must be 16-byte aligned. */
 typedef struct {
@@ -163,7 +169,7 @@ moe_status_t moe_quantize_fp8(const moe_config_t* cfg, const void* x, uint8_t* x
  * group MOE_GROUP_SHARED: rows t in [0, N) use the shared expert (Is in place
  *   of I); a_t = a[t]; sorted_ids and offsets are ignored (may be NULL).
  * bf16 weights: a and out are bf16; a_scales and out_scales are ignored.
- * fp8 weights: a is e4m3 with a_scales [rows of a, cols/128] fp32 (from
+ * fp8 and mxfp4 weights: a is e4m3 with a_scales [rows of a, cols/128] fp32 (from
  *   moe_quantize_fp8 for GATE_UP, from the GATE_UP output for DOWN); GATE_UP
  *   writes e4m3 codes + out_scales [P or N, I/128] quantised per 128 columns
  *   like moe_quantize_fp8; DOWN writes bf16.

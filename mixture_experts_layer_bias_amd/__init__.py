@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, 1, 2, 3, 4
 MOE_SCORING_SOFTMAX, MOE_SCORING_SIGMOID, MOE_SCORING_SQRTSOFTPLUS = 0, 1, 2
-MOE_WEIGHTS_BF16, MOE_WEIGHTS_FP8_E4M3 = 0, 1
+MOE_WEIGHTS_BF16, MOE_WEIGHTS_FP8_E4M3, MOE_WEIGHTS_MXFP4 = 0, 1, 2
 MOE_STAGE_GATE_UP, MOE_STAGE_DOWN = 0, 1
 MOE_GROUP_ROUTED, MOE_GROUP_SHARED = 0, 1
 
@@ -114,7 +114,7 @@ def make_config(num_tokens: int, hidden: int, num_experts: int, router_width: in
                         {"softmax": MOE_SCORING_SOFTMAX, "sigmoid": MOE_SCORING_SIGMOID,
                          "sqrtsoftplus": MOE_SCORING_SQRTSOFTPLUS}[scoring],
                         1 if renormalize else 0, routed_scale,
-                        {"bf16": MOE_WEIGHTS_BF16, "fp8": MOE_WEIGHTS_FP8_E4M3}[weight_dtype],
+                        {"bf16": MOE_WEIGHTS_BF16, "fp8": MOE_WEIGHTS_FP8_E4M3, "mxfp4": MOE_WEIGHTS_MXFP4}[weight_dtype],
                         1 if row_invariant else 0)
 
 

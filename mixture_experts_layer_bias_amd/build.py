@@ -12,7 +12,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build", "libmoe")
 LIB = os.path.join(HERE, "libmoe.so")
 
-SOURCES = ["route.hip", "permute.hip", "quant.hip", "gemm_bf16.hip", "gemm_fp8.hip", "gemm_decode.hip", "reduce.hip", "api.cpp"]
+SOURCES = ["route.hip", "permute.hip", "quant.hip", "gemm_bf16.hip", "gemm_fp8.hip", "gemm_decode.hip", "gemm_mxfp4.hip", "reduce.hip", "api.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -86,7 +86,9 @@ moe_status_t check_config(const moe_config_t* c) {
   MOE_CHECK(c->scoring == MOE_SCORING_SOFTMAX || c->scoring == MOE_SCORING_SIGMOID ||
                 c->scoring == MOE_SCORING_SQRTSOFTPLUS,
             MOE_ERR_INVALID, "scoring %d is not a MOE_SCORING_* value", c->scoring);
-  MOE_CHECK(c->weight_dtype == MOE_WEIGHTS_BF16 || c->weight_dtype == MOE_WEIGHTS_FP8_E4M3, MOE_ERR_INVALID,
+  MOE_CHECK(c->weight_dtype == MOE_WEIGHTS_BF16 || c->weight_dtype == MOE_WEIGHTS_FP8_E4M3 ||
+                c->weight_dtype == MOE_WEIGHTS_MXFP4,
+            MOE_ERR_INVALID,
             "weight_dtype %d is not a MOE_WEIGHTS_* value", c->weight_dtype);
   MOE_CHECK(std::isfinite(c->routed_scale), MOE_ERR_INVALID, "routed_scale is not finite");
   MOE_CHECK(c->row_invariant == 0 || c->row_invariant == 1, MOE_ERR_INVALID, "row_invariant %d is not 0 or 1",
@@ -109,7 +111,7 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 void compute_layout(const moe_config_t* c, moe_workspace_layout_t* L) {
   const size_t N = c->num_tokens, H = c->hidden, R = c->router_width, K = c->top_k, I = c->inter,
                Is = c->shared_inter, P = N * K;
-  const bool fp8 = c->weight_dtype == MOE_WEIGHTS_FP8_E4M3;
+  const bool fp8 = c->weight_dtype != MOE_WEIGHTS_BF16;  // fp8 or mxfp4: e4m3 activations, scaled weights
   const size_t none = SIZE_MAX;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -148,7 +150,7 @@ moe_status_t check_weights(const moe_config_t* c, const moe_weights_t* w) {
   MOE_RET(check_ptr(w->gate_w, 8, "gate_w table"));
   MOE_RET(check_ptr(w->up_w, 8, "up_w table"));
   MOE_RET(check_ptr(w->down_w, 8, "down_w table"));
-  const bool fp8 = c->weight_dtype == MOE_WEIGHTS_FP8_E4M3;
+  const bool fp8 = c->weight_dtype != MOE_WEIGHTS_BF16;  // fp8 or mxfp4: e4m3 activations, scaled weights
   if (fp8) {
     MOE_RET(check_ptr(w->gate_s, 8, "gate_s table"));
     MOE_RET(check_ptr(w->up_s, 8, "up_s table"));
@@ -207,8 +209,10 @@ moe::GroupedGemmArgs gemm_args(const moe_config_t* c, int stage, int group, cons
 moe_status_t run_gemm(const moe_config_t* c, const moe::GroupedGemmArgs& g, hipStream_t s) {
   if (c->weight_dtype == MOE_WEIGHTS_BF16) {
     MOE_HIP(moe::launch_grouped_gemm_bf16(g, s));
-  } else {
+  } else if (c->weight_dtype == MOE_WEIGHTS_FP8_E4M3) {
     MOE_HIP(moe::launch_grouped_gemm_fp8(g, s));
+  } else {
+    MOE_HIP(moe::launch_grouped_gemm_mxfp4(g, s));
   }
   return MOE_OK;
 }
@@ -233,7 +237,7 @@ moe_status_t run_experts(const moe_config_t* cfg, const moe_weights_t* w, const 
                          void* out, const moe_workspace_layout_t& L, char* base, bool fused, hipStream_t s) {
   const moe_config_t& c = *cfg;
   auto at = [&](size_t off) -> void* { return off == SIZE_MAX ? nullptr : base + off; };
-  const bool fp8 = c.weight_dtype == MOE_WEIGHTS_FP8_E4M3;
+  const bool fp8 = c.weight_dtype != MOE_WEIGHTS_BF16;  // e4m3 activations
   if (fp8)
     MOE_HIP(moe::launch_quant_fp8(static_cast<const uint16_t*>(x), static_cast<uint8_t*>(at(L.xq)),
                                   static_cast<float*>(at(L.x_scales)), c.num_tokens, c.hidden, s));
@@ -387,7 +391,7 @@ moe_status_t moe_grouped_gemm(const moe_config_t* cfg, int32_t stage, int32_t gr
   MOE_CHECK(group == MOE_GROUP_ROUTED || group == MOE_GROUP_SHARED, MOE_ERR_INVALID,
             "group %d is not a MOE_GROUP_* value", group);
   MOE_CHECK(w != nullptr, MOE_ERR_INVALID, "weights is NULL");
-  const bool fp8 = cfg->weight_dtype == MOE_WEIGHTS_FP8_E4M3;
+  const bool fp8 = cfg->weight_dtype != MOE_WEIGHTS_BF16;  // scaled weights, e4m3 activations
   const bool shared = group == MOE_GROUP_SHARED;
   if (shared) MOE_CHECK(cfg->shared_inter > 0, MOE_ERR_INVALID, "MOE_GROUP_SHARED with shared_inter == 0");
   if (cfg->num_tokens == 0) return ok();

@@ -87,6 +87,8 @@ hipError_t launch_decode_fused(const GroupedGemmArgs& gu, const GroupedGemmArgs&
                                int32_t* done, hipStream_t s);
 
 hipError_t launch_grouped_gemm_fp8(const GroupedGemmArgs& g, hipStream_t s);
+// MXFP4 weights (packed E2M1 [rows, K/2], E8M0 scales [rows, K/32] in the s_* / sh_*_s pointers)
+hipError_t launch_grouped_gemm_mxfp4(const GroupedGemmArgs& g, hipStream_t s);
 
 // unpermute + weighted reduce + identity-expert and (gated) shared blends
 hipError_t launch_unpermute_reduce(const uint16_t* y_sorted, const ReduceArgs& r, hipStream_t s);

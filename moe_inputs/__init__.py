@@ -71,9 +71,12 @@ FP8_SIGMOID = Workload("fp8_2048tok_h7168_e256_top8_i2048_shared2048_sigmoid_bia
                        2048, "sigmoid", True, 2.5, "fp8", True)
 ZERO_EXPERTS = Workload("zero_experts_512tok_h6144_e256+128id_top12_i2048", 512, 6144, 256, 384, 12, 2048, 0,
                         "softmax", False, 1.0, "bf16", True)
+# The DeepSeek-like layer with MXFP4 experts (E2M1 codes, E8M0 scales per 32 columns), fp8 activations.
+MXFP4_SIGMOID = Workload("mxfp4_2048tok_h7168_e256_top8_i2048_shared2048_sigmoid_bias", 2048, 7168, 256, 256, 8,
+                         2048, 2048, "sigmoid", True, 2.5, "mxfp4", True)
 
 WORKLOADS = {"tiny": TINY, "decode": DECODE, "prefill_zipf": PREFILL_ZIPF, "fp8_sigmoid": FP8_SIGMOID,
-             "zero_experts": ZERO_EXPERTS}
+             "zero_experts": ZERO_EXPERTS, "mxfp4_sigmoid": MXFP4_SIGMOID}
 
 
 # ----------------------------------------------------------------------------- build

@@ -57,11 +57,18 @@ FP8_SMALL = {
     # sqrt(softplus) + bias with a gated fp8 shared expert
     "fp8_sqrtsoftplus_gated_shared": W("fp8g", 40, 256, 8, 8, 2, 128, 128, "sqrtsoftplus", True, 2.5, "fp8", True,
                                        seed=21, shared_gated=True),
+    # MXFP4 experts (E2M1 + E8M0 per 32 columns, e4m3 activations): a shared expert, sigmoid + bias
+    "mxfp4_sigmoid_bias_shared": W("mx", 33, 512, 8, 8, 2, 256, 128, "sigmoid", True, 2.5, "mxfp4", True, seed=23),
+    # ragged MXFP4 layer with identity experts, sqrt(softplus) + bias and a gated shared expert
+    "mxfp4_ragged_sqrtsoftplus_gated": W("mxg", 70, 256, 16, 20, 4, 384, 128, "sqrtsoftplus", True, 1.5, "mxfp4",
+                                         True, seed=24, shared_gated=True),
+    # a decode-sized MXFP4 batch
+    "mxfp4_decode_4tok": W("mxd", 4, 512, 32, 32, 4, 256, 0, "softmax", True, 1.0, "mxfp4", False, seed=25),
 }
 
 
 def _tol(wl):
-    return FP8_TOL if wl.weight_dtype == "fp8" else BF16_TOL
+    return FP8_TOL if wl.weight_dtype != "bf16" else BF16_TOL
 
 
 # ============================================================================ generator
@@ -332,7 +339,7 @@ def test_forward_matches_oracle_and_composed_stages(name):
     counts, offsets = s("counts")[:4 * R].view(torch.int32), s("offsets")[:4 * (R + 1)].view(torch.int32)
     sid, inv = s("sorted_ids")[:4 * P].view(torch.int32), s("inv_perm")[:4 * P].view(torch.int32)
     moe.moe_permute(cfg, ids, counts, offsets, sid, inv, ws2)
-    fp8 = wl.weight_dtype == "fp8"
+    fp8 = wl.weight_dtype != "bf16"  # fp8 and mxfp4: e4m3 activations
     a, a_sc, hs, shs = dl.x, None, None, None
     if fp8:
         a = s("xq")[:N * H]
@@ -414,7 +421,7 @@ def test_experts_forward_matches_forward(name):
         assert int(ws2[L["sync"]:].view(torch.int32)[:nsync].abs().sum()) == 0, f"counters after call {i}"
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "mxfp4"])
 def test_row_invariant_mode_gives_each_token_the_same_bits_in_any_batch(dtype):
     """With row_invariant set, a token's output bits do not depend on the batch it comes in: the
     rows of a 200-token batch equal those of a 5-token tail, a single token and the first 100
