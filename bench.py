@@ -66,7 +66,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="decode", choices=["tiny", "decode", "prefill_zipf", "fp8_sigmoid",
-                                                              "zero_experts"])
+                                                              "zero_experts", "mxfp4_sigmoid"])
     ap.add_argument("--layers", type=int, default=0,
                     help="distinct weight copies cycled through (0: enough to exceed the 256 MB MALL)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle leg")
