@@ -38,8 +38,8 @@ MEASURED_TRAFFIC = {
                     "mixture_experts_layer_bias_amd/csrc/gemm_common.h",
                     "mixture_experts_layer_bias_amd/csrc/unpermute.h",
                     "mixture_experts_layer_bias_amd/csrc/common.h"],
-        "sha256": "a33cd0fd93e5018d274c2b424763a39939a95022c38ff4136abafee7d3773d78",
-        "fetch_kib": 140118.35, "write_kib": 253.78, "fetch_scale": 2.0, "write_scale": 1.0,
+        "sha256": "56072b933dd1000aef22a59d0d32ccd8df9357d493feb2340963cf911a0c6a7d",
+        "fetch_kib": 140123.25, "write_kib": 253.78, "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
 
