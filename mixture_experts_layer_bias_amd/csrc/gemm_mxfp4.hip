@@ -12,11 +12,15 @@
 //
 // Block tile BM = 128 rows x BN = 128 output columns, K step 128 columns
 // (128 bytes of A, 64 bytes of packed B per row), 4 waves in 2 x 2, each wave
-// 64 x 64 (x2 for gate and up).  Operands are staged through LDS with register
-// prefetch of the next K step.  The gate/up epilogue computes h = silu(g) * u and
+// 64 x 64 (x2 for gate and up).  The operands stream through an LDS ring filled
+// by direct global -> LDS loads (A and B rows in 16-byte pieces, XOR-swizzled;
+// the weight rows' E8M0 codes and the activation rows' fp32 scales of each step
+// in 4-byte pieces), several K steps ahead of the MFMAs, so the loads in flight
+// hold no registers.  The gate/up epilogue computes h = silu(g) * u and
 // quantises it per row over the tile's 128 columns to e4m3 (the recipe of
 // moe_quantize_fp8); the down stage writes bf16.
 #include "common.h"
+#include "dma.h"
 #include "gemm_common.h"
 #include "kernels.h"
 
@@ -25,18 +29,37 @@ namespace moe {
 namespace {
 
 constexpr int BM = 128, BN = 128, BK = 128;
-constexpr int A_STRIDE = BK + 16;      // bytes per LDS row of A (e4m3)
-constexpr int B_STRIDE = BK / 2 + 16;  // bytes per LDS row of B (two E2M1 codes per byte)
-constexpr int E8M0_ONE = 127;          // E8M0 code of 2^0
+constexpr int E8M0_ONE = 127;  // E8M0 code of 2^0
 
 template <int STAGE>
-struct MxTile {
-  static constexpr int BROWS = STAGE == 0 ? 2 * BN : BN;   // weight rows per tile
-  static constexpr int A_LOADS = BM * (BK / 16) / 256;     // 16-byte chunks per thread
-  static constexpr int B_LOADS = BROWS * (BK / 32) / 256;  // 64 bytes per row = four 16-byte chunks
+struct MxShape {
+  static constexpr int BROWS = STAGE == 0 ? 2 * BN : BN;  // weight rows per tile
+  static constexpr int NSTAGE = STAGE == 0 ? 4 : 3;       // gate/up: one block per CU; down: two
+  static constexpr int ABYTES = BM * BK;                  // e4m3 rows
+  static constexpr int BBYTES = BROWS * BK / 2;           // packed E2M1 rows
+  static constexpr int BSBYTES = BROWS * 4;               // the 4 E8M0 codes of each weight row
+  static constexpr int ASBYTES = BM * 4;                  // the fp32 scale of each activation row
+  static constexpr int SBYTES = ABYTES + BBYTES + BSBYTES + ASBYTES;
+  static constexpr int B_DMA = BBYTES / 1024 / 4;         // 16-byte B loads per wave per step
+  static constexpr int VM = 4 + B_DMA + 1 + 1;            // load instructions per wave per step
+  static constexpr int LDS = NSTAGE * SBYTES;
 };
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+
+__device__ __forceinline__ void dma4(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                   (void __attribute__((address_space(3)))*)lds_base, 4, 0, 0);
+}
+
+// wait until at most `stages_after` later steps (VM loads each) are still in flight
+template <int NSTAGE, int VM>
+__device__ __forceinline__ void wait_steps(int stages_after) {
+  static_assert(NSTAGE == 3 || NSTAGE == 4, "one case per possible count of later steps");
+  if (stages_after == 0) dma_wait<0>();
+  else if (NSTAGE == 3 || stages_after == 1) dma_wait<VM>();
+  else dma_wait<(NSTAGE == 4 ? 2 * VM : VM)>();
+}
 
 // Operand order of this MFMA (e4m3 A, E2M1 B), measured on the device: a B lane (row l % 32,
 // half h = l / 32) holds 32 E2M1 values whose scale is that lane's E8M0 byte, and its value e
@@ -52,14 +75,11 @@ __device__ __forceinline__ f32x16 mfma_e4m3_x_e2m1(i32x8 a, i32x8 b, int b_scale
 
 template <int STAGE>
 __global__ __launch_bounds__(256, STAGE == 0 ? 1 : 2) void k_grouped_gemm_mxfp4(GroupedGemmArgs g) {
-  using T = MxTile<STAGE>;
-  __shared__ __align__(16) uint8_t a_lds[BM * A_STRIDE];
-  __shared__ __align__(16) uint8_t b_lds[T::BROWS * B_STRIDE];
-  __shared__ uint32_t s_bsc[T::BROWS];  // the four E8M0 codes of each weight row in this K step
-  __shared__ float s_asc[BM];           // activation row scales of this K step
-  __shared__ float s_amax[2][BM];       // gate/up epilogue: per-row amax of each column half
-  __shared__ int s_prefix[kMaxGroups + 1];
-  __shared__ int s_wsum[4];
+  using S = MxShape<STAGE>;
+  constexpr int NSTAGE = S::NSTAGE, VM = S::VM, BROWS = S::BROWS;
+  extern __shared__ __align__(16) uint8_t smem[];  // S::LDS bytes: the ring
+  int* s_prefix = reinterpret_cast<int*>(smem);     // scheduler scratch, dead before the first load
+  int* s_wsum = s_prefix + kMaxGroups + 1;
 
   const int KD = STAGE == 0 ? g.H : g.I;
   const int NCOLS = STAGE == 0 ? g.I : g.H;
@@ -67,12 +87,14 @@ __global__ __launch_bounds__(256, STAGE == 0 ? 1 : 2) void k_grouped_gemm_mxfp4(
   const int KB = KD / BK;
   const TileCoord tc =
       schedule_tile(g.offsets, g.shared ? 1 : g.E, g.shared ? g.N : -1, BM, NT, s_prefix, s_wsum);
-  if (tc.expert < 0) return;
+  if (tc.expert < 0) return;  // the same decision in every thread
+  __syncthreads();            // every wave is done with the scheduler scratch before the loads reuse it
 
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int n0 = tc.n_tile * BN;
 
-  const uint8_t *wa, *wb = nullptr;  // packed codes [rows, KD/2]
+  const uint8_t *wa, *wb = nullptr;      // packed codes [rows, KD/2]
   const uint8_t *sa_w, *sb_w = nullptr;  // E8M0 codes [rows, KD/32]
   if (STAGE == 0) {
     wa = static_cast<const uint8_t*>(g.shared ? g.sh_gate : g.w_gate[tc.expert]);
@@ -83,55 +105,51 @@ __global__ __launch_bounds__(256, STAGE == 0 ? 1 : 2) void k_grouped_gemm_mxfp4(
     wa = static_cast<const uint8_t*>(g.shared ? g.sh_down : g.w_down[tc.expert]);
     sa_w = reinterpret_cast<const uint8_t*>(g.shared ? g.sh_down_s : g.s_down[tc.expert]);
   }
-
-  // A: row tid / 8 (+ 32 i), 16-byte chunk tid % 8
-  const uint8_t* a_src = static_cast<const uint8_t*>(g.a);
-  const int lrow = tid >> 3, lcol = (tid & 7) * 16;
-  const uint8_t* a_ptr[T::A_LOADS];
-#pragma unroll
-  for (int i = 0; i < T::A_LOADS; ++i) {
-    int p = tc.row0 + lrow + 32 * i;
-    if (p >= tc.row_end) p = tc.row_end - 1;  // rows past the segment are computed, never stored
-    const long arow = STAGE == 0 ? (g.shared ? p : g.sorted_ids[p] / g.K) : p;
-    a_ptr[i] = a_src + (size_t)arow * KD + lcol;
-  }
-  const float* asc_ptr = nullptr;  // threads 0..127: the scale row of A row tid
-  if (tid < BM) {
-    int p = tc.row0 + tid;
-    if (p >= tc.row_end) p = tc.row_end - 1;
-    const long arow = STAGE == 0 ? (g.shared ? p : g.sorted_ids[p] / g.K) : p;
-    asc_ptr = g.a_scales + (size_t)arow * KB;
-  }
-  // B: weight row tid / 4 (+ 64 i), 16-byte chunk tid % 4 (gate/up: rows [0, BN) gate, then up)
-  const int brow = tid >> 2, bcol = (tid & 3) * 16;
   auto weight_row = [&](int r, const uint8_t* base_a, const uint8_t* base_b, size_t row_bytes) {
     if (STAGE == 0) return r < BN ? base_a + (size_t)(n0 + r) * row_bytes : base_b + (size_t)(n0 + r - BN) * row_bytes;
     return base_a + (size_t)(n0 + r) * row_bytes;
   };
-  const uint8_t* b_ptr[T::B_LOADS];
-#pragma unroll
-  for (int i = 0; i < T::B_LOADS; ++i) b_ptr[i] = weight_row(brow + 64 * i, wa, wb, (size_t)KD / 2) + bcol;
-  // threads 0..BROWS-1: the E8M0 row of weight row tid (4 codes per K step, one dword)
-  const uint8_t* bsc_ptr = tid < T::BROWS ? weight_row(tid, sa_w, sb_w, (size_t)KD / 32) : nullptr;
-
-  u32x4 ra[T::A_LOADS], rb[T::B_LOADS];
-  float rsc = 0.f;
-  uint32_t rbs = 0;
-  auto load_tile = [&](int kb) {
-#pragma unroll
-    for (int i = 0; i < T::A_LOADS; ++i) ra[i] = ldg16(a_ptr[i] + (size_t)kb * BK);
-#pragma unroll
-    for (int i = 0; i < T::B_LOADS; ++i) rb[i] = ldg16(b_ptr[i] + (size_t)kb * (BK / 2));
-    if (tid < BM) rsc = ldg_f32(asc_ptr + kb);
-    if (tid < T::BROWS) rbs = *reinterpret_cast<const uint32_t*>(bsc_ptr + (size_t)kb * (BK / 32));
+  auto a_row = [&](int trow) {  // the x / h row behind tile row trow
+    int p = tc.row0 + trow;
+    if (p >= tc.row_end) p = tc.row_end - 1;  // rows past the segment are computed, never stored
+    return STAGE == 0 ? (g.shared ? (long)p : (long)(g.sorted_ids[p] / g.K)) : (long)p;
   };
-  auto store_tile = [&]() {
+
+  // Load sources.  A: instruction i of wave w writes tile rows 8 (4 w + i) .. + 7, lane l row
+  // + l / 8 at 16-byte slot l % 8, which holds memory chunk (l % 8) ^ (row % 8).  B: instruction i
+  // writes weight rows 16 (B_DMA w + i) .. + 15, lane l row + l / 4 at slot l % 4 = chunk
+  // (l % 4) ^ (row % 4).  Scales: 4-byte pieces, the weight rows' E8M0 words (gate/up: 64 rows per
+  // wave; down: 32) and the activation rows' fp32 scales (32 rows per wave), row r at 4 r.
+  const uint8_t* a_src = static_cast<const uint8_t*>(g.a);
+  const uint8_t* a_ptr[4];
 #pragma unroll
-    for (int i = 0; i < T::A_LOADS; ++i) st16(a_lds + (lrow + 32 * i) * A_STRIDE + lcol, ra[i]);
+  for (int i = 0; i < 4; ++i) {
+    const int trow = (4 * wave + i) * 8 + lane / 8;
+    a_ptr[i] = a_src + (size_t)a_row(trow) * KD + (((lane % 8) ^ (trow % 8)) << 4);
+  }
+  const uint8_t* b_ptr[S::B_DMA];
 #pragma unroll
-    for (int i = 0; i < T::B_LOADS; ++i) st16(b_lds + (brow + 64 * i) * B_STRIDE + bcol, rb[i]);
-    if (tid < BM) s_asc[tid] = rsc;
-    if (tid < T::BROWS) s_bsc[tid] = rbs;
+  for (int i = 0; i < S::B_DMA; ++i) {
+    const int wr = (S::B_DMA * wave + i) * 16 + lane / 4;
+    b_ptr[i] = weight_row(wr, wa, wb, (size_t)KD / 2) + (((lane % 4) ^ (wr % 4)) << 4);
+  }
+  const int bs_rows = BROWS / 4;  // E8M0 rows per wave
+  const bool bs_lane = lane < bs_rows;
+  const uint8_t* bs_ptr = weight_row(bs_lane ? wave * bs_rows + lane : 0, sa_w, sb_w, (size_t)KD / 32);
+  const bool as_lane = lane < 32;
+  const float* as_ptr = g.a_scales + (size_t)a_row(as_lane ? wave * 32 + lane : 0) * KB;
+
+  auto issue = [&](int buf, int kb) {
+    uint8_t* sa = smem + buf * S::SBYTES;
+    uint8_t* sb = sa + S::ABYTES;
+    uint8_t* sbs = sb + S::BBYTES;
+    uint8_t* sas = sbs + S::BSBYTES;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(a_ptr[i] + (size_t)kb * BK, sa + (4 * wave + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < S::B_DMA; ++i) dma16(b_ptr[i] + (size_t)kb * (BK / 2), sb + (S::B_DMA * wave + i) * 1024);
+    if (bs_lane) dma4(bs_ptr + (size_t)kb * 4, sbs + wave * bs_rows * 4);
+    if (as_lane) dma4(as_ptr + kb, sas + wave * 128);
   };
 
   constexpr int NB = STAGE == 0 ? 4 : 2;
@@ -145,13 +163,22 @@ __global__ __launch_bounds__(256, STAGE == 0 ? 1 : 2) void k_grouped_gemm_mxfp4(
 
   const int wm = wave >> 1, wn = wave & 1;
   const int frow = lane & 31, half = lane >> 5;  // the lane's row and half of a 64-wide MFMA step
-  auto item_row = [&](int r) { return 8 * (r / 4) + 4 * (lane / 32) + (r % 4); };
+  auto item_row = [&](int r) { return 8 * (r / 4) + 4 * half + (r % 4); };
 
-  load_tile(0);
-  store_tile();
-  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < NSTAGE - 1; ++s)
+    if (s < KB) issue(s, s);
+
   for (int kb = 0; kb < KB; ++kb) {
-    if (kb + 1 < KB) load_tile(kb + 1);
+    const int later = KB - 1 - kb;  // steps issued after step kb (capped by the ring depth)
+    wait_steps<NSTAGE, VM>(later < NSTAGE - 2 ? later : NSTAGE - 2);
+    __builtin_amdgcn_s_barrier();  // step kb has landed in every wave; every wave is done with kb - 1
+    __builtin_amdgcn_sched_barrier(0);
+    if (kb + NSTAGE - 1 < KB) issue((kb + NSTAGE - 1) % NSTAGE, kb + NSTAGE - 1);
+    const uint8_t* sa = smem + (kb % NSTAGE) * S::SBYTES;
+    const uint8_t* sb = sa + S::ABYTES;
+    const uint32_t* sbs = reinterpret_cast<const uint32_t*>(sb + S::BBYTES);
+    const float* sas = reinterpret_cast<const float*>(sb + S::BBYTES + S::BSBYTES);
     f32x16 blk[2][NB];
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
@@ -165,17 +192,21 @@ __global__ __launch_bounds__(256, STAGE == 0 ? 1 : 2) void k_grouped_gemm_mxfp4(
       int bsc[NB];
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi) {
-        const uint8_t* p = a_lds + (wm * 64 + mi * 32 + frow) * A_STRIDE + kk + 16 * half;
-        const u32x4 lo = ld16(p), hi = ld16(p + 32);
+        const int ar = wm * 64 + mi * 32 + frow;
+        const uint8_t* rowp = sa + ar * BK;
+        const int c1 = kk / 16 + half, c2 = kk / 16 + 2 + half;  // memory K 16 h and 32 + 16 h
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(rowp + ((c1 ^ (ar % 8)) << 4));
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(rowp + ((c2 ^ (ar % 8)) << 4));
         af[mi] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
       }
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         // stage 0: nb 0,1 -> gate rows, nb 2,3 -> up rows of the same columns
         const int wr = (STAGE == 0 && nb >= 2 ? BN : 0) + wn * 64 + (nb & 1) * 32 + frow;
-        const u32x4 c = ld16(b_lds + wr * B_STRIDE + (kk + 32 * half) / 2);  // two codes per byte
-        bfr[nb] = i32x8{(int)c[0], (int)c[1], (int)c[2], (int)c[3], 0, 0, 0, 0};
-        bsc[nb] = (int)((s_bsc[wr] >> (8 * (kk / 32 + half))) & 0xFFu);
+        const int c = kk / 32 + half;  // memory block of the lane's 32 codes (16 bytes)
+        const u32x4 v = *reinterpret_cast<const u32x4*>(sb + wr * (BK / 2) + ((c ^ (wr % 4)) << 4));
+        bfr[nb] = i32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+        bsc[nb] = (int)((sbs[wr] >> (8 * c)) & 0xFFu);
       }
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi)
@@ -187,15 +218,11 @@ __global__ __launch_bounds__(256, STAGE == 0 ? 1 : 2) void k_grouped_gemm_mxfp4(
     for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float rs = s_asc[wm * 64 + mi * 32 + item_row(r)];
+        const float rs = sas[wm * 64 + mi * 32 + item_row(r)];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[mi][nb][r] += blk[mi][nb][r] * rs;
       }
-    __syncthreads();
-    if (kb + 1 < KB) {
-      store_tile();
-      __syncthreads();
-    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   if (STAGE == 1) {
@@ -216,6 +243,8 @@ __global__ __launch_bounds__(256, STAGE == 0 ? 1 : 2) void k_grouped_gemm_mxfp4(
   }
 
   // ---- gate/up epilogue: h = silu(g) * u, quantised per row over this tile's 128 columns
+  __syncthreads();  // every wave is past its last ring read: the per-row maxima reuse the ring
+  float* s_amax = reinterpret_cast<float*>(smem);  // [2][BM]
   float h[2][16][2];
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
@@ -229,7 +258,7 @@ __global__ __launch_bounds__(256, STAGE == 0 ? 1 : 2) void k_grouped_gemm_mxfp4(
       }
 #pragma unroll
       for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));  // the row's 32 lanes
-      if ((lane & 31) == 0) s_amax[wn][wm * 64 + mi * 32 + item_row(r)] = m;
+      if ((lane & 31) == 0) s_amax[wn * BM + wm * 64 + mi * 32 + item_row(r)] = m;
     }
   __syncthreads();
   uint8_t* out = static_cast<uint8_t*>(g.out);
@@ -240,7 +269,7 @@ __global__ __launch_bounds__(256, STAGE == 0 ? 1 : 2) void k_grouped_gemm_mxfp4(
     for (int r = 0; r < 16; ++r) {
       const int trow = wm * 64 + mi * 32 + item_row(r);
       const int row = tc.row0 + trow;
-      const float amax = fmaxf(s_amax[0][trow], s_amax[1][trow]);
+      const float amax = fmaxf(s_amax[trow], s_amax[BM + trow]);
       const float inv = amax > 0.f ? 448.0f / amax : 1.0f;
       if (row < tc.row_end) {
 #pragma unroll
@@ -260,9 +289,13 @@ hipError_t launch_grouped_gemm_mxfp4(const GroupedGemmArgs& g, hipStream_t s) {
   const int rows = g.shared ? g.N : g.P;
   if (rows == 0) return hipSuccess;
   if (g.stage == 0) {
-    k_grouped_gemm_mxfp4<0><<<grouped_grid(rows, groups, BM, g.I / BN), 256, 0, s>>>(g);
+    const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&k_grouped_gemm_mxfp4<0>), MxShape<0>::LDS);
+    if (e != hipSuccess) return e;
+    k_grouped_gemm_mxfp4<0><<<grouped_grid(rows, groups, BM, g.I / BN), 256, MxShape<0>::LDS, s>>>(g);
   } else {
-    k_grouped_gemm_mxfp4<1><<<grouped_grid(rows, groups, BM, g.H / BN), 256, 0, s>>>(g);
+    const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&k_grouped_gemm_mxfp4<1>), MxShape<1>::LDS);
+    if (e != hipSuccess) return e;
+    k_grouped_gemm_mxfp4<1><<<grouped_grid(rows, groups, BM, g.H / BN), 256, MxShape<1>::LDS, s>>>(g);
   }
   return hipGetLastError();
 }
