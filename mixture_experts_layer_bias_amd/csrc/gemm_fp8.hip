@@ -259,7 +259,7 @@ __global__ __launch_bounds__(256, STAGE == 0 ? 1 : 2) void k_grouped_gemm_fp8(Gr
 // overlap the other's MFMAs) in 2 x 4, each 64 rows x 2 blocks of 32 weight rows
 // (gate/up: one gate block and the matching up block; down: 64 columns); a
 // wave's block sums and accumulators stay in its VGPRs, so a promotion is one
-// FMA per value.  Chunk c of LDS row r sits at 16-byte slot c ^ (r % 8).
+// FMA per value.  Chunk c of LDS row r sits at 16-byte slot c ^ ((r / 2) % 8).
 constexpr int SBM = 128, SBNB = 256, SROWB = 128, SNSTAGE = 3, SWAVES = 8;
 constexpr int SABYTES = SBM * SROWB, SBBYTES = SBNB * SROWB;
 constexpr int SSTAGE = SABYTES + SBBYTES + SBM * 4;  // 48.5 KB
@@ -312,8 +312,13 @@ __global__ __launch_bounds__(512, 1) void k_grouped_gemm_fp8_stream(GroupedGemmA
   }
 
   // load sources.  One 16-byte instruction writes 8 rows x 128 B; lane l covers row l / 8 of
-  // its group and slot l % 8, i.e. logical chunk (l % 8) ^ (row % 8).
-  const int prow = lane >> 3, lch = (lane & 7) ^ prow;
+  // its group and slot l % 8, i.e. logical chunk (l % 8) ^ swz(row), swz(row) = (row / 2) % 8.
+  // A fragment read serves 16 lanes (16 consecutive rows, one chunk) per LDS cycle: with this
+  // swizzle they fall in 16 different 16-byte bank groups (row % 8 left rows r and r + 8 on the
+  // same banks).  Instruction i writes rows 8 i + prow past a multiple of 16, so there
+  // swz = (4 i + prow / 2) % 8.
+  const int prow = lane >> 3;
+  auto lch = [&](int i) { return (lane & 7) ^ ((4 * i + (prow >> 1)) & 7); };
   auto a_row = [&](int trow) -> long {  // source row of tile row trow (clamped into the segment)
     int p = tc.row0 + trow;
     if (p >= tc.row_end) p = tc.row_end - 1;  // rows past the segment are computed, never stored
@@ -322,11 +327,14 @@ __global__ __launch_bounds__(512, 1) void k_grouped_gemm_fp8_stream(GroupedGemmA
   const uint8_t* a_ptr[2];  // A: wave w fills tile rows 16 w .. 16 w + 15
 #pragma unroll
   for (int i = 0; i < 2; ++i)
-    a_ptr[i] = static_cast<const uint8_t*>(g.a) + (size_t)a_row(wave * 16 + 8 * i + prow) * KD + (lch << 4);
+    a_ptr[i] = static_cast<const uint8_t*>(g.a) + (size_t)a_row(wave * 16 + 8 * i + prow) * KD + (lch(i) << 4);
   // B: wave w fills weight rows 32 w .. 32 w + 31 (gate/up: waves 0..3 gate, waves 4..7 up)
   const uint8_t* b_ptr;
-  if (STAGE == 0) b_ptr = (wave < 4 ? wa : wb) + (size_t)(n0 + (wave & 3) * 32 + prow) * KD + (lch << 4);
-  else b_ptr = wa + (size_t)(n0 + wave * 32 + prow) * KD + (lch << 4);
+  if (STAGE == 0) b_ptr = (wave < 4 ? wa : wb) + (size_t)(n0 + (wave & 3) * 32 + prow) * KD;
+  else b_ptr = wa + (size_t)(n0 + wave * 32 + prow) * KD;
+  size_t b_off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) b_off[i] = (size_t)(8 * i) * KD + (lch(i) << 4);
   // row scales: lanes 0..15 of wave w load the scale of tile row 16 w + lane
   const float* sc_ptr = g.a_scales + (size_t)a_row(wave * 16 + (lane & 15)) * KB;
 
@@ -338,12 +346,12 @@ __global__ __launch_bounds__(512, 1) void k_grouped_gemm_fp8_stream(GroupedGemmA
 #pragma unroll
     for (int i = 0; i < 2; ++i) dma16(a_ptr[i] + koff, sa + (wave * 2 + i) * 1024);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(b_ptr + (size_t)(8 * i) * KD + koff, sb + (wave * 4 + i) * 1024);
+    for (int i = 0; i < 4; ++i) dma16(b_ptr + b_off[i] + koff, sb + (wave * 4 + i) * 1024);
     if (lane < 16)
       __builtin_amdgcn_global_load_lds((dma_gptr_t)(sc_ptr + kb), (dma_lptr_t)(ss + wave * 64), 4, 0, 0);
   };
   auto lds16 = [&](const uint8_t* base, int row, int chunk) {
-    return *reinterpret_cast<const u32x4*>(base + row * SROWB + ((chunk ^ (row & 7)) << 4));
+    return *reinterpret_cast<const u32x4*>(base + row * SROWB + ((chunk ^ ((row >> 1) & 7)) << 4));
   };
 
   f32x16 acc[2][2], blk[2][2];
