@@ -116,22 +116,23 @@ __global__ __launch_bounds__(256, STAGE == 0 ? 1 : 2) void k_grouped_gemm_mxfp4(
   };
 
   // Load sources.  A: instruction i of wave w writes tile rows 8 (4 w + i) .. + 7, lane l row
-  // + l / 8 at 16-byte slot l % 8, which holds memory chunk (l % 8) ^ (row % 8).  B: instruction i
-  // writes weight rows 16 (B_DMA w + i) .. + 15, lane l row + l / 4 at slot l % 4 = chunk
-  // (l % 4) ^ (row % 4).  Scales: 4-byte pieces, the weight rows' E8M0 words (gate/up: 64 rows per
+  // + l / 8 at 16-byte slot l % 8, which holds memory chunk (l % 8) ^ ((row / 2) % 8).  B:
+  // instruction i writes weight rows 16 (B_DMA w + i) .. + 15, lane l row + l / 4 at slot l % 4 =
+  // chunk (l % 4) ^ ((row / 4) % 4).  A fragment read serves 16 lanes (16 consecutive rows, one
+  // chunk) per LDS cycle; these swizzles put them in 16 different 16-byte bank groups.  Scales: 4-byte pieces, the weight rows' E8M0 words (gate/up: 64 rows per
   // wave; down: 32) and the activation rows' fp32 scales (32 rows per wave), row r at 4 r.
   const uint8_t* a_src = static_cast<const uint8_t*>(g.a);
   const uint8_t* a_ptr[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int trow = (4 * wave + i) * 8 + lane / 8;
-    a_ptr[i] = a_src + (size_t)a_row(trow) * KD + (((lane % 8) ^ (trow % 8)) << 4);
+    a_ptr[i] = a_src + (size_t)a_row(trow) * KD + (((lane % 8) ^ ((trow >> 1) & 7)) << 4);
   }
   const uint8_t* b_ptr[S::B_DMA];
 #pragma unroll
   for (int i = 0; i < S::B_DMA; ++i) {
     const int wr = (S::B_DMA * wave + i) * 16 + lane / 4;
-    b_ptr[i] = weight_row(wr, wa, wb, (size_t)KD / 2) + (((lane % 4) ^ (wr % 4)) << 4);
+    b_ptr[i] = weight_row(wr, wa, wb, (size_t)KD / 2) + (((lane % 4) ^ ((wr >> 2) & 3)) << 4);
   }
   const int bs_rows = BROWS / 4;  // E8M0 rows per wave
   const bool bs_lane = lane < bs_rows;
@@ -195,8 +196,8 @@ __global__ __launch_bounds__(256, STAGE == 0 ? 1 : 2) void k_grouped_gemm_mxfp4(
         const int ar = wm * 64 + mi * 32 + frow;
         const uint8_t* rowp = sa + ar * BK;
         const int c1 = kk / 16 + half, c2 = kk / 16 + 2 + half;  // memory K 16 h and 32 + 16 h
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(rowp + ((c1 ^ (ar % 8)) << 4));
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(rowp + ((c2 ^ (ar % 8)) << 4));
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(rowp + ((c1 ^ ((ar >> 1) & 7)) << 4));
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(rowp + ((c2 ^ ((ar >> 1) & 7)) << 4));
         af[mi] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
       }
 #pragma unroll
@@ -204,7 +205,7 @@ __global__ __launch_bounds__(256, STAGE == 0 ? 1 : 2) void k_grouped_gemm_mxfp4(
         // stage 0: nb 0,1 -> gate rows, nb 2,3 -> up rows of the same columns
         const int wr = (STAGE == 0 && nb >= 2 ? BN : 0) + wn * 64 + (nb & 1) * 32 + frow;
         const int c = kk / 32 + half;  // memory block of the lane's 32 codes (16 bytes)
-        const u32x4 v = *reinterpret_cast<const u32x4*>(sb + wr * (BK / 2) + ((c ^ (wr % 4)) << 4));
+        const u32x4 v = *reinterpret_cast<const u32x4*>(sb + wr * (BK / 2) + ((c ^ ((wr >> 2) & 3)) << 4));
         bfr[nb] = i32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
         bsc[nb] = (int)((sbs[wr] >> (8 * c)) & 0xFFu);
       }
