@@ -254,21 +254,37 @@ __global__ __launch_bounds__(256, STAGE == 0 ? 1 : 2) void k_grouped_gemm_fp8(Gr
 // weight-scale blocks).  K step = 128 bytes = one scale block.  The operands go
 // through a 3-stage LDS ring filled by direct global -> LDS loads, two steps
 // ahead of the MFMAs; the activation rows' scales of each step ride in the ring
-// (one 4-byte load per lane, 16 rows per wave), the tile's weight-block scales
-// are read into LDS once.  8 waves (two per SIMD, so one wave's promotions
-// overlap the other's MFMAs) in 2 x 4, each 64 rows x 2 blocks of 32 weight rows
-// (gate/up: one gate block and the matching up block; down: 64 columns); a
-// wave's block sums and accumulators stay in its VGPRs, so a promotion is one
-// FMA per value.  Chunk c of LDS row r sits at 16-byte slot c ^ ((r / 2) % 8).
-constexpr int SBM = 128, SBNB = 256, SROWB = 128, SNSTAGE = 3, SWAVES = 8;
+// (one 4-byte load per lane and row), the tile's weight-block scales are read
+// into LDS once.  Several waves per SIMD, so one wave's promotions overlap
+// another's MFMAs: gate/up 16 waves in 4 x 4, each 32 rows x 2 blocks of 32
+// weight rows (one gate block and the matching up block); down 8 waves in 2 x 4,
+// each 64 rows x 64 columns.  A wave's block sums and accumulators stay in its
+// VGPRs, so a promotion is one FMA per value.  Chunk c of LDS row r sits at
+// 16-byte slot c ^ ((r / 2) % 8).
+constexpr int SBM = 128, SBNB = 256, SROWB = 128, SNSTAGE = 3;
 constexpr int SABYTES = SBM * SROWB, SBBYTES = SBNB * SROWB;
 constexpr int SSTAGE = SABYTES + SBBYTES + SBM * 4;  // 48.5 KB
-constexpr int SVM = 2 + 4 + 1;                       // load instructions per wave per stage
+// Waves per block: gate/up 16 (four per SIMD, 32 x 64 wave tiles: 1,430 -> 1,358 us on the
+// DeepSeek-like layer), down 8 (two per SIMD, 64 x 64; 16 waves ran it 660 -> 684 us).
+template <int STAGE>
+struct StreamWaves {
+  static constexpr int WAVES = STAGE == 0 ? 16 : 8;
+  static constexpr int WM = WAVES / 4;     // waves along the rows (4 along the weight rows)
+  static constexpr int WR = SBM / WM;      // tile rows per wave
+  static constexpr int MI = WR / 32;       // 32-row MFMA blocks per wave
+  static constexpr int AR = SBM / WAVES;   // A rows each wave loads per stage
+  static constexpr int AI = AR / 8;        // ... in 8-row load instructions
+  static constexpr int BR = SBNB / WAVES;  // B rows each wave loads per stage
+  static constexpr int BI = BR / 8;
+  static constexpr int VM = AI + BI + 1;   // load instructions per wave per stage
+};
 constexpr int SMAXKB = 64;                           // weight-scale blocks along K held in LDS (K <= 8192)
 constexpr int SLDS = SNSTAGE * SSTAGE + 2 * SMAXKB * 4;  // 146 KB: one block per CU
 
 template <int STAGE>
-__global__ __launch_bounds__(512, 1) void k_grouped_gemm_fp8_stream(GroupedGemmArgs g) {
+__global__ __launch_bounds__(StreamWaves<STAGE>::WAVES * 64, 1) void k_grouped_gemm_fp8_stream(GroupedGemmArgs g) {
+  using W = StreamWaves<STAGE>;
+  constexpr int SWR = W::WR, SMI = W::MI, SAR = W::AR, SAI = W::AI, SBR = W::BR, SBI = W::BI, SVM = W::VM;
   extern __shared__ __align__(16) uint8_t smem[];
   int* s_prefix = reinterpret_cast<int*>(smem);  // scheduler scratch, dead before the first load
   int* s_wsum = s_prefix + kMaxGroups + 1;
@@ -318,25 +334,29 @@ __global__ __launch_bounds__(512, 1) void k_grouped_gemm_fp8_stream(GroupedGemmA
   // same banks).  Instruction i writes rows 8 i + prow past a multiple of 16, so there
   // swz = (4 i + prow / 2) % 8.
   const int prow = lane >> 3;
-  auto lch = [&](int i) { return (lane & 7) ^ ((4 * i + (prow >> 1)) & 7); };
+  auto lch = [&](int lds_row) { return (lane & 7) ^ ((lds_row >> 1) & 7); };
   auto a_row = [&](int trow) -> long {  // source row of tile row trow (clamped into the segment)
     int p = tc.row0 + trow;
     if (p >= tc.row_end) p = tc.row_end - 1;  // rows past the segment are computed, never stored
     return STAGE == 0 ? (g.shared ? p : g.sorted_ids[p] / g.K) : p;
   };
-  const uint8_t* a_ptr[2];  // A: wave w fills tile rows 16 w .. 16 w + 15
+  const uint8_t* a_ptr[SAI];  // A: wave w fills tile rows SAR w .. SAR w + SAR - 1
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-    a_ptr[i] = static_cast<const uint8_t*>(g.a) + (size_t)a_row(wave * 16 + 8 * i + prow) * KD + (lch(i) << 4);
-  // B: wave w fills weight rows 32 w .. 32 w + 31 (gate/up: waves 0..3 gate, waves 4..7 up)
-  const uint8_t* b_ptr;
-  if (STAGE == 0) b_ptr = (wave < 4 ? wa : wb) + (size_t)(n0 + (wave & 3) * 32 + prow) * KD;
-  else b_ptr = wa + (size_t)(n0 + wave * 32 + prow) * KD;
-  size_t b_off[4];
+  for (int i = 0; i < SAI; ++i) {
+    const int r = wave * SAR + 8 * i + prow;
+    a_ptr[i] = static_cast<const uint8_t*>(g.a) + (size_t)a_row(r) * KD + (lch(r) << 4);
+  }
+  // B: wave w fills weight rows SBR w .. SBR w + SBR - 1 (gate/up: the first 128 gate, the rest up)
+  const uint8_t* b_ptr[SBI];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) b_off[i] = (size_t)(8 * i) * KD + (lch(i) << 4);
-  // row scales: lanes 0..15 of wave w load the scale of tile row 16 w + lane
-  const float* sc_ptr = g.a_scales + (size_t)a_row(wave * 16 + (lane & 15)) * KB;
+  for (int i = 0; i < SBI; ++i) {
+    const int r = wave * SBR + 8 * i + prow;
+    const uint8_t* row_base = STAGE == 0 ? (r < SBNB / 2 ? wa + (size_t)(n0 + r) * KD : wb + (size_t)(n0 + r - SBNB / 2) * KD)
+                                         : wa + (size_t)(n0 + r) * KD;
+    b_ptr[i] = row_base + (lch(r) << 4);
+  }
+  // row scales: lanes 0 .. SAR - 1 of wave w load the scale of tile row SAR w + lane
+  const float* sc_ptr = g.a_scales + (size_t)a_row(wave * SAR + (lane % SAR)) * KB;
 
   auto issue = [&](int buf, int kb) {
     uint8_t* sa = smem + buf * SSTAGE;
@@ -344,19 +364,19 @@ __global__ __launch_bounds__(512, 1) void k_grouped_gemm_fp8_stream(GroupedGemmA
     uint8_t* ss = sb + SBBYTES;
     const size_t koff = (size_t)kb * SROWB;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dma16(a_ptr[i] + koff, sa + (wave * 2 + i) * 1024);
+    for (int i = 0; i < SAI; ++i) dma16(a_ptr[i] + koff, sa + (wave * SAI + i) * 1024);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(b_ptr + b_off[i] + koff, sb + (wave * 4 + i) * 1024);
-    if (lane < 16)
-      __builtin_amdgcn_global_load_lds((dma_gptr_t)(sc_ptr + kb), (dma_lptr_t)(ss + wave * 64), 4, 0, 0);
+    for (int i = 0; i < SBI; ++i) dma16(b_ptr[i] + koff, sb + (wave * SBI + i) * 1024);
+    if (lane < SAR)
+      __builtin_amdgcn_global_load_lds((dma_gptr_t)(sc_ptr + kb), (dma_lptr_t)(ss + wave * SAR * 4), 4, 0, 0);
   };
   auto lds16 = [&](const uint8_t* base, int row, int chunk) {
     return *reinterpret_cast<const u32x4*>(base + row * SROWB + ((chunk ^ ((row >> 1) & 7)) << 4));
   };
 
-  f32x16 acc[2][2], blk[2][2];
+  f32x16 acc[SMI][2], blk[SMI][2];
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int mi = 0; mi < SMI; ++mi)
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
@@ -388,10 +408,10 @@ __global__ __launch_bounds__(512, 1) void k_grouped_gemm_fp8_stream(GroupedGemmA
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {  // 64-byte k slices: logical chunks 4 ks + 2 (l / 32) and +1
       const int c0 = 4 * ks + 2 * fh;
-      i32x8 af[2], bf[2];
+      i32x8 af[SMI], bf[2];
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi) {
-        const int row = wm * 64 + mi * 32 + frow;
+      for (int mi = 0; mi < SMI; ++mi) {
+        const int row = wm * SWR + mi * 32 + frow;
         const u32x4 lo = lds16(sa, row, c0), hi = lds16(sa, row, c0 + 1);
         af[mi] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
       }
@@ -401,7 +421,7 @@ __global__ __launch_bounds__(512, 1) void k_grouped_gemm_fp8_stream(GroupedGemmA
         bf[nb] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
       }
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
+      for (int mi = 0; mi < SMI; ++mi)
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
           if (ks == 0) blk[mi][nb] = mfma_32x32x64_fp8(af[mi], bf[nb], f32x16{});
@@ -411,10 +431,10 @@ __global__ __launch_bounds__(512, 1) void k_grouped_gemm_fp8_stream(GroupedGemmA
     // promote this scale block: acc += blk * (row scale * weight-block scale)
     const float ws0 = s_ws[ws_row0 * SMAXKB + kb], ws1 = s_ws[ws_row1 * SMAXKB + kb];
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+    for (int mi = 0; mi < SMI; ++mi)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {  // items 4 q .. 4 q + 3 are 4 consecutive rows
-        const f32x4 rs = *reinterpret_cast<const f32x4*>(ss + wm * 64 + mi * 32 + 8 * q + 4 * fh);
+        const f32x4 rs = *reinterpret_cast<const f32x4*>(ss + wm * SWR + mi * 32 + 8 * q + 4 * fh);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           acc[mi][0][4 * q + j] += blk[mi][0][4 * q + j] * (rs[j] * ws0);
@@ -427,10 +447,10 @@ __global__ __launch_bounds__(512, 1) void k_grouped_gemm_fp8_stream(GroupedGemmA
   if (STAGE == 1) {
     uint16_t* out = static_cast<uint16_t*>(g.out);
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+    for (int mi = 0; mi < SMI; ++mi)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = tc.row0 + wm * 64 + mi * 32 + item_row(r);
+        const int row = tc.row0 + wm * SWR + mi * 32 + item_row(r);
         if (row >= tc.row_end) continue;
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
@@ -442,24 +462,24 @@ __global__ __launch_bounds__(512, 1) void k_grouped_gemm_fp8_stream(GroupedGemmA
   // gate/up epilogue: h = silu(g) * u, quantised per row over the tile's 128 columns
   __syncthreads();  // the ring is free: s_amax is aliased onto it
   float* s_amax = reinterpret_cast<float*>(smem);  // [wn][tile row]
-  float h[2][16];
+  float h[SMI][16];
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int mi = 0; mi < SMI; ++mi)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       h[mi][r] = silu(acc[mi][0][r]) * acc[mi][1][r];
       float m = fabsf(h[mi][r]);
 #pragma unroll
       for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));  // the 32 lanes of this row
-      if (frow == 0) s_amax[wn * SBM + wm * 64 + mi * 32 + item_row(r)] = m;
+      if (frow == 0) s_amax[wn * SBM + wm * SWR + mi * 32 + item_row(r)] = m;
     }
   __syncthreads();
   uint8_t* out = static_cast<uint8_t*>(g.out);
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int mi = 0; mi < SMI; ++mi)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int trow = wm * 64 + mi * 32 + item_row(r);
+      const int trow = wm * SWR + mi * 32 + item_row(r);
       const int row = tc.row0 + trow;
       const float amax =
           fmaxf(fmaxf(s_amax[trow], s_amax[SBM + trow]), fmaxf(s_amax[2 * SBM + trow], s_amax[3 * SBM + trow]));
@@ -475,7 +495,7 @@ template <int STAGE>
 hipError_t launch_stream(const GroupedGemmArgs& g, int groups, int rows, int nt, hipStream_t s) {
   const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&k_grouped_gemm_fp8_stream<STAGE>), SLDS);
   if (e != hipSuccess) return e;
-  k_grouped_gemm_fp8_stream<STAGE><<<grouped_grid(rows, groups, SBM, nt), 512, SLDS, s>>>(g);
+  k_grouped_gemm_fp8_stream<STAGE><<<grouped_grid(rows, groups, SBM, nt), StreamWaves<STAGE>::WAVES * 64, SLDS, s>>>(g);
   return hipGetLastError();
 }
 
