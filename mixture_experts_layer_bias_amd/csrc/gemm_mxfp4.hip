@@ -31,8 +31,18 @@ namespace {
 constexpr int BM = 128, BN = 128, BK = 128;
 constexpr int E8M0_ONE = 127;  // E8M0 code of 2^0
 
+// Waves per block: gate/up 16 (four per SIMD, one block per CU, 32 x 32 wave tiles x gate and up;
+// 4 waves ran 1,467 us, 8 ran 1,255 and 16 ran 1,228 on the DeepSeek-like layer); down 4 (two blocks
+// per CU).
+constexpr int MX_GU_WAVES = 16, MX_DN_WAVES = 4;
+
 template <int STAGE>
 struct MxShape {
+  static constexpr int WAVES = STAGE == 0 ? MX_GU_WAVES : MX_DN_WAVES;
+  static constexpr int WN = WAVES == 4 ? 2 : 4;           // waves along the columns
+  static constexpr int WM = WAVES / WN;                   // ... along the rows
+  static constexpr int MI = BM / WM / 32;                 // 32-row MFMA blocks per wave
+  static constexpr int NI = BN / WN / 32;                 // 32-column blocks per wave (x2 gate/up)
   static constexpr int BROWS = STAGE == 0 ? 2 * BN : BN;  // weight rows per tile
   static constexpr int NSTAGE = STAGE == 0 ? 4 : 3;       // gate/up: one block per CU; down: two
   static constexpr int ABYTES = BM * BK;                  // e4m3 rows
@@ -40,8 +50,9 @@ struct MxShape {
   static constexpr int BSBYTES = BROWS * 4;               // the 4 E8M0 codes of each weight row
   static constexpr int ASBYTES = BM * 4;                  // the fp32 scale of each activation row
   static constexpr int SBYTES = ABYTES + BBYTES + BSBYTES + ASBYTES;
-  static constexpr int B_DMA = BBYTES / 1024 / 4;         // 16-byte B loads per wave per step
-  static constexpr int VM = 4 + B_DMA + 1 + 1;            // load instructions per wave per step
+  static constexpr int A_DMA = ABYTES / 1024 / WAVES;     // 16-byte A loads per wave per step
+  static constexpr int B_DMA = BBYTES / 1024 / WAVES;     // 16-byte B loads per wave per step
+  static constexpr int VM = A_DMA + B_DMA + 1 + 1;        // load instructions per wave per step
   static constexpr int LDS = NSTAGE * SBYTES;
 };
 
@@ -74,9 +85,10 @@ __device__ __forceinline__ f32x16 mfma_e4m3_x_e2m1(i32x8 a, i32x8 b, int b_scale
 }
 
 template <int STAGE>
-__global__ __launch_bounds__(256, STAGE == 0 ? 1 : 2) void k_grouped_gemm_mxfp4(GroupedGemmArgs g) {
+__global__ __launch_bounds__(MxShape<STAGE>::WAVES * 64, STAGE == 0 ? 1 : 2) void k_grouped_gemm_mxfp4(GroupedGemmArgs g) {
   using S = MxShape<STAGE>;
-  constexpr int NSTAGE = S::NSTAGE, VM = S::VM, BROWS = S::BROWS;
+  constexpr int NSTAGE = S::NSTAGE, VM = S::VM, BROWS = S::BROWS, MI = S::MI, NI = S::NI;
+  constexpr int WR = BM / S::WM, WC = BN / S::WN;  // a wave's tile rows and columns
   extern __shared__ __align__(16) uint8_t smem[];  // S::LDS bytes: the ring
   int* s_prefix = reinterpret_cast<int*>(smem);     // scheduler scratch, dead before the first load
   int* s_wsum = s_prefix + kMaxGroups + 1;
@@ -122,10 +134,10 @@ __global__ __launch_bounds__(256, STAGE == 0 ? 1 : 2) void k_grouped_gemm_mxfp4(
   // chunk) per LDS cycle; these swizzles put them in 16 different 16-byte bank groups.  Scales: 4-byte pieces, the weight rows' E8M0 words (gate/up: 64 rows per
   // wave; down: 32) and the activation rows' fp32 scales (32 rows per wave), row r at 4 r.
   const uint8_t* a_src = static_cast<const uint8_t*>(g.a);
-  const uint8_t* a_ptr[4];
+  const uint8_t* a_ptr[S::A_DMA];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int trow = (4 * wave + i) * 8 + lane / 8;
+  for (int i = 0; i < S::A_DMA; ++i) {
+    const int trow = (S::A_DMA * wave + i) * 8 + lane / 8;
     a_ptr[i] = a_src + (size_t)a_row(trow) * KD + (((lane % 8) ^ ((trow >> 1) & 7)) << 4);
   }
   const uint8_t* b_ptr[S::B_DMA];
@@ -134,11 +146,12 @@ __global__ __launch_bounds__(256, STAGE == 0 ? 1 : 2) void k_grouped_gemm_mxfp4(
     const int wr = (S::B_DMA * wave + i) * 16 + lane / 4;
     b_ptr[i] = weight_row(wr, wa, wb, (size_t)KD / 2) + (((lane % 4) ^ ((wr >> 2) & 3)) << 4);
   }
-  const int bs_rows = BROWS / 4;  // E8M0 rows per wave
+  const int bs_rows = BROWS / S::WAVES;  // E8M0 rows per wave
   const bool bs_lane = lane < bs_rows;
   const uint8_t* bs_ptr = weight_row(bs_lane ? wave * bs_rows + lane : 0, sa_w, sb_w, (size_t)KD / 32);
-  const bool as_lane = lane < 32;
-  const float* as_ptr = g.a_scales + (size_t)a_row(as_lane ? wave * 32 + lane : 0) * KB;
+  const int as_rows = BM / S::WAVES;  // activation-scale rows per wave
+  const bool as_lane = lane < as_rows;
+  const float* as_ptr = g.a_scales + (size_t)a_row(as_lane ? wave * as_rows + lane : 0) * KB;
 
   auto issue = [&](int buf, int kb) {
     uint8_t* sa = smem + buf * S::SBYTES;
@@ -146,23 +159,23 @@ __global__ __launch_bounds__(256, STAGE == 0 ? 1 : 2) void k_grouped_gemm_mxfp4(
     uint8_t* sbs = sb + S::BBYTES;
     uint8_t* sas = sbs + S::BSBYTES;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(a_ptr[i] + (size_t)kb * BK, sa + (4 * wave + i) * 1024);
+    for (int i = 0; i < S::A_DMA; ++i) dma16(a_ptr[i] + (size_t)kb * BK, sa + (S::A_DMA * wave + i) * 1024);
 #pragma unroll
     for (int i = 0; i < S::B_DMA; ++i) dma16(b_ptr[i] + (size_t)kb * (BK / 2), sb + (S::B_DMA * wave + i) * 1024);
     if (bs_lane) dma4(bs_ptr + (size_t)kb * 4, sbs + wave * bs_rows * 4);
-    if (as_lane) dma4(as_ptr + kb, sas + wave * 128);
+    if (as_lane) dma4(as_ptr + kb, sas + wave * as_rows * 4);
   };
 
-  constexpr int NB = STAGE == 0 ? 4 : 2;
-  f32x16 acc[2][NB];
+  constexpr int NB = STAGE == 0 ? 2 * NI : NI;
+  f32x16 acc[MI][NB];
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][nb][r] = 0.f;
 
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / S::WN, wn = wave % S::WN;
   const int frow = lane & 31, half = lane >> 5;  // the lane's row and half of a 64-wide MFMA step
   auto item_row = [&](int r) { return 8 * (r / 4) + 4 * half + (r % 4); };
 
@@ -180,20 +193,20 @@ __global__ __launch_bounds__(256, STAGE == 0 ? 1 : 2) void k_grouped_gemm_mxfp4(
     const uint8_t* sb = sa + S::ABYTES;
     const uint32_t* sbs = reinterpret_cast<const uint32_t*>(sb + S::BBYTES);
     const float* sas = reinterpret_cast<const float*>(sb + S::BBYTES + S::BSBYTES);
-    f32x16 blk[2][NB];
+    f32x16 blk[MI][NB];
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) blk[mi][nb][r] = 0.f;
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 64) {
-      i32x8 af[2], bfr[NB];
+      i32x8 af[MI], bfr[NB];
       int bsc[NB];
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi) {
-        const int ar = wm * 64 + mi * 32 + frow;
+      for (int mi = 0; mi < MI; ++mi) {
+        const int ar = wm * WR + mi * 32 + frow;
         const uint8_t* rowp = sa + ar * BK;
         const int c1 = kk / 16 + half, c2 = kk / 16 + 2 + half;  // memory K 16 h and 32 + 16 h
         const u32x4 lo = *reinterpret_cast<const u32x4*>(rowp + ((c1 ^ ((ar >> 1) & 7)) << 4));
@@ -202,24 +215,24 @@ __global__ __launch_bounds__(256, STAGE == 0 ? 1 : 2) void k_grouped_gemm_mxfp4(
       }
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        // stage 0: nb 0,1 -> gate rows, nb 2,3 -> up rows of the same columns
-        const int wr = (STAGE == 0 && nb >= 2 ? BN : 0) + wn * 64 + (nb & 1) * 32 + frow;
+        // stage 0: nb < NI -> gate rows, nb >= NI -> up rows of the same columns
+        const int wr = (STAGE == 0 && nb >= NI ? BN : 0) + wn * WC + (nb % NI) * 32 + frow;
         const int c = kk / 32 + half;  // memory block of the lane's 32 codes (16 bytes)
         const u32x4 v = *reinterpret_cast<const u32x4*>(sb + wr * (BK / 2) + ((c ^ ((wr >> 2) & 3)) << 4));
         bfr[nb] = i32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
         bsc[nb] = (int)((sbs[wr] >> (8 * c)) & 0xFFu);
       }
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
+      for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) blk[mi][nb] = mfma_e4m3_x_e2m1(af[mi], bfr[nb], bsc[nb], blk[mi][nb]);
     }
     // promote this K step: acc += blk * (activation row scale); the weight scales are inside blk
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float rs = sas[wm * 64 + mi * 32 + item_row(r)];
+        const float rs = sas[wm * WR + mi * 32 + item_row(r)];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[mi][nb][r] += blk[mi][nb][r] * rs;
       }
@@ -229,14 +242,14 @@ __global__ __launch_bounds__(256, STAGE == 0 ? 1 : 2) void k_grouped_gemm_mxfp4(
   if (STAGE == 1) {
     uint16_t* out = static_cast<uint16_t*>(g.out);
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = tc.row0 + wm * 64 + mi * 32 + item_row(r);
+        const int row = tc.row0 + wm * WR + mi * 32 + item_row(r);
         if (row >= tc.row_end) continue;
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
-          const int col = n0 + wn * 64 + ni * 32 + (lane % 32);
+        for (int ni = 0; ni < NI; ++ni) {
+          const int col = n0 + wn * WC + ni * 32 + (lane % 32);
           out[(size_t)row * NCOLS + col] = (uint16_t)f32_to_bf16(acc[mi][ni][r]);
         }
       }
@@ -245,37 +258,39 @@ __global__ __launch_bounds__(256, STAGE == 0 ? 1 : 2) void k_grouped_gemm_mxfp4(
 
   // ---- gate/up epilogue: h = silu(g) * u, quantised per row over this tile's 128 columns
   __syncthreads();  // every wave is past its last ring read: the per-row maxima reuse the ring
-  float* s_amax = reinterpret_cast<float*>(smem);  // [2][BM]
-  float h[2][16][2];
+  float* s_amax = reinterpret_cast<float*>(smem);  // [WN][BM]
+  float h[MI][16][NI];
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float m = 0.f;
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni) {
-        h[mi][r][ni] = silu(acc[mi][ni][r]) * acc[mi][ni + 2][r];
+      for (int ni = 0; ni < NI; ++ni) {
+        h[mi][r][ni] = silu(acc[mi][ni][r]) * acc[mi][ni + NI][r];
         m = fmaxf(m, fabsf(h[mi][r][ni]));
       }
 #pragma unroll
       for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));  // the row's 32 lanes
-      if ((lane & 31) == 0) s_amax[wn * BM + wm * 64 + mi * 32 + item_row(r)] = m;
+      if ((lane & 31) == 0) s_amax[wn * BM + wm * WR + mi * 32 + item_row(r)] = m;
     }
   __syncthreads();
   uint8_t* out = static_cast<uint8_t*>(g.out);
   const int groups = NCOLS / 128;
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int trow = wm * 64 + mi * 32 + item_row(r);
+      const int trow = wm * WR + mi * 32 + item_row(r);
       const int row = tc.row0 + trow;
-      const float amax = fmaxf(s_amax[trow], s_amax[BM + trow]);
+      float amax = s_amax[trow];
+#pragma unroll
+      for (int w = 1; w < S::WN; ++w) amax = fmaxf(amax, s_amax[w * BM + trow]);
       const float inv = amax > 0.f ? 448.0f / amax : 1.0f;
       if (row < tc.row_end) {
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
-          const int col = n0 + wn * 64 + ni * 32 + (lane % 32);
+        for (int ni = 0; ni < NI; ++ni) {
+          const int col = n0 + wn * WC + ni * 32 + (lane % 32);
           out[(size_t)row * NCOLS + col] = (uint8_t)f32_to_e4m3(h[mi][r][ni] * inv);
         }
         if (wn == 0 && (lane & 31) == 0) g.out_scales[(size_t)row * groups + tc.n_tile] = amax > 0.f ? amax / 448.0f : 1.0f;
@@ -292,11 +307,11 @@ hipError_t launch_grouped_gemm_mxfp4(const GroupedGemmArgs& g, hipStream_t s) {
   if (g.stage == 0) {
     const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&k_grouped_gemm_mxfp4<0>), MxShape<0>::LDS);
     if (e != hipSuccess) return e;
-    k_grouped_gemm_mxfp4<0><<<grouped_grid(rows, groups, BM, g.I / BN), 256, MxShape<0>::LDS, s>>>(g);
+    k_grouped_gemm_mxfp4<0><<<grouped_grid(rows, groups, BM, g.I / BN), MxShape<0>::WAVES * 64, MxShape<0>::LDS, s>>>(g);
   } else {
     const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&k_grouped_gemm_mxfp4<1>), MxShape<1>::LDS);
     if (e != hipSuccess) return e;
-    k_grouped_gemm_mxfp4<1><<<grouped_grid(rows, groups, BM, g.H / BN), 256, MxShape<1>::LDS, s>>>(g);
+    k_grouped_gemm_mxfp4<1><<<grouped_grid(rows, groups, BM, g.H / BN), MxShape<1>::WAVES * 64, MxShape<1>::LDS, s>>>(g);
   }
   return hipGetLastError();
 }
