@@ -303,7 +303,8 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ part, in
 // counting sort by expert in ONE block of 16 waves, so a decode step spends one
 // launch on both (same results as k_topk followed by the three sort passes).
 // Expanded row i of expert e lands at offsets[e] + (the number of rows j < i of
-// expert e), counted from LDS broadcast reads of the ids.
+// expert e): up to 64 rows, one wave finds it from ballots; otherwise every row
+// counts it from LDS broadcast reads of the ids.
 template <int MAXJ>
 __global__ __launch_bounds__(1024) void k_topk_sort_small(const float* __restrict__ part, int nslices,
                                                          float* __restrict__ logits, const float* __restrict__ bias,
@@ -329,6 +330,62 @@ __global__ __launch_bounds__(1024) void k_topk_sort_small(const float* __restric
     if (lane < K) s_ids[t * K + lane] = my_id;
   }
   __syncthreads();
+  if (P <= kWave) {
+    // Up to 64 rows (decode): wave 0 sorts them with ballots.  Lane p holds row p's id v; one ballot
+    // per id bit, from the top, splits the rows into those with a smaller id (lt) and those with
+    // the same id (eq), so row p lands at |lt| + |{q in eq : q < p}|: the stable counting sort.
+    if (wave == 0) {
+      const bool valid = lane < P;
+      const int v = valid ? s_ids[lane] : 0;
+      uint64_t eq = __ballot(valid), lt = 0;
+      for (int b = 31 - __builtin_clz((unsigned)R); b >= 0; --b) {  // ids < R fit in these bits
+        const bool bit = (v >> b) & 1;
+        const uint64_t ones = __ballot(valid && bit);
+        if (bit) {
+          lt |= eq & ~ones;
+          eq &= ones;
+        } else {
+          eq &= ~ones;
+        }
+      }
+      const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));  // lanes before this one
+      const int rank = __popcll(eq & below);
+      if (valid) {
+        const int pos = __popcll(lt) + rank;
+        sorted_ids[pos] = lane;
+        inv_perm[lane] = pos;
+        if (rank == 0) s_off[v] = __popcll(eq);  // the expert's first row writes its count
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // exclusive scan of the R counts: lane l owns buckets [l C, l C + C)
+      const int C = (R + kWave - 1) / kWave;
+      int sum = 0;
+      for (int c = 0; c < C; ++c) {
+        const int r = lane * C + c;
+        if (r < R) sum += s_off[r];
+      }
+      int incl = sum;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int xo = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += xo;
+      }
+      int run = incl - sum;
+      for (int c = 0; c < C; ++c) {
+        const int r = lane * C + c;
+        if (r < R) {
+          const int cnt = s_off[r];
+          counts[r] = cnt;
+          offsets[r] = run;
+          run += cnt;
+        }
+      }
+      if (lane == kWave - 1) offsets[R] = incl;  // = P
+    }
+    return;
+  }
   // one expanded row per thread, in order
   const int v = tid < P ? s_ids[tid] : -1;
   if (v >= 0) atomicAdd(&s_off[v], 1);

@@ -239,6 +239,31 @@ def _dequant_dev(q: torch.Tensor, sc: torch.Tensor) -> np.ndarray:
     return om.dequant_rows(q.cpu().numpy(), sc.cpu().numpy())
 
 
+# (tokens, top-K, router width, real experts): the one-block top-K + sort of small batches, with up to 64
+# rows (one wave sorts them with ballots) and beyond (every row counts its rank), identity experts included
+SMALL_SORT = [(1, 1, 1, 1), (1, 8, 64, 64), (4, 8, 128, 128), (8, 8, 128, 128), (5, 12, 384, 256),
+              (2, 32, 1024, 1000), (9, 8, 128, 128), (64, 16, 1024, 1024)]
+
+
+@pytest.mark.parametrize("N,K,R,E", SMALL_SORT)
+def test_small_batch_sort_bit_exact(N, K, R, E):
+    """moe_forward's counts, offsets, sorted ids and inverse permutation equal the oracle's counting
+    sort of the ids the GPU chose (so near-ties cannot interfere)."""
+    print(f"\n[case] small-batch sort N{N} K{K} R{R} E{E}", flush=True)
+    wl = W(f"sort{N}_{K}_{R}", N, 128, E, R, K, 128, 0, "softmax", False, 1.0, "bf16", R > E, seed=31)
+    dl = mi.device.device_layer(wl)
+    cfg, w = config_of(wl), weights_of(dl)
+    out, ws = run_forward(cfg, w, dl.x)
+    torch.cuda.synchronize()
+    L = moe.moe_workspace_layout(cfg)
+    rd = lambda k, n: ws[L[k]:L[k] + 4 * n].view(torch.int32).cpu().numpy()
+    gids = rd("topk_ids", N * K).reshape(N, K)
+    assert ((gids >= 0) & (gids < R)).all() and all(len(set(r)) == K for r in gids)
+    oc, oo, osid, oinv = om.sort_by_expert(gids, R)
+    assert np.array_equal(rd("counts", R), oc) and np.array_equal(rd("offsets", R + 1), oo)
+    assert np.array_equal(rd("sorted_ids", N * K), osid) and np.array_equal(rd("inv_perm", N * K), oinv)
+
+
 def test_quantize_fp8_is_bit_exact():
     """Activation codes and scales equal the oracle's fp32 recipe bit for bit,
     including zero groups, tiny groups and large magnitudes."""
