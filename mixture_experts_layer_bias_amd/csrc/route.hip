@@ -187,7 +187,9 @@ __device__ __forceinline__ int topk_token(const float* __restrict__ part, int ns
 #pragma unroll
   for (int j = 0; j < MAXJ; ++j) {
     const int r = lane + 64 * j;
-    if (r < R) {
+    if (r < R && nslices == 1) {  // whole logits (the GEMV router): one load
+      v[j] = part[(size_t)t * R + r];
+    } else if (r < R) {
       // all planes are loaded before the (in-order) additions, so the loads overlap
       float pl[16];
 #pragma unroll
@@ -197,7 +199,7 @@ __device__ __forceinline__ int topk_token(const float* __restrict__ part, int ns
       for (int z = 1; z < 16; ++z)
         if (z < nslices) acc += pl[z];
       v[j] = acc;
-      if (nslices > 1) logits[(size_t)t * R + r] = acc;
+      logits[(size_t)t * R + r] = acc;
     } else {
       v[j] = -INFINITY;
     }
@@ -255,14 +257,13 @@ __device__ __forceinline__ int topk_token(const float* __restrict__ part, int ns
     for (int j = 0; j < MAXJ; ++j)
       if ((avail >> j) & 1u) best = key[j] > best ? key[j] : best;
     best = wave_max_u32(best);
+    // the lowest column holding it: slices from the top, so the lowest slice with a hit is the
+    // last to set r_star (selects, no branches)
     int r_star = 0;
 #pragma unroll
-    for (int j = 0; j < MAXJ; ++j) {
+    for (int j = MAXJ - 1; j >= 0; --j) {
       const uint64_t hit = __ballot(((avail >> j) & 1u) && key[j] == best);
-      if (hit) {  // uniform
-        r_star = 64 * j + (int)__builtin_ctzll(hit);
-        break;
-      }
+      r_star = hit ? 64 * j + (int)__builtin_ctzll(hit) : r_star;
     }
     if (lane == (r_star & 63)) avail &= ~(1u << (r_star >> 6));
     if (lane == k) my_id = r_star;
