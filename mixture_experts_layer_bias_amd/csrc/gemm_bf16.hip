@@ -112,6 +112,9 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_bf16(GroupedGemmArgs g)
 
   const int wm = wave >> 1, wn = wave & 1;
   const int frow = lane & 31, fk = (lane >> 5) * 8;
+  // 32-row MFMA blocks that lie wholly past the segment's last row hold only padding: their
+  // waves skip the fragment reads and products (wave-uniform), which leaves them zero
+  const int live_mi = (tc.row0 + wm * 64 < tc.row_end) + (tc.row0 + wm * 64 + 32 < tc.row_end);
 
   load_tile(0);
   store_tile();
@@ -121,9 +124,11 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_bf16(GroupedGemmArgs g)
     if (kt + 1 < nk) load_tile((kt + 1) * BK);
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 16) {
+      if (live_mi == 0) break;
       u32x4 af[2], bfr[NB];
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi) af[mi] = ld16(a_lds + (wm * 64 + mi * 32 + frow) * LDS_STRIDE + kk + fk);
+      for (int mi = 0; mi < 2; ++mi)
+        if (mi < live_mi) af[mi] = ld16(a_lds + (wm * 64 + mi * 32 + frow) * LDS_STRIDE + kk + fk);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         // stage 0: nb 0,1 -> gate rows, nb 2,3 -> up rows of the same columns
@@ -131,9 +136,11 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_bf16(GroupedGemmArgs g)
         bfr[nb] = ld16(b_lds + brow * LDS_STRIDE + kk + fk);
       }
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
+      for (int mi = 0; mi < 2; ++mi) {
+        if (mi >= live_mi) continue;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[mi][nb] = mfma_32x32x16_bf16(af[mi], bfr[nb], acc[mi][nb]);
+      }
     }
     __syncthreads();
     if (kt + 1 < nk) {

@@ -392,6 +392,12 @@ __global__ __launch_bounds__(StreamWaves<STAGE>::WAVES * 64, 1) void k_grouped_g
   // weight-scale row of block nb: gate/up: gate (0) or up (1); down: column block of 64 wn + 32 nb
   const int ws_row0 = STAGE == 0 ? 0 : (wn * 64) / 128, ws_row1 = STAGE == 0 ? 1 : (wn * 64 + 32) / 128;
 
+  // 32-row MFMA blocks that lie wholly past the segment's last row hold only padding: their
+  // waves skip the fragment reads and products (wave-uniform), which leaves them zero
+  int live_mi = 0;
+#pragma unroll
+  for (int mi = 0; mi < SMI; ++mi) live_mi += tc.row0 + wm * SWR + mi * 32 < tc.row_end;
+
 #pragma unroll
   for (int s = 0; s < SNSTAGE - 1; ++s)
     if (s < KB) issue(s, s);
@@ -402,6 +408,7 @@ __global__ __launch_bounds__(StreamWaves<STAGE>::WAVES * 64, 1) void k_grouped_g
     __builtin_amdgcn_s_barrier();  // ... in every wave; every wave is done with step kb - 1
     __builtin_amdgcn_sched_barrier(0);
     if (kb + SNSTAGE - 1 < KB) issue((kb + SNSTAGE - 1) % SNSTAGE, kb + SNSTAGE - 1);
+    if (live_mi == 0) continue;
     const uint8_t* sa = smem + (kb % SNSTAGE) * SSTAGE;
     const uint8_t* sb = sa + SABYTES;
     const float* ss = reinterpret_cast<const float*>(sb + SBBYTES);
@@ -411,6 +418,7 @@ __global__ __launch_bounds__(StreamWaves<STAGE>::WAVES * 64, 1) void k_grouped_g
       i32x8 af[SMI], bf[2];
 #pragma unroll
       for (int mi = 0; mi < SMI; ++mi) {
+        if (mi >= live_mi) continue;
         const int row = wm * SWR + mi * 32 + frow;
         const u32x4 lo = lds16(sa, row, c0), hi = lds16(sa, row, c0 + 1);
         af[mi] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
@@ -424,6 +432,7 @@ __global__ __launch_bounds__(StreamWaves<STAGE>::WAVES * 64, 1) void k_grouped_g
       for (int mi = 0; mi < SMI; ++mi)
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
+          if (mi >= live_mi) continue;
           if (ks == 0) blk[mi][nb] = mfma_32x32x64_fp8(af[mi], bf[nb], f32x16{});
           else blk[mi][nb] = mfma_32x32x64_fp8(af[mi], bf[nb], blk[mi][nb]);
         }
@@ -431,7 +440,8 @@ __global__ __launch_bounds__(StreamWaves<STAGE>::WAVES * 64, 1) void k_grouped_g
     // promote this scale block: acc += blk * (row scale * weight-block scale)
     const float ws0 = s_ws[ws_row0 * SMAXKB + kb], ws1 = s_ws[ws_row1 * SMAXKB + kb];
 #pragma unroll
-    for (int mi = 0; mi < SMI; ++mi)
+    for (int mi = 0; mi < SMI; ++mi) {
+      if (mi >= live_mi) continue;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {  // items 4 q .. 4 q + 3 are 4 consecutive rows
         const f32x4 rs = *reinterpret_cast<const f32x4*>(ss + wm * SWR + mi * 32 + 8 * q + 4 * fh);
@@ -441,6 +451,7 @@ __global__ __launch_bounds__(StreamWaves<STAGE>::WAVES * 64, 1) void k_grouped_g
           acc[mi][1][4 * q + j] += blk[mi][1][4 * q + j] * (rs[j] * ws1);
         }
       }
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 

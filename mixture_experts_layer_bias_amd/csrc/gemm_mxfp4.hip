@@ -178,6 +178,11 @@ __global__ __launch_bounds__(MxShape<STAGE>::WAVES * 64, STAGE == 0 ? 1 : 2) voi
   const int wm = wave / S::WN, wn = wave % S::WN;
   const int frow = lane & 31, half = lane >> 5;  // the lane's row and half of a 64-wide MFMA step
   auto item_row = [&](int r) { return 8 * (r / 4) + 4 * half + (r % 4); };
+  // 32-row MFMA blocks that lie wholly past the segment's last row hold only padding: their
+  // waves skip the fragment reads and products (wave-uniform), which leaves them zero
+  int live_mi = 0;
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) live_mi += tc.row0 + wm * WR + mi * 32 < tc.row_end;
 
 #pragma unroll
   for (int s = 0; s < NSTAGE - 1; ++s)
@@ -189,6 +194,7 @@ __global__ __launch_bounds__(MxShape<STAGE>::WAVES * 64, STAGE == 0 ? 1 : 2) voi
     __builtin_amdgcn_s_barrier();  // step kb has landed in every wave; every wave is done with kb - 1
     __builtin_amdgcn_sched_barrier(0);
     if (kb + NSTAGE - 1 < KB) issue((kb + NSTAGE - 1) % NSTAGE, kb + NSTAGE - 1);
+    if (live_mi == 0) continue;
     const uint8_t* sa = smem + (kb % NSTAGE) * S::SBYTES;
     const uint8_t* sb = sa + S::ABYTES;
     const uint32_t* sbs = reinterpret_cast<const uint32_t*>(sb + S::BBYTES);
@@ -206,6 +212,7 @@ __global__ __launch_bounds__(MxShape<STAGE>::WAVES * 64, STAGE == 0 ? 1 : 2) voi
       int bsc[NB];
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
+        if (mi >= live_mi) continue;
         const int ar = wm * WR + mi * 32 + frow;
         const uint8_t* rowp = sa + ar * BK;
         const int c1 = kk / 16 + half, c2 = kk / 16 + 2 + half;  // memory K 16 h and 32 + 16 h
@@ -223,19 +230,23 @@ __global__ __launch_bounds__(MxShape<STAGE>::WAVES * 64, STAGE == 0 ? 1 : 2) voi
         bsc[nb] = (int)((sbs[wr] >> (8 * c)) & 0xFFu);
       }
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
+      for (int mi = 0; mi < MI; ++mi) {
+        if (mi >= live_mi) continue;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) blk[mi][nb] = mfma_e4m3_x_e2m1(af[mi], bfr[nb], bsc[nb], blk[mi][nb]);
+      }
     }
     // promote this K step: acc += blk * (activation row scale); the weight scales are inside blk
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+    for (int mi = 0; mi < MI; ++mi) {
+      if (mi >= live_mi) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float rs = sas[wm * WR + mi * 32 + item_row(r)];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[mi][nb][r] += blk[mi][nb][r] * rs;
       }
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 
