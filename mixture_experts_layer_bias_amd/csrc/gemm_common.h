@@ -27,15 +27,18 @@ struct TileCoord {
   int m_tile;
   int n_tile;
   int row0;     // first sorted row of the tile
-  int row_end;  // end of the expert's segment
+  int row_end;  // end of the tile's rows: the segment's end, or the next tile's first row (even split)
   int m_tiles;  // row tiles over all groups (the tiles of one column tile)
 };
 
 // s_prefix must hold kMaxGroups + 1 ints in LDS.  Block of at least 256 threads.  `b` is the
 // block's tile slot (blockIdx.x unless one launch runs several grids of tiles).
+// split_align == 0: a segment's tiles start every BM rows, the last one ragged.  split_align > 0 (a
+// divisor of BM): the segment is cut into the same number of tiles, of ceil(rows / tiles) rows
+// rounded up to split_align, so its tiles carry nearly equal work (130 rows: 96 + 34, not 128 + 2).
 __device__ __forceinline__ TileCoord schedule_tile_at(const int32_t* __restrict__ offsets, int num_groups,
                                                       int shared_rows, int BM, int NT, int* s_prefix, int* s_wsum,
-                                                      int b) {
+                                                      int b, int split_align = 0) {
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   // each thread owns 4 consecutive groups
   int cnt[4], local = 0;
@@ -89,14 +92,22 @@ __device__ __forceinline__ TileCoord schedule_tile_at(const int32_t* __restrict_
   tc.n_tile = rem / mt_e;
   tc.m_tile = rem % mt_e;
   const int seg0 = shared_rows >= 0 ? 0 : offsets[e];
-  tc.row_end = shared_rows >= 0 ? shared_rows : offsets[e + 1];
-  tc.row0 = seg0 + tc.m_tile * BM;
+  const int seg_end = shared_rows >= 0 ? shared_rows : offsets[e + 1];
+  // rows per tile: BM, or the even split (never above BM, and mt_e - 1 tiles of it stay below the
+  // segment's rows, so every tile is non-empty)
+  int rpt = BM;
+  if (split_align > 0 && mt_e > 1) {
+    const int even = (seg_end - seg0 + mt_e - 1) / mt_e;
+    rpt = (even + split_align - 1) / split_align * split_align;
+  }
+  tc.row0 = seg0 + tc.m_tile * rpt;
+  tc.row_end = min(tc.row0 + rpt, seg_end);
   return tc;
 }
 
 __device__ __forceinline__ TileCoord schedule_tile(const int32_t* __restrict__ offsets, int num_groups, int shared_rows,
-                                                   int BM, int NT, int* s_prefix, int* s_wsum) {
-  return schedule_tile_at(offsets, num_groups, shared_rows, BM, NT, s_prefix, s_wsum, blockIdx.x);
+                                                   int BM, int NT, int* s_prefix, int* s_wsum, int split_align = 0) {
+  return schedule_tile_at(offsets, num_groups, shared_rows, BM, NT, s_prefix, s_wsum, blockIdx.x, split_align);
 }
 
 // Grid size for a grouped GEMM: an upper bound of the tile count, rounded up to 8.

@@ -53,7 +53,7 @@ __global__ __launch_bounds__(256, STAGE == 0 ? 1 : 2) void k_grouped_gemm_fp8(Gr
   const int NT = NCOLS / BN;
   const int KB = KD / 128;  // scale blocks along K
   const TileCoord tc =
-      schedule_tile(g.offsets, g.shared ? 1 : g.E, g.shared ? g.N : -1, BM, NT, s_prefix, s_wsum);
+      schedule_tile(g.offsets, g.shared ? 1 : g.E, g.shared ? g.N : -1, BM, NT, s_prefix, s_wsum, 32);
   if (tc.expert < 0) return;
 
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
@@ -296,7 +296,7 @@ __global__ __launch_bounds__(StreamWaves<STAGE>::WAVES * 64, 1) void k_grouped_g
   const int NT = NCOLS / COLS;
   const int KB = KD / 128;
   const TileCoord tc =
-      schedule_tile(g.offsets, g.shared ? 1 : g.E, g.shared ? g.N : -1, SBM, NT, s_prefix, s_wsum);
+      schedule_tile(g.offsets, g.shared ? 1 : g.E, g.shared ? g.N : -1, SBM, NT, s_prefix, s_wsum, 32);
   if (tc.expert < 0) return;  // the same decision in every thread
 
   const int tid = threadIdx.x, lane = tid % kWave;
