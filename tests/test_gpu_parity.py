@@ -336,6 +336,57 @@ def test_fp8_stages_match_oracle(name):
         assert_close(f64(shy), om.down_fp8(shq_ref, shs_ref, sd), FP8_TOL, "fp8 shared y")
 
 
+# Segment sizes around the 32-row block and 128-row tile edges, where the fp8 kernels' even split of a
+# segment's tiles moves the tile boundaries (130 rows: 96 + 34; 257: 96 + 96 + 65).  The first case runs
+# the streaming kernels (up to 256 rows per group), the second the register-staged ones.
+SEGMENTS = {
+    "streaming": (600, 4, [0, 1, 31, 32, 33, 96, 97, 127, 128, 129, 130, 160, 255, 256, 257, 385]),
+    "register_staged": (450, 2, [257, 640]),
+}
+
+
+@pytest.mark.parametrize("name", list(SEGMENTS))
+def test_fp8_segment_edges_match_oracle(name):
+    N, K, counts = SEGMENTS[name]
+    E, H, I = len(counts), 256, 256
+    print(f"\n[case] fp8 segment edges {name}: counts {counts}", flush=True)
+    wl = W(f"fp8seg{E}", N, H, E, E, K, I, 0, "sigmoid", True, 2.5, "fp8", True, seed=31)
+    P = N * K
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    Pr = int(offsets[E])
+    assert Pr <= P
+    rng = np.random.default_rng(31)
+    sid = rng.permutation(P).astype(np.int32)  # the first Pr slots are the routed rows, in segment order
+    dl = mi.device.device_layer(wl)
+    cfg, w = config_of(wl), weights_of(dl)
+    host = mi.host_inputs(wl)
+    xq_ref, xs_ref = om.quantize_fp8_groups(om.bf16_to_f64(host.x).astype(np.float32))
+    hq_ref = np.zeros((P, I), np.uint8)
+    hs_ref = np.ones((P, I // 128), np.float32)
+    y_ref = np.zeros((P, H))
+    for e in range(E):
+        rows = np.arange(offsets[e], offsets[e + 1])
+        if len(rows) == 0:
+            continue
+        wg, wu, wd = mi.host_expert(wl, e)
+        t = sid[rows] // K
+        hq_ref[rows], hs_ref[rows] = om.gate_up_fp8(xq_ref[t], xs_ref[t], wg, wu)
+        y_ref[rows] = om.down_fp8(hq_ref[rows], hs_ref[rows], wd)
+    sid_d, off_d = torch.from_numpy(sid).cuda(), torch.from_numpy(offsets).cuda()
+    hq = torch.zeros((P, I), dtype=torch.uint8, device="cuda")
+    hs = torch.zeros((P, I // 128), dtype=torch.float32, device="cuda")
+    moe.moe_grouped_gemm(cfg, 0, 0, w, torch.from_numpy(xq_ref).cuda(), torch.from_numpy(xs_ref).cuda(), sid_d,
+                         off_d, hq, hs)
+    y = torch.zeros((P, H), dtype=torch.bfloat16, device="cuda")
+    moe.moe_grouped_gemm(cfg, 1, 0, w, torch.from_numpy(hq_ref).cuda(), torch.from_numpy(hs_ref).cuda(), sid_d,
+                         off_d, y)
+    torch.cuda.synchronize()
+    assert_close(_dequant_dev(hq, hs)[:Pr], om.dequant_rows(hq_ref[:Pr], hs_ref[:Pr]), FP8_TOL, "fp8 h by segment")
+    assert_close(f64(y)[:Pr], y_ref[:Pr], FP8_TOL, "fp8 y by segment")
+    # every row is written by exactly one tile: rows past the routed ones stay untouched
+    assert (hq[Pr:] == 0).all() and (hs[Pr:] == 0).all() and (bits(y)[Pr:] == 0).all()
+
+
 # ============================================================================ end to end
 
 @pytest.mark.parametrize("name", list(SMALL) + list(FP8_SMALL))
