@@ -38,8 +38,8 @@ MEASURED_TRAFFIC = {
                     "mixture_experts_layer_bias_amd/csrc/gemm_common.h",
                     "mixture_experts_layer_bias_amd/csrc/unpermute.h",
                     "mixture_experts_layer_bias_amd/csrc/common.h"],
-        "sha256": "56072b933dd1000aef22a59d0d32ccd8df9357d493feb2340963cf911a0c6a7d",
-        "fetch_kib": 140123.25, "write_kib": 253.78, "fetch_scale": 2.0, "write_scale": 1.0,
+        "sha256": "74c10d1180400613c8c488d4182eaa59096788872960652ab2e8dcf822e7b8af",
+        "fetch_kib": 140121.41, "write_kib": 253.78, "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
 

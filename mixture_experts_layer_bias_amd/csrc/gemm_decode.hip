@@ -186,17 +186,6 @@ __device__ __forceinline__ void decode_tile(const GroupedGemmArgs& g, uint8_t* s
     return;
   }
   __syncthreads();               // every wave is done with the scheduler scratch before the loads reuse it
-  if (STAGE == 1 && FUSED) {
-    if (threadIdx.x == 0) {
-      const int count = g.offsets[tc.expert + 1] - g.offsets[tc.expert];
-      const int need = gu_tiles_per_row_tile * ((count + DecodeShape<0>::BM - 1) / DecodeShape<0>::BM);
-      for (int it = 0; it < kDoneSpinLimit; ++it) {
-        if (__hip_atomic_load(done + tc.expert, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need) break;
-        __builtin_amdgcn_s_sleep(2);
-      }
-    }
-    __syncthreads();
-  }
 
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -239,17 +228,24 @@ __device__ __forceinline__ void decode_tile(const GroupedGemmArgs& g, uint8_t* s
       base = wa + (size_t)(n0 + trow) * row_bytes;
     b_ptr[i] = base + ((pslot ^ (trow % LPR)) << 4);
   }
-  auto issue = [&](int stage, int kstep) {
+  auto issue_a = [&](int stage, int kstep) {
     uint8_t* sa = smem + stage * SBYTES;
-    uint8_t* sb = sa + ABYTES;
     const size_t koff = (size_t)kstep * ROWB;
 #pragma unroll
     for (int i = 0; i < AI; ++i) {
       if (STAGE == 1 && FUSED) dma16_device_scope(a_ptr[i] + koff, sa + (wave * AI + i) * 1024);
       else dma16(a_ptr[i] + koff, sa + (wave * AI + i) * 1024);
     }
+  };
+  auto issue_b = [&](int stage, int kstep) {
+    uint8_t* sb = smem + stage * SBYTES + ABYTES;
+    const size_t koff = (size_t)kstep * ROWB;
 #pragma unroll
     for (int i = 0; i < BI; ++i) dma16(b_ptr[i] + koff, sb + (wave * BI + i) * 1024);
+  };
+  auto issue = [&](int stage, int kstep) {
+    issue_a(stage, kstep);
+    issue_b(stage, kstep);
   };
   auto lds_chunk = [&](const uint8_t* base, int row, int chunk) {
     return *reinterpret_cast<const u32x4*>(base + row * ROWB + ((chunk ^ (row % LPR)) << 4));
@@ -272,13 +268,38 @@ __device__ __forceinline__ void decode_tile(const GroupedGemmArgs& g, uint8_t* s
 #pragma unroll
     for (int j = 0; j < NTW; ++j) acc[mi][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  if (STAGE == 1 && FUSED) {
+    // The first stages' weight rows do not depend on h: they are in flight while thread 0 waits
+    // for the expert's gate/up tiles, and only the h loads follow the wait.  The raw barrier
+    // (no vmcnt drain) keeps those weight loads in flight.
 #pragma unroll
-  for (int s = 0; s < NSTAGE - 1; ++s)
-    if (s < nk) issue(s, s);
+    for (int s = 0; s < NSTAGE - 1; ++s)
+      if (s < nk) issue_b(s, s);
+    if (threadIdx.x == 0) {
+      const int count = g.offsets[tc.expert + 1] - g.offsets[tc.expert];
+      const int need = gu_tiles_per_row_tile * ((count + DecodeShape<0>::BM - 1) / DecodeShape<0>::BM);
+      for (int it = 0; it < kDoneSpinLimit; ++it) {
+        if (__hip_atomic_load(done + tc.expert, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need) break;
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < NSTAGE - 1; ++s)
+      if (s < nk) issue_a(s, s);
+  } else {
+#pragma unroll
+    for (int s = 0; s < NSTAGE - 1; ++s)
+      if (s < nk) issue(s, s);
+  }
 
   for (int k = 0; k < nk; ++k) {
     const int later = nk - 1 - k;  // stages issued after step k (capped by the ring depth)
-    wait_stages<NSTAGE, VM>(later < NSTAGE - 2 ? later : NSTAGE - 2);
+    // the fused down prologue issued its stages out of order (weights, then h): the first step
+    // waits for all of them
+    if (STAGE == 1 && FUSED && k == 0) dma_wait<0>();
+    else wait_stages<NSTAGE, VM>(later < NSTAGE - 2 ? later : NSTAGE - 2);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     if (k + NSTAGE - 1 < nk) issue((k + NSTAGE - 1) % NSTAGE, k + NSTAGE - 1);
