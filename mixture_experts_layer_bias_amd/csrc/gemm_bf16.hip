@@ -13,6 +13,11 @@
 // A and B tiles are staged through LDS with a 16-byte pad per row (row stride
 // 144 B) against bank conflicts; the next K step's global loads are issued
 // before the current step's MFMAs (register prefetch).
+//
+// STAGE 0: gate/up.  STAGE 1: down over 128 output columns.  STAGE 2: down over
+// 256 output columns (H a multiple of 256), the same 256 weight rows, 4 MFMA
+// column blocks per wave and registers as gate/up: a wave's 64 x 128 outputs
+// read 0.75 LDS fragments per MFMA instead of 1.
 #include "common.h"
 #include "gemm_common.h"
 #include "kernels.h"
@@ -26,7 +31,8 @@ constexpr int LDS_STRIDE = BK + 8;  // bf16 elements per LDS row
 
 template <int STAGE>
 struct Bf16Tile {
-  static constexpr int BROWS = STAGE == 0 ? 2 * BN : BN;  // weight rows per tile
+  static constexpr int BROWS = STAGE == 1 ? BN : 2 * BN;  // weight rows per tile
+  static constexpr int COLS = STAGE == 2 ? 2 * BN : BN;   // output columns per tile
   static constexpr int A_LOADS = BM * (BK / 8) / 256;      // 16-byte chunks per thread
   static constexpr int B_LOADS = BROWS * (BK / 8) / 256;
   static constexpr int LDS_BYTES = (BM + BROWS) * LDS_STRIDE * 2;
@@ -45,13 +51,13 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_bf16(GroupedGemmArgs g)
 
   const int KD = STAGE == 0 ? g.H : g.I;     // reduction length
   const int NCOLS = STAGE == 0 ? g.I : g.H;  // output columns
-  const int NT = NCOLS / BN;
+  const int NT = NCOLS / T::COLS;
   const TileCoord tc =
       schedule_tile(g.offsets, g.shared ? 1 : g.E, g.shared ? g.N : -1, BM, NT, s_prefix, s_wsum);
   if (tc.expert < 0) return;
 
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int n0 = tc.n_tile * BN;
+  const int n0 = tc.n_tile * T::COLS;
 
   // ---- operand pointers
   const uint16_t* wa;  // gate (stage 0) or down (stage 1) weights
@@ -101,7 +107,7 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_bf16(GroupedGemmArgs g)
     for (int i = 0; i < T::B_LOADS; ++i) st16(b_lds + (lrow + 32 * i) * LDS_STRIDE + lcol, rb[i]);
   };
 
-  constexpr int NB = STAGE == 0 ? 4 : 2;  // B fragments per wave: (gate, up) x 2, or 2
+  constexpr int NB = STAGE == 1 ? 2 : 4;  // B fragments per wave: (gate, up) x 2, 2, or 4
   f32x16 acc[2][NB];
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
@@ -131,8 +137,9 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_bf16(GroupedGemmArgs g)
         if (mi < live_mi) af[mi] = ld16(a_lds + (wm * 64 + mi * 32 + frow) * LDS_STRIDE + kk + fk);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        // stage 0: nb 0,1 -> gate rows, nb 2,3 -> up rows of the same columns
-        const int brow = (STAGE == 0 && nb >= 2 ? BN : 0) + wn * 64 + (nb & 1) * 32 + frow;
+        // stage 0: nb 0,1 -> gate rows, nb 2,3 -> up rows of the same columns; stage 2: nb 2,3 ->
+        // the tile's second 128 columns
+        const int brow = (STAGE != 1 && nb >= 2 ? BN : 0) + wn * 64 + (nb & 1) * 32 + frow;
         bfr[nb] = ld16(b_lds + brow * LDS_STRIDE + kk + fk);
       }
 #pragma unroll
@@ -158,8 +165,8 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_bf16(GroupedGemmArgs g)
       const int row = tc.row0 + wm * 64 + mi * 32 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
       if (row >= tc.row_end) continue;
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni) {
-        const int col = n0 + wn * 64 + ni * 32 + (lane % 32);
+      for (int ni = 0; ni < (STAGE == 2 ? 4 : 2); ++ni) {
+        const int col = n0 + (ni >= 2 ? BN : 0) + wn * 64 + (ni & 1) * 32 + (lane % 32);
         float v;
         if (STAGE == 0) v = silu(acc[mi][ni][r]) * acc[mi][ni + 2][r];
         else v = acc[mi][ni][r];
@@ -177,6 +184,8 @@ hipError_t launch_grouped_gemm_bf16(const GroupedGemmArgs& g, hipStream_t s) {
   if (!g.row_invariant && decode_gemm_fits(g)) return launch_grouped_gemm_decode(g, s);
   if (g.stage == 0) {
     k_grouped_gemm_bf16<0><<<grouped_grid(rows, groups, BM, g.I / BN), 256, 0, s>>>(g);
+  } else if (g.H % (2 * BN) == 0) {
+    k_grouped_gemm_bf16<2><<<grouped_grid(rows, groups, BM, g.H / (2 * BN)), 256, 0, s>>>(g);
   } else {
     k_grouped_gemm_bf16<1><<<grouped_grid(rows, groups, BM, g.H / BN), 256, 0, s>>>(g);
   }
