@@ -47,6 +47,8 @@ SMALL = {
     # many tokens, softmax, sigmoid-gated shared expert
     "gated_shared_150tok": W("gsp", 150, 256, 8, 8, 2, 128, 256, "softmax", True, 1.0, "bf16", False, seed=20,
                              shared_gated=True),
+    # H = 384 (not a multiple of 256): the routed and shared down GEMMs take the 128-column tiles
+    "h384_128col_down_200tok": W("h384", 200, 384, 8, 8, 2, 256, 128, "softmax", True, 1.0, "bf16", False, seed=26),
 }
 FP8_SMALL = {
     "fp8_sigmoid_bias_shared": W("fp8s", 33, 512, 8, 8, 2, 256, 128, "sigmoid", True, 2.5, "fp8", True, seed=9),
