@@ -339,20 +339,23 @@ def test_fp8_stages_match_oracle(name):
 
 
 # Segment sizes around the 32-row block and 128-row tile edges, where the fp8 kernels' even split of a
-# segment's tiles moves the tile boundaries (130 rows: 96 + 34; 257: 96 + 96 + 65).  The first case runs
-# the streaming kernels (up to 256 rows per group), the second the register-staged ones.
+# segment's tiles moves the tile boundaries (130 rows: 96 + 34; 257: 96 + 96 + 65) and every kernel skips
+# the 32-row blocks past a segment's end.  fp8: the first case runs the streaming kernels (up to 256 rows
+# per group), the second the register-staged ones; MXFP4 runs its one kernel pair on both, and bf16 its
+# tile kernels (the decode-shaped ones take only a few rows per expert).
 SEGMENTS = {
-    "streaming": (600, 4, [0, 1, 31, 32, 33, 96, 97, 127, 128, 129, 130, 160, 255, 256, 257, 385]),
-    "register_staged": (450, 2, [257, 640]),
+    "e16_0_to_385_rows": (600, 4, [0, 1, 31, 32, 33, 96, 97, 127, 128, 129, 130, 160, 255, 256, 257, 385]),
+    "e2_257_and_640_rows": (450, 2, [257, 640]),
 }
 
 
+@pytest.mark.parametrize("dtype", ["fp8", "mxfp4"])
 @pytest.mark.parametrize("name", list(SEGMENTS))
-def test_fp8_segment_edges_match_oracle(name):
+def test_quantised_segment_edges_match_oracle(name, dtype):
     N, K, counts = SEGMENTS[name]
     E, H, I = len(counts), 256, 256
-    print(f"\n[case] fp8 segment edges {name}: counts {counts}", flush=True)
-    wl = W(f"fp8seg{E}", N, H, E, E, K, I, 0, "sigmoid", True, 2.5, "fp8", True, seed=31)
+    print(f"\n[case] {dtype} segment edges {name}: counts {counts}", flush=True)
+    wl = W(f"{dtype}seg{E}", N, H, E, E, K, I, 0, "sigmoid", True, 2.5, dtype, True, seed=31)
     P = N * K
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     Pr = int(offsets[E])
@@ -387,6 +390,41 @@ def test_fp8_segment_edges_match_oracle(name):
     assert_close(f64(y)[:Pr], y_ref[:Pr], FP8_TOL, "fp8 y by segment")
     # every row is written by exactly one tile: rows past the routed ones stay untouched
     assert (hq[Pr:] == 0).all() and (hs[Pr:] == 0).all() and (bits(y)[Pr:] == 0).all()
+
+
+@pytest.mark.parametrize("H", [256, 384])  # down over 256-column tiles, and over 128-column ones
+@pytest.mark.parametrize("name", list(SEGMENTS))
+def test_bf16_segment_edges_match_oracle(name, H):
+    N, K, counts = SEGMENTS[name]
+    E, I = len(counts), 256
+    print(f"\n[case] bf16 segment edges {name} H{H}: counts {counts}", flush=True)
+    wl = W(f"bf16seg{E}", N, H, E, E, K, I, 0, "softmax", True, 1.0, "bf16", False, seed=32)
+    P = N * K
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    Pr = int(offsets[E])
+    rng = np.random.default_rng(32)
+    sid = rng.permutation(P).astype(np.int32)
+    dl = mi.device.device_layer(wl)
+    cfg, w = config_of(wl), weights_of(dl)
+    x64 = om.bf16_to_f64(mi.host_inputs(wl).x)
+    h_ref = np.zeros((P, I), np.uint16)
+    y_ref = np.zeros((P, H))
+    for e in range(E):
+        rows = np.arange(offsets[e], offsets[e + 1])
+        if len(rows) == 0:
+            continue
+        wg, wu, wd = mi.host_expert(wl, e)
+        h_ref[rows] = om.gate_up_bf16(x64[sid[rows] // K], wg, wu)
+        y_ref[rows] = om.down_bf16(h_ref[rows], wd)
+    sid_d, off_d = torch.from_numpy(sid).cuda(), torch.from_numpy(offsets).cuda()
+    h = torch.zeros((P, I), dtype=torch.bfloat16, device="cuda")
+    moe.moe_grouped_gemm(cfg, 0, 0, w, dl.x, None, sid_d, off_d, h, None)
+    y = torch.zeros((P, H), dtype=torch.bfloat16, device="cuda")
+    moe.moe_grouped_gemm(cfg, 1, 0, w, from_bits(h_ref), None, sid_d, off_d, y, None)
+    torch.cuda.synchronize()
+    assert_close(f64(h)[:Pr], om.bf16_to_f64(h_ref[:Pr]), BF16_TOL, "bf16 h by segment")
+    assert_close(f64(y)[:Pr], y_ref[:Pr], BF16_TOL, "bf16 y by segment")
+    assert (bits(h)[Pr:] == 0).all() and (bits(y)[Pr:] == 0).all()
 
 
 # ============================================================================ end to end
