@@ -412,6 +412,9 @@ __global__ __launch_bounds__(StreamWaves<STAGE>::WAVES * 64, 1) void k_grouped_g
     const uint8_t* sa = smem + (kb % SNSTAGE) * SSTAGE;
     const uint8_t* sb = sa + SABYTES;
     const float* ss = reinterpret_cast<const float*>(sb + SBBYTES);
+    // fragment reads and MFMAs at raised wave priority: a wave whose operands are ready issues ahead of
+    // the waves in their scale promotions (back to normal priority before its own promotions)
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {  // 64-byte k slices: logical chunks 4 ks + 2 (l / 32) and +1
       const int c0 = 4 * ks + 2 * fh;
@@ -437,6 +440,7 @@ __global__ __launch_bounds__(StreamWaves<STAGE>::WAVES * 64, 1) void k_grouped_g
           else blk[mi][nb] = mfma_32x32x64_fp8(af[mi], bf[nb], blk[mi][nb]);
         }
     }
+    __builtin_amdgcn_s_setprio(0);
     // promote this scale block: acc += blk * (row scale * weight-block scale)
     const float ws0 = s_ws[ws_row0 * SMAXKB + kb], ws1 = s_ws[ws_row1 * SMAXKB + kb];
 #pragma unroll

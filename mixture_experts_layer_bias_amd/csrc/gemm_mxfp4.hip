@@ -206,6 +206,9 @@ __global__ __launch_bounds__(MxShape<STAGE>::WAVES * 64, STAGE == 0 ? 1 : 2) voi
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) blk[mi][nb][r] = 0.f;
+    // fragment reads and MFMAs at raised wave priority: a wave whose operands are ready issues ahead of
+    // the waves in their scale promotions (back to normal priority before its own promotions)
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 64) {
       i32x8 af[MI], bfr[NB];
@@ -236,6 +239,7 @@ __global__ __launch_bounds__(MxShape<STAGE>::WAVES * 64, STAGE == 0 ? 1 : 2) voi
         for (int nb = 0; nb < NB; ++nb) blk[mi][nb] = mfma_e4m3_x_e2m1(af[mi], bfr[nb], bsc[nb], blk[mi][nb]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     // promote this K step: acc += blk * (activation row scale); the weight scales are inside blk
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
