@@ -212,11 +212,18 @@ moe_status_t moe_forward(const moe_config_t* cfg, const moe_weights_t* w, const 
  * and moe_unpermute_reduce_indexed; forward.rs page, apply_zero_expert.
  * x [N, H] bf16; topk_ids, topk_w [N, K]; offsets [R + 1], sorted_ids [P],
  * inv_perm [P] as moe_permute writes them; out [N, H] bf16.
- * ws: at least moe_workspace_size(cfg) bytes.  With bf16 weights and a few rows
- * per touched expert (decode) the routed GEMMs and the reduce run as one launch
- * whose tiles wait on counters in the workspace's `sync` piece: that piece must
- * hold zeros when the call starts.  Zero it once (e.g. zero the whole
- * workspace after allocating it); every call of this library leaves it zero. */
+ * ws: at least moe_workspace_size(cfg) bytes.  With bf16 weights, H <= 65536 and
+ * a few rows per touched expert (decode) the routed GEMMs and the reduce run as
+ * one launch whose tiles wait on counters in the workspace's `sync` piece.  That
+ * piece is the first 6152 bytes of every workspace, whatever the sizes, and its
+ * counters must hold zeros when the call starts: zero them once (e.g. zero the
+ * whole workspace after allocating it); every call of this library leaves them
+ * zero, so the workspace can then serve any batch size and layer shape.
+ * The int32 at byte offset `sync_error` (moe_workspace_layout) is set to 1 if a
+ * tile's bounded wait for another tile ever expires (an error of this library,
+ * not of the input); the output of that call is then undefined.  No launch
+ * clears the word: moe_forward clears it when it starts, and otherwise the
+ * caller does.  Calls that overlap on one workspace race. */
 moe_status_t moe_experts_forward(const moe_config_t* cfg, const moe_weights_t* w, const void* x,
                                  const int32_t* topk_ids, const float* topk_w, const int32_t* offsets,
                                  const int32_t* sorted_ids, const int32_t* inv_perm, void* out, void* ws,
@@ -224,11 +231,12 @@ moe_status_t moe_experts_forward(const moe_config_t* cfg, const moe_weights_t* w
 
 /* Offsets of the intermediates inside the moe_forward workspace, so a caller
  * can inspect them after moe_forward (all in bytes from the workspace start;
- * a piece that the config does not use has offset SIZE_MAX).  `sync` holds the
- * counters of the one-launch decode experts path (see moe_experts_forward). */
+ * a piece that the config does not use has offset SIZE_MAX).  `sync` (always 0)
+ * holds the counters of the one-launch decode experts path and `sync_error` its
+ * error word (see moe_experts_forward). */
 typedef struct {
   size_t logits, topk_ids, topk_w, zero_w, counts, offsets, sorted_ids, inv_perm;
-  size_t xq, x_scales, h, h_scales, y, shared_h, shared_h_scales, shared_y, scratch, sync, total;
+  size_t xq, x_scales, h, h_scales, y, shared_h, shared_h_scales, shared_y, scratch, sync, sync_error, total;
 } moe_workspace_layout_t;
 moe_status_t moe_workspace_layout(const moe_config_t* cfg, moe_workspace_layout_t* layout);
 

@@ -55,7 +55,7 @@ class moe_weights_t(ctypes.Structure):
 class moe_workspace_layout_t(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "logits", "topk_ids", "topk_w", "zero_w", "counts", "offsets", "sorted_ids", "inv_perm", "xq", "x_scales",
-        "h", "h_scales", "y", "shared_h", "shared_h_scales", "shared_y", "scratch", "sync", "total")]
+        "h", "h_scales", "y", "shared_h", "shared_h_scales", "shared_y", "scratch", "sync", "sync_error", "total")]
 
 
 _lib = None

@@ -119,6 +119,10 @@ void compute_layout(const moe_config_t* c, moe_workspace_layout_t* L) {
     off = align256(off + bytes);
     return at;
   };
+  // first, at a place and size independent of the layer's sizes: the one-launch decode path's
+  // counters stay where the previous call left them (zero) whatever the batch size
+  L->sync = take((size_t)moe::kSyncInts * 4);
+  L->sync_error = L->sync + (size_t)moe::kSyncError * 4;
   L->logits = take(N * R * 4);
   L->topk_ids = take(P * 4);
   L->topk_w = take(P * 4);
@@ -131,7 +135,6 @@ void compute_layout(const moe_config_t* c, moe_workspace_layout_t* L) {
   const size_t hist_bytes = ((size_t)moe::permute_chunks((int)P) + 1) * R * 4;  // chunk histograms + bucket totals
   const size_t part_bytes = slices > 1 ? (size_t)slices * N * R * 4 : 0;
   L->scratch = take(hist_bytes > part_bytes ? hist_bytes : part_bytes);
-  L->sync = take((size_t)moe::decode_fused_counters(c->num_experts, (int)H) * 4);
   L->xq = fp8 ? take(N * H) : none;
   L->x_scales = fp8 ? take(N * (H / 128) * 4) : none;
   L->h = take(P * I * (fp8 ? 1 : 2));
@@ -220,6 +223,7 @@ moe_status_t run_gemm(const moe_config_t* c, const moe::GroupedGemmArgs& g, hipS
 // Whether the decode experts path (routed gate/up, down and the reduce in one launch) applies.
 bool experts_fused(const moe_config_t* c) {
   if (c->weight_dtype != MOE_WEIGHTS_BF16 || c->row_invariant) return false;
+  if (!moe::decode_fused_fits(c->num_experts, c->hidden)) return false;
   const moe_weights_t none{};  // the fit is a function of the sizes only
   const moe::GroupedGemmArgs gu = gemm_args(c, MOE_STAGE_GATE_UP, MOE_GROUP_ROUTED, &none, nullptr, nullptr,
                                             nullptr, nullptr, nullptr, nullptr);
@@ -489,7 +493,7 @@ moe_status_t moe_forward(const moe_config_t* cfg, const moe_weights_t* w, const 
   const int P = c.num_tokens * c.top_k;
   int32_t* sync = static_cast<int32_t*>(at(L.sync));
   // small batch: router GEMM, then top-K and the sort in one block, which also zeroes the counters
-  // of the one-launch decode experts path
+  // and the error word of the one-launch decode experts path
   const bool small = moe::topk_sort_small_fits(c.num_tokens, c.top_k);
   const bool fused = small && experts_fused(cfg);
   if (small) {
@@ -499,8 +503,7 @@ moe_status_t moe_forward(const moe_config_t* cfg, const moe_weights_t* w, const 
     MOE_HIP(moe::launch_router_logits(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w->router_w),
                                       part, c.num_tokens, c.hidden, c.router_width, slices, inv, s));
     MOE_HIP(moe::launch_topk_sort_small(part, slices, logits, w->correction_bias, ids, tw, zw, counts, offsets,
-                                        sorted_ids, inv_perm, fused ? sync : nullptr,
-                                        moe::decode_fused_counters(c.num_experts, c.hidden), c.num_tokens,
+                                        sorted_ids, inv_perm, fused ? sync : nullptr, moe::kSyncInts, c.num_tokens,
                                         c.router_width, c.num_experts, c.top_k, c.scoring, c.renormalize,
                                         c.routed_scale, s));
   } else {

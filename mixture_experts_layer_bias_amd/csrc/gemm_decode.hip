@@ -76,8 +76,14 @@ __device__ __forceinline__ float silu_d(float g) { return g / (1.0f + __expf(-g)
 
 // Bounded wait of a down tile for its expert's gate/up tiles (the fused launch).  The bound only
 // guarantees that every wave exits; gate/up tiles never wait, and all of them are dispatched
-// before the first down tile, so the count is reached long before it.
+// before the first down tile, so the count is reached long before it.  Should the bound ever be
+// reached, the tile sets the error word sync[kSyncError] (which the launch never clears) and
+// carries on, so that every counter still completes and is reset; that launch's output is then
+// undefined and the word says so.
 constexpr int kDoneSpinLimit = 1 << 22;
+static_assert(kSyncExperts + kMaxGroups <= kSyncColTiles && kSyncColTiles + kSyncMaxColTiles <= kSyncReduced &&
+                  kSyncReduced < kSyncError && kSyncError < kSyncInts,
+              "the counters' pieces do not overlap");
 
 // 16 bytes of y (8 bf16) at device scope: y is written in the same launch by down tiles that may
 // run on other XCDs, whose L2s are not coherent with this one's
@@ -142,8 +148,9 @@ __device__ void reduce_columns(const ReduceArgs& r, const uint16_t* y, int c0, i
 }
 
 // One tile of a decode-shaped grouped GEMM.  `block` is the tile slot (blockIdx.x of a plain
-// launch).  FUSED (gate/up, down and the reduce in one launch; `done` holds E per-expert counts,
-// one count per down column tile and one count of reduced column tiles, all zero at the start):
+// launch).  FUSED (gate/up, down and the reduce in one launch; `done` is the kSyncInts counters:
+// per-expert counts at kSyncExperts, one count per down column tile at kSyncColTiles and the count
+// of reduced column tiles at kSyncReduced, all zero at the start):
 //   - a gate/up tile writes h with device-scope stores, waits until they are complete, then adds
 //     one to its expert's count;
 //   - a down tile waits until its expert's gate/up tiles are all counted, loads h at device scope,
@@ -278,10 +285,13 @@ __device__ __forceinline__ void decode_tile(const GroupedGemmArgs& g, uint8_t* s
     if (threadIdx.x == 0) {
       const int count = g.offsets[tc.expert + 1] - g.offsets[tc.expert];
       const int need = gu_tiles_per_row_tile * ((count + DecodeShape<0>::BM - 1) / DecodeShape<0>::BM);
-      for (int it = 0; it < kDoneSpinLimit; ++it) {
-        if (__hip_atomic_load(done + tc.expert, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need) break;
-        __builtin_amdgcn_s_sleep(2);
+      bool ready = false;
+      for (int it = 0; it < kDoneSpinLimit && !ready; ++it) {
+        ready = __hip_atomic_load(done + kSyncExperts + tc.expert, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
+                need;
+        if (!ready) __builtin_amdgcn_s_sleep(2);
       }
+      if (!ready) __hip_atomic_store(done + kSyncError, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
@@ -377,7 +387,8 @@ __device__ __forceinline__ void decode_tile(const GroupedGemmArgs& g, uint8_t* s
     static_assert(STAGE != 0 || WK == 4, "the fused h stores are the partial-sum epilogue's");
     dma_wait<0>();     // this wave's device-scope h stores are complete
     __syncthreads();   // ... and every other wave's
-    if (threadIdx.x == 0) __hip_atomic_fetch_add(done + tc.expert, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0)
+      __hip_atomic_fetch_add(done + kSyncExperts + tc.expert, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   if (STAGE == 1 && FUSED) {
     static_assert(STAGE != 1 || WK == 1, "the fused y stores are the whole-sum epilogue's");
@@ -385,20 +396,26 @@ __device__ __forceinline__ void decode_tile(const GroupedGemmArgs& g, uint8_t* s
     __syncthreads();   // ... and every other wave's; the ring is free
     int* s_last = reinterpret_cast<int*>(smem);
     if (threadIdx.x == 0) {
-      const int before = __hip_atomic_fetch_add(done + g.E + tc.n_tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int before =
+          __hip_atomic_fetch_add(done + kSyncColTiles + tc.n_tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       *s_last = before == tc.m_tiles - 1;
     }
     __syncthreads();
     if (*s_last) {
       reduce_columns(*ra, out, n0, BNB, reinterpret_cast<float*>(smem) + 16);
       if (threadIdx.x == 0) {
-        const int before = __hip_atomic_fetch_add(done + g.E + NT, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int before =
+            __hip_atomic_fetch_add(done + kSyncReduced, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last[1] = before == NT - 1;
       }
       __syncthreads();
-      if (s_last[1])
-        for (int i = threadIdx.x; i <= g.E + NT; i += 256)
-          __hip_atomic_store(done + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (s_last[1]) {  // every other tile has counted itself: clear what this launch used
+        for (int i = threadIdx.x; i < g.E; i += 256)
+          __hip_atomic_store(done + kSyncExperts + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int i = threadIdx.x; i < NT; i += 256)
+          __hip_atomic_store(done + kSyncColTiles + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (threadIdx.x == 0) __hip_atomic_store(done + kSyncReduced, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
   }
 }
@@ -433,7 +450,9 @@ hipError_t launch_decode(const GroupedGemmArgs& g, int groups, int rows, int nt,
 
 }  // namespace
 
-int decode_fused_counters(int E, int H) { return E + H / DecodeShape<1>::BNB + 1; }
+bool decode_fused_fits(int E, int H) {
+  return E <= kMaxGroups && H % DecodeShape<1>::BNB == 0 && H / DecodeShape<1>::BNB <= kSyncMaxColTiles;
+}
 
 hipError_t launch_decode_fused(const GroupedGemmArgs& gu, const GroupedGemmArgs& dn, const ReduceArgs& r,
                                int32_t* done, hipStream_t s) {

@@ -24,7 +24,8 @@ hipError_t launch_topk(const float* part, int slices, float* logits, const float
 
 // a2 + a3 for small batches (N <= 64, N*K <= 1024): top-K and the stable sort in one block
 bool topk_sort_small_fits(int N, int K);
-// `done` ([done_len] int32, may be null) is zeroed for a following fused decode launch
+// `done` ([done_len] int32, may be null) is zeroed for a following one-launch decode (its counters and
+// its error word)
 hipError_t launch_topk_sort_small(const float* part, int slices, float* logits, const float* bias, int32_t* ids,
                                   float* w, float* zero_w, int32_t* counts, int32_t* offsets, int32_t* sorted_ids,
                                   int32_t* inv_perm, int32_t* done, int done_len, int N, int R, int E, int K,
@@ -79,12 +80,21 @@ struct ReduceArgs {
   uint16_t* out;             // [N, H]
   int N, H, K, E;
 };
+// The counters of the one-launch decode path: kSyncInts int32 at a fixed place (the start of the
+// workspace), whose indices do not depend on the layer's sizes, so that a workspace reused for
+// another batch size finds them where the last call left them.
+constexpr int kSyncExperts = 0;         // [1024]: gate/up tiles finished, per expert
+constexpr int kSyncColTiles = 1024;     // [kSyncMaxColTiles]: down tiles finished, per 128-column block
+constexpr int kSyncMaxColTiles = 512;   // so the path takes H <= 65536
+constexpr int kSyncReduced = 1536;      // column blocks reduced
+constexpr int kSyncError = 1537;        // set to 1 when a bounded wait expires; the launch never clears it
+constexpr int kSyncInts = 1538;
 // Routed gate/up, down and the unpermute-reduce of a decode layer in one launch (the shared expert,
-// if any, must already be in r.shared_y).  done: decode_fused_counters(E, H) int32 that hold zeros when
-// the launch starts; the launch leaves them zero.
-int decode_fused_counters(int E, int H);
+// if any, must already be in r.shared_y).  sync: kSyncInts int32 whose counters hold zeros when the
+// launch starts; the launch leaves them zero (and sets sync[kSyncError] if a wait expired).
+bool decode_fused_fits(int E, int H);
 hipError_t launch_decode_fused(const GroupedGemmArgs& gu, const GroupedGemmArgs& dn, const ReduceArgs& r,
-                               int32_t* done, hipStream_t s);
+                               int32_t* sync, hipStream_t s);
 
 hipError_t launch_grouped_gemm_fp8(const GroupedGemmArgs& g, hipStream_t s);
 // MXFP4 weights (packed E2M1 [rows, K/2], E8M0 scales [rows, K/32] in the s_* / sh_*_s pointers)

@@ -48,7 +48,7 @@ def f32_to_bf16(v: np.ndarray) -> np.ndarray:
 
 # ----------------------------------------------------------------------------- E4M3
 
-def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+def _e4m3_from_bits(codes: np.ndarray) -> np.ndarray:
     """E4M3 codes (uint8) -> float64, from the bit-field definition."""
     c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
     sign = np.where(c & 0x80, -1.0, 1.0)
@@ -58,6 +58,16 @@ def e4m3_decode(codes: np.ndarray) -> np.ndarray:
     nor = (1.0 + man / 8.0) * np.ldexp(1.0, (exp - 7).astype(np.int64))
     val = sign * np.where(exp == 0, sub, nor)
     return np.where((c & 0x7F) == 0x7F, np.nan, val)
+
+
+# the value of every one of the 256 codes, from the bit-field definition above
+_E4M3_TABLE = _e4m3_from_bits(np.arange(256, dtype=np.uint8))
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """E4M3 codes (uint8) -> float64: the bit-field definition's value of each code
+    (looked up in the table of all 256 codes, so large weight matrices decode quickly)."""
+    return _E4M3_TABLE[np.asarray(codes, dtype=np.uint8)]
 
 
 _POS_CODES = np.arange(0x7F, dtype=np.uint8)  # 0x00..0x7E: every non-negative finite code
@@ -87,7 +97,7 @@ def e4m3_encode(v: np.ndarray) -> np.ndarray:
 
 # ----------------------------------------------------------------------------- MXFP4
 
-def e2m1_decode(codes: np.ndarray) -> np.ndarray:
+def _e2m1_from_bits(codes: np.ndarray) -> np.ndarray:
     """FP4 E2M1 codes (low 4 bits) -> float64, from the bit-field definition of the OCP
     Microscaling Formats (MX) v1.0 spec: sign bit, 2 exponent bits with bias 1, 1
     mantissa bit, exponent field 0 is subnormal (0 or 0.5); no infinities or NaN."""
@@ -97,6 +107,15 @@ def e2m1_decode(codes: np.ndarray) -> np.ndarray:
     man = c & 0x1
     val = np.where(exp == 0, man * 0.5, (1.0 + man / 2.0) * np.ldexp(1.0, (exp - 1).astype(np.int64)))
     return sign * val
+
+
+_E2M1_TABLE = _e2m1_from_bits(np.arange(16, dtype=np.uint8))  # the 16 codes, from the definition above
+
+
+def e2m1_decode(codes: np.ndarray) -> np.ndarray:
+    """FP4 E2M1 codes (low 4 bits) -> float64: the bit-field definition's value of each code
+    (looked up in the table of all 16 codes)."""
+    return _E2M1_TABLE[np.asarray(codes, dtype=np.uint8) & np.uint8(0xF)]
 
 
 def e8m0_decode(codes: np.ndarray) -> np.ndarray:

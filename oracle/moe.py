@@ -294,7 +294,8 @@ def shared_gate(x_bits: np.ndarray, gate_bits: Optional[np.ndarray]) -> np.ndarr
 
 def moe_forward(cfg: MoeConfig, x_bits: np.ndarray, router_bits: np.ndarray, bias: Optional[np.ndarray],
                 expert: ExpertFn, shared: Optional[tuple], tokens: Optional[np.ndarray] = None,
-                shared_gate_bits: Optional[np.ndarray] = None) -> OracleResult:
+                shared_gate_bits: Optional[np.ndarray] = None,
+                forced_ids: Optional[np.ndarray] = None) -> OracleResult:
     """out[t] = bf16( sum_{k: id<E} w[t,k] * y_{t,k} + zero_accum[t] * x[t] + g[t] * shared[t] ),
     with g[t] = sigmoid(x[t] . shared_expert_gate), or 1 without that gate.
 
@@ -310,6 +311,12 @@ def moe_forward(cfg: MoeConfig, x_bits: np.ndarray, router_bits: np.ndarray, bia
     blend (sigmoid-gated, or weight 1); then the zero-computation experts' term of
     ``MoeLayer::apply_zero_expert`` (forward.rs page).  Reading: the three
     terms are summed in float64 and rounded to bf16 once.
+
+    ``forced_ids`` ([n, K], optional) replaces the selected expert ids, for rows
+    whose K-th and (K+1)-th selection scores are a near-tie, where a selection in
+    lower precision may pick the other expert; the weights are still the unbiased
+    scores of those ids, renormalised and scaled as usual (``gap`` stays the
+    float64 selection's).
     """
     n = x_bits.shape[0]
     tokens = np.arange(n) if tokens is None else np.asarray(tokens)
@@ -317,6 +324,8 @@ def moe_forward(cfg: MoeConfig, x_bits: np.ndarray, router_bits: np.ndarray, bia
     logits = router_logits(x_bits, router_bits)
     p = scores(logits, cfg.scoring)
     ids, gap = select_topk(p, bias, K)
+    if forced_ids is not None:
+        ids = np.asarray(forced_ids, dtype=np.int32).reshape(n, K)
     w, zero_accum = routing_weights(p, ids, cfg.renormalize, cfg.routed_scale, E)
 
     x64 = bf16_to_f64(x_bits)

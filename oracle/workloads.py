@@ -21,8 +21,10 @@ def config_of(wl: mi.Workload) -> MoeConfig:
 
 
 def run(wl: mi.Workload, tokens: Optional[np.ndarray] = None, layer: int = 0,
-        inputs: Optional[mi.HostInputs] = None, expert_cache: Optional[dict] = None) -> OracleResult:
-    """The oracle on workload ``wl`` (all tokens, or the rows ``tokens``)."""
+        inputs: Optional[mi.HostInputs] = None, expert_cache: Optional[dict] = None,
+        forced_ids: Optional[np.ndarray] = None) -> OracleResult:
+    """The oracle on workload ``wl`` (all tokens, or the rows ``tokens``), optionally with the
+    expert ids of each row given (``forced_ids``, see ``moe_forward``)."""
     inp = inputs if inputs is not None else mi.host_inputs(wl, layer) if tokens is None else None
     if tokens is None:
         x = inp.x
@@ -39,7 +41,7 @@ def run(wl: mi.Workload, tokens: Optional[np.ndarray] = None, layer: int = 0,
         return expert_cache[e]
 
     return moe_forward(config_of(wl), x, router, bias, expert, mi.host_shared(wl, layer), tokens=tokens,
-                       shared_gate_bits=mi.host_shared_gate(wl, layer))
+                       shared_gate_bits=mi.host_shared_gate(wl, layer), forced_ids=forced_ids)
 
 
 @functools.lru_cache(maxsize=8)

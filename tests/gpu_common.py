@@ -64,3 +64,11 @@ def check_routing(gpu_ids: np.ndarray, res, K: int):
     bad = ~same & ~near
     assert not bad.any(), f"ids differ on {bad.sum()} rows that are not near-ties: {np.nonzero(bad)[0][:8]}"
     return same
+
+
+def assert_sync_clear(ws, L: dict, what: str):
+    """The one-launch decode path's counters (the workspace's first bytes, up to its error word) are
+    back at zero, and the error word (set if a tile's bounded wait ever expired) is zero."""
+    words = ws[L["sync"]:L["sync_error"] + 4].view(torch.int32)
+    assert int(words[-1]) == 0, f"{what}: the decode path's error word is set (a bounded wait expired)"
+    assert int(words[:-1].abs().sum()) == 0, f"{what}: decode counters not back at zero"

@@ -83,9 +83,15 @@ def test_workspace_size_and_layout():
     n = moe.moe_workspace_size(c)
     L = moe.moe_workspace_layout(c)
     assert L["total"] == n
-    offs = [v for k, v in L.items() if k != "total" and v != 2**64 - 1]
+    offs = [v for k, v in L.items() if k not in ("total", "sync_error") and v != 2**64 - 1]
     assert all(o % 256 == 0 for o in offs) and max(offs) < n
     assert L["xq"] == 2**64 - 1  # bf16 experts: no fp8 staging
+    # the decode path's counters sit at the start of every workspace, whatever the sizes; the
+    # error word lies inside them
+    for m in (c, moe.config_with_tokens(c, 1), moe.config_with_tokens(c, 4000), _cfg(row_invariant=True)):
+        Lm = moe.moe_workspace_layout(m)
+        assert Lm["sync"] == 0 and 0 < Lm["sync_error"] < Lm["logits"] and Lm["sync_error"] % 4 == 0
+    assert L["sync_error"] == moe.moe_workspace_layout(moe.config_with_tokens(c, 4000))["sync_error"]
     c.weight_dtype = moe.MOE_WEIGHTS_FP8_E4M3
     assert moe.moe_workspace_layout(c)["xq"] != 2**64 - 1
     assert moe.moe_workspace_size(moe.config_with_tokens(c, 0)) >= 0
