@@ -229,6 +229,24 @@ moe_status_t moe_experts_forward(const moe_config_t* cfg, const moe_weights_t* w
                                  const int32_t* sorted_ids, const int32_t* inv_perm, void* out, void* ws,
                                  size_t ws_bytes, void* stream);
 
+/* moe_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same computation and result, with the workspace taken from a static array of
+ * MOE_NOALLOC_WORKSPACE_BYTES inside the library instead of from the caller.
+ * Each GPU the library runs on holds its own copy of that array from the
+ * library's load until the process ends; the call uses the copy of the current
+ * device (`stream` must belong to it).  Nothing is allocated or freed.
+ * A layer whose moe_workspace_size exceeds MOE_NOALLOC_WORKSPACE_BYTES is
+ * refused with MOE_ERR_WORKSPACE before anything is launched (32 MiB serves,
+ * e.g., decode batches up to a few hundred tokens at H 2048, 128 experts, top-8).
+ * Every call on one GPU shares that GPU's array and leaves its contents there
+ * (the next call accepts any contents): calls that overlap on one GPU, from
+ * several streams or threads, race and give undefined results.
+ * x [N, H] bf16 -> out [N, H] bf16. */
+#define MOE_NOALLOC_WORKSPACE_BYTES (32u << 20)
+moe_status_t moe_forward_noalloc(const moe_config_t* cfg, const moe_weights_t* w, const void* x, void* out,
+                                 void* stream);
+
 /* Offsets of the intermediates inside the moe_forward workspace, so a caller
  * can inspect them after moe_forward (all in bytes from the workspace start;
  * a piece that the config does not use has offset SIZE_MAX).  `sync` (always 0)

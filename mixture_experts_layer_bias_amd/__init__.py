@@ -28,8 +28,9 @@ MOE_STAGE_GATE_UP, MOE_STAGE_DOWN = 0, 1
 MOE_GROUP_ROUTED, MOE_GROUP_SHARED = 0, 1
 
 EXPORTED = ["moe_workspace_size", "moe_workspace_layout", "moe_route_topk", "moe_permute", "moe_quantize_fp8",
-            "moe_grouped_gemm", "moe_unpermute_reduce", "moe_forward", "moe_experts_forward", "moe_status_str",
-            "moe_last_error"]
+            "moe_grouped_gemm", "moe_unpermute_reduce", "moe_forward", "moe_experts_forward", "moe_forward_noalloc",
+            "moe_status_str", "moe_last_error"]
+MOE_NOALLOC_WORKSPACE_BYTES = 32 << 20  # the static workspace of moe_forward_noalloc
 
 
 class MoeError(RuntimeError):
@@ -80,6 +81,7 @@ def lib() -> ctypes.CDLL:
             "moe_unpermute_reduce": [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
             "moe_forward": [cfgp, ctypes.POINTER(moe_weights_t), vp, vp, vp, sz, vp],
             "moe_experts_forward": [cfgp, ctypes.POINTER(moe_weights_t), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+            "moe_forward_noalloc": [cfgp, ctypes.POINTER(moe_weights_t), vp, vp, vp],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -245,6 +247,11 @@ def moe_unpermute_reduce(cfg, y_sorted, inv_perm, topk_ids, topk_w, x, shared_y,
 def moe_forward(cfg, weights: LayerWeights, x, out, ws, stream=None) -> None:
     _check(lib().moe_forward(ctypes.byref(cfg), ctypes.byref(weights.struct), _ptr(x, "x", 2), _ptr(out, "out", 2),
                              _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_forward_noalloc(cfg, weights: LayerWeights, x, out, stream=None) -> None:
+    _check(lib().moe_forward_noalloc(ctypes.byref(cfg), ctypes.byref(weights.struct), _ptr(x, "x", 2),
+                                     _ptr(out, "out", 2), _stream(stream)))
 
 
 def moe_experts_forward(cfg, weights: LayerWeights, x, topk_ids, topk_w, offsets, sorted_ids, inv_perm, out, ws,

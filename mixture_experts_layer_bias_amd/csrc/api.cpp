@@ -283,6 +283,35 @@ moe_status_t run_experts(const moe_config_t* cfg, const moe_weights_t* w, const 
   return ok();
 }
 
+// ---- the workspace of moe_forward_noalloc: one array in the library's code object, so each GPU the
+// library runs on holds its own copy from load until the process ends.  In host code `scratch` names
+// a host-side stand-in, never the device memory: kernels get the address that hipGetSymbolAddress
+// returns for the current device.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_WORKSPACE_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, looked up once
+
+// The address of `scratch` on the current device (looked up at the first call on that device, with it
+// current).
+moe_status_t scratch_on_current_device(void** ptr) {
+  int dev = 0;
+  MOE_HIP(hipGetDevice(&dev));
+  MOE_CHECK(dev >= 0 && dev < kMaxDevices, MOE_ERR_UNSUPPORTED, "device %d: only devices 0..%d are supported", dev,
+            kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    MOE_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    MOE_CHECK(p != nullptr && aligned(p, 256), MOE_ERR_HIP, "static workspace of device %d has no usable address",
+              dev);
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 moe_status_t launch_route(const moe_config_t* c, const void* x, const void* router_w, const float* bias,
                           float* logits, int32_t* ids, float* tw, float* zw, float* scratch, hipStream_t s) {
   const bool inv = c->row_invariant != 0;
@@ -535,6 +564,21 @@ moe_status_t moe_experts_forward(const moe_config_t* cfg, const moe_weights_t* w
   MOE_RET(check_ptr(ws, 256, "ws"));
   return run_experts(cfg, w, x, topk_ids, topk_w, offsets, sorted_ids, inv_perm, out, L, static_cast<char*>(ws),
                      experts_fused(cfg), static_cast<hipStream_t>(stream));
+}
+
+moe_status_t moe_forward_noalloc(const moe_config_t* cfg, const moe_weights_t* w, const void* x, void* out,
+                                 void* stream) {
+  MOE_RET(check_config(cfg));
+  moe_workspace_layout_t L;
+  compute_layout(cfg, &L);
+  MOE_CHECK(L.total <= (size_t)MOE_NOALLOC_WORKSPACE_BYTES, MOE_ERR_WORKSPACE,
+            "moe_forward_noalloc: this layer needs %zu bytes of workspace, more than the static %zu bytes; "
+            "call moe_forward with a workspace of its own",
+            L.total, (size_t)MOE_NOALLOC_WORKSPACE_BYTES);
+  if (cfg->num_tokens == 0) return ok();
+  void* ws = nullptr;
+  MOE_RET(scratch_on_current_device(&ws));
+  return moe_forward(cfg, w, x, out, ws, (size_t)MOE_NOALLOC_WORKSPACE_BYTES, stream);
 }
 
 }  // extern "C"

@@ -165,3 +165,16 @@ def test_last_error_is_cleared_by_success():
     assert lib.moe_last_error() != b""
     moe.moe_workspace_size(_cfg())
     assert lib.moe_last_error() == b""
+
+
+def test_noalloc_refuses_a_layer_beyond_its_static_workspace_before_any_launch():
+    """moe_forward_noalloc checks the layer's workspace against its static array before touching the
+    GPU (the pointers here are never dereferenced)."""
+    lib = moe.lib()
+    c = _cfg(num_tokens=4096, hidden=2048, num_experts=128, router_width=128, top_k=8, inter=768, shared_inter=0)
+    assert moe.moe_workspace_size(c) > moe.MOE_NOALLOC_WORKSPACE_BYTES
+    w = moe.moe_weights_t()
+    st = lib.moe_forward_noalloc(ctypes.byref(c), ctypes.byref(w), _fake(), _fake(), None)
+    assert st == moe.MOE_ERR_WORKSPACE
+    msg = lib.moe_last_error().decode()
+    assert "static" in msg and str(moe.MOE_NOALLOC_WORKSPACE_BYTES) in msg
