@@ -1,22 +1,32 @@
-"""Benchmark of the MoE layer forward on one MI355X.
+"""Benchmark of the MoE layer forward on one MI355X, over the five workloads.
 
 A step is one whole layer forward (router GEMM, scoring + top-K, sort by
 expert, grouped gate/up + SwiGLU, grouped down, unpermute-reduce and blends)
 over one batch of seeded synthetic tokens, with every input resident in HBM.
-Prints one JSON line.  The default workload is the decode layer (4 tokens,
-H 2048, 128 experts, top-8, I 768); --workload picks another.
+Every workload is timed in the same run:
 
-The dominant kernel is timed with HIP events recorded on the stream the
-library launches on, over the same kind of steps, and reported against the
-binding roofline: for a decode batch with bf16 weights and no shared expert,
-the one launch that runs the routed gate/up GEMM, the down GEMM and the
-unpermute-reduce (through moe_experts_forward); otherwise the routed gate/up
-grouped GEMM.  The oracle (float64 numpy on the
-host cores) is timed on a bounded sample of the same workload.
+  tiny          16 tokens, H 256, 8 experts, top-2, I 128, shared expert 256
+  decode        4 tokens, H 2048, 128 experts, top-8, I 768
+  prefill_zipf  4096 tokens of the decode layer, Zipf(1.1)-skewed expert loads
+  fp8_sigmoid   2048 tokens, H 7168, 256 fp8 experts, top-8, I 2048, shared 2048,
+                sigmoid + correction bias, weights x 2.5
+  zero_experts  512 tokens, H 6144, 256 experts + 128 identity experts, top-12, I 2048
+
+One JSON line is printed.  Its headline (`value`, `ms_per_step`, `config`,
+`roofline`, `cpu_baseline`) is the prefill layer's tokens/s; `decode_us_per_layer`
+names the decode layer's time; `workloads` holds every workload's entry (layer
+time, tokens/s, the dominant kernels against their rooflines, the oracle beside
+it).  The kernels are timed with HIP events recorded on the stream the library
+launches on: for a decode-sized batch the expert half of the layer
+(moe_experts_forward: one launch for the routed gate/up, down and reduce),
+otherwise the routed gate/up and the routed down grouped GEMMs
+(moe_grouped_gemm), each on the layer's own routing.  The oracle (float64 numpy
+on the host cores) is timed on a bounded sample of each workload.
 """
 import argparse
 import json
 import os
+import platform
 import sys
 import time
 
@@ -25,30 +35,27 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "mxfp4": 5000.0}  # dense MFMA peaks (mxfp4: e4m3 x e2m1 MFMA)
+ORDER = ["tiny", "decode", "prefill_zipf", "fp8_sigmoid", "zero_experts"]
+HEADLINE = "prefill_zipf"
+# tokens of the oracle's bounded sample per workload: its cost is dominated by the touched experts
+CPU_SAMPLE_TOKENS = {"tiny": 16, "decode": 4, "prefill_zipf": 32, "fp8_sigmoid": 2, "zero_experts": 4,
+                     "mxfp4_sigmoid": 2}
 
-# HBM traffic of the dominant kernel per launch, from two rocprofv3 --pmc runs of this script
-# (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch averaged over the kernel's dispatches), each scaled by
-# what the same counter reads for a plain 1 GiB device copy (FETCH_SIZE reads half the bytes moved:
-# x2.0; WRITE_SIZE reads them all: x1.0).  An entry holds only while the kernel's sources hash to the
-# value they had when the counters were taken; otherwise the traffic is reported as null.
-MEASURED_TRAFFIC = {
-    "decode_4tok_h2048_e128_top8_i768": {
-        "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_decode.hip",
-                    "mixture_experts_layer_bias_amd/csrc/dma.h",
-                    "mixture_experts_layer_bias_amd/csrc/gemm_common.h",
-                    "mixture_experts_layer_bias_amd/csrc/unpermute.h",
-                    "mixture_experts_layer_bias_amd/csrc/common.h"],
-        "sha256": "74c10d1180400613c8c488d4182eaa59096788872960652ab2e8dcf822e7b8af",
-        "fetch_kib": 140121.41, "write_kib": 253.78, "fetch_scale": 2.0, "write_scale": 1.0,
-    },
-}
+# HBM traffic of a kernel per launch, from two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
+# WRITE_SIZE; KiB per dispatch averaged over the kernel's dispatches), each scaled by what the same
+# counter reads for a plain 1 GiB device copy (FETCH_SIZE reads half the bytes moved: x2.0; WRITE_SIZE
+# reads them all: x1.0).  An entry holds only while the kernel's sources hash to the value they had
+# when the counters were taken; otherwise the traffic is reported as null.
+_GEMM_SOURCES = ["mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h",
+                 "mixture_experts_layer_bias_amd/csrc/dma.h"]
+MEASURED_TRAFFIC = {}
 
 
-def measured_traffic(workload: str):
-    """Bytes per launch of the dominant kernel from the stored counter readings, or None."""
+def measured_traffic(workload: str, kernel: str):
+    """Bytes per launch of a kernel from the stored counter readings, or None."""
     import hashlib
 
-    rec = MEASURED_TRAFFIC.get(workload)
+    rec = MEASURED_TRAFFIC.get((workload, kernel))
     if rec is None:
         return None
     h = hashlib.sha256()
@@ -63,13 +70,15 @@ def measured_traffic(workload: str):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="decode", choices=["tiny", "decode", "prefill_zipf", "fp8_sigmoid",
-                                                              "zero_experts", "mxfp4_sigmoid"])
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workloads", default=",".join(ORDER),
+                    help="comma-separated workloads to time (tiny, decode, prefill_zipf, fp8_sigmoid, zero_experts, "
+                         "mxfp4_sigmoid); the headline is the prefill layer when it is among them")
+    ap.add_argument("--workload", default=None, help="time this one workload only (same as --workloads W)")
     ap.add_argument("--layers", type=int, default=0,
                     help="distinct weight copies cycled through (0: enough to exceed the 256 MB MALL)")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle leg")
+    ap.add_argument("--cpu-seconds", type=float, default=4.0, help="target CPU time of each workload's oracle leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only (no HIP graph replay)")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -78,18 +87,30 @@ def parse():
     return ap.parse_args()
 
 
+def host_info() -> dict:
+    model = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count()
+    return {"nproc": os.cpu_count(), "cpus_available": avail, "cpu_model": model}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); every box here has a single MI355X "
               f"and the multi-GPU expert-parallel path is design only.", file=sys.stderr)
         sys.exit(2)
-    import numpy as np
     import torch
-
-    import mixture_experts_layer_bias_amd as moe
-    import moe_inputs as mi
-    import moe_inputs.device as mid
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -101,18 +122,71 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": args.copy_bytes, "steps": args.steps}))
         return
-    wl = mi.WORKLOADS[args.workload]
+    names = [args.workload] if args.workload else [w for w in args.workloads.split(",") if w]
+    entries = {}
+    for name in names:
+        print(f"[bench] {name} ...", file=sys.stderr, flush=True)
+        entries[name] = measure(name, args)
+        torch.cuda.empty_cache()
+        print(f"[bench] {name}: {entries[name]['us_per_layer']:.1f} us/layer", file=sys.stderr, flush=True)
+    head = HEADLINE if HEADLINE in entries else names[0]
+    h = entries[head]
+    result = {
+        "metric": "MoE-layer tokens/sec (prefill) + decode µs/layer; % of MFMA / HBM peak",
+        "value": h["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": h["us_per_layer"] * 1e-3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": h["dtype"],
+        "data": "synthetic (seeded counter-based generator; random-init weights)",
+        "config": h["config"],
+        "headline": f"{head}: {h['tokens_per_s']:.4g} tokens/s ({h['us_per_layer']:.1f} us/layer)",
+        "decode_us_per_layer": entries["decode"]["us_per_layer"] if "decode" in entries else None,
+        "roofline": h["roofline"],
+        "host": host_info(),
+        "workloads": entries,
+    }
+    if "cpu_baseline" in h:
+        result["cpu_baseline"] = h["cpu_baseline"]
+    print(json.dumps(result))
+
+
+def one_launch_experts(wl) -> bool:
+    """Whether the workload is a decode-sized bf16 batch whose experts the library runs as one launch
+    (the routed gate/up, down and the reduce), i.e. what moe_experts_forward times as one kernel."""
+    P = wl.num_tokens * wl.top_k
+    return (wl.weight_dtype == "bf16" and wl.num_tokens <= 64 and P <= 1024 and P <= min(8 * wl.num_experts, 512)
+            and wl.hidden % 256 == 0 and wl.inter % 64 == 0)
+
+
+def measure(name: str, args) -> dict:
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_bias_amd as moe
+    import moe_inputs as mi
+    import moe_inputs.device as mid
+
+    dev = torch.device("cuda:0")
+    wl = mi.WORKLOADS[name]
     N, H, E, R, K, I, Is = (wl.num_tokens, wl.hidden, wl.num_experts, wl.router_width, wl.top_k, wl.inter,
                             wl.shared_inter)
     fp8 = wl.weight_dtype != "bf16"  # fp8 and mxfp4 experts take e4m3 activations
     abytes = 1 if fp8 else 2  # activation and h element bytes
     wbytes = {"bf16": 2, "fp8": 1, "mxfp4": 0.5 + 1 / 32}[wl.weight_dtype]  # mxfp4: codes + E8M0 per 32
+    sbytes = (4.0 / (128 * 128)) if wl.weight_dtype == "fp8" else 0.0  # fp8 block scales per weight element
     layer_bytes = 3 * E * I * H * wbytes
-    # enough distinct weight copies that the touched experts of consecutive steps cannot be
-    # served from the 256 MB Infinity Cache (at least ~8 GB of weights in rotation, at most 8 copies)
+    # enough distinct weight copies that the touched experts of consecutive steps cannot be served from
+    # the 256 MB Infinity Cache (at least ~8 GB of weights in rotation, at most 8 copies; two copies of
+    # the layers whose steps touch gigabytes each)
     n_layers = args.layers or max(2, min(8, int(np.ceil(8.0e9 / layer_bytes))))
-    if layer_bytes * n_layers > 150e9:
-        n_layers = max(1, int(150e9 // layer_bytes))
+    if layer_bytes * n_layers > 60e9:
+        n_layers = max(1, int(60e9 // layer_bytes))
 
     cfg = moe.make_config(N, H, E, R, K, I, Is, wl.scoring, wl.renormalize, wl.routed_scale, wl.weight_dtype)
     layers = []
@@ -120,7 +194,7 @@ def main():
         dl = mid.device_layer(wl, layer=l, device="cuda:0")
         w = moe.weights_from_stacked(dl.router, dl.bias, dl.gate, dl.up, dl.down, dl.gate_s, dl.up_s, dl.down_s,
                                      dl.sh_gate, dl.sh_up, dl.sh_down, dl.sh_gate_s, dl.sh_up_s, dl.sh_down_s,
-                                    sh_expert_gate=dl.sh_expert_gate)
+                                     sh_expert_gate=dl.sh_expert_gate)
         layers.append((dl, w))
     # zeroed once: the decode experts path keeps its counters in the workspace and leaves them zero
     ws = torch.zeros(moe.moe_workspace_size(cfg), dtype=torch.uint8, device=dev)
@@ -133,7 +207,7 @@ def main():
         dl, w = layers[i % n_layers]
         moe.moe_forward(cfg, w, dl.x, out, ws, stream)
 
-    # ---- whole-layer timing, eager launches
+    # ---- whole-layer timing, eager launches, between a barrier-free pair of device synchronisations
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -141,13 +215,12 @@ def main():
     for i in range(args.steps):
         step(i)
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_eager = (t1 - t0) * 1e3 / args.steps
+    ms_eager = (time.perf_counter() - t0) * 1e3 / args.steps
 
     # ---- the same steps replayed from HIP graphs (one captured moe_forward per weight copy), the way a
     # serving loop runs a decode layer: the launches are the library's own, only host overhead goes away
     ms_graph = None
-    if not args.no_graph:
+    if not args.no_graph and N <= 64:
         graphs = []
         cap = torch.cuda.Stream()
         cap.wait_stream(stream)
@@ -166,13 +239,13 @@ def main():
         for i in range(args.steps):
             graphs[i % n_layers].replay()
         torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        ms_graph = (t1 - t0) * 1e3 / args.steps
+        ms_graph = (time.perf_counter() - t0) * 1e3 / args.steps
+        del graphs
     # the faster of the two launch modes is reported (named in "timing"); both run the same kernels
     use_graph = ms_graph is not None and ms_graph < ms_eager
     ms = ms_graph if use_graph else ms_eager
 
-    # ---- realised routing per layer (for the algorithmic bytes / flops)
+    # ---- realised routing per weight copy (for the algorithmic bytes / flops)
     touched, rows_real = [], []
     for l in range(n_layers):
         step(l)
@@ -183,120 +256,128 @@ def main():
     e_t = float(np.mean(touched))
     p_r = float(np.mean(rows_real))
 
-    # ---- dominant kernel, timed with events on the launch stream.  The calls below reuse
-    # moe_forward's own routing and intermediates in the workspace (refreshed before every launch).
-    # A decode batch (bf16 weights, a few rows per touched expert, no shared expert) runs its experts
-    # as one launch: routed gate/up + SwiGLU, down and the unpermute-reduce.  Otherwise the routed
-    # gate/up grouped GEMM dominates.
-    P = N * K
-    one_launch = not fp8 and Is == 0 and P <= min(8 * E, 512) and H % 128 == 0 and I % 64 == 0
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    a_off = L["xq"] if fp8 else None
+    # ---- the dominant kernels, timed with events on the launch stream over the same kind of steps.
+    # The calls reuse moe_forward's own routing and intermediates in the workspace, refreshed by a
+    # moe_forward (outside the events) before every timed launch.
     base = ws.data_ptr()
-    for i in range(args.warmup + args.steps):
-        dl, w = layers[i % n_layers]
-        moe.moe_forward(cfg, w, dl.x, out, ws, stream)  # refreshes ids / offsets / quantised x for this batch
-        if i >= args.warmup:
-            ev[i - args.warmup][0].record(stream)
-        if one_launch:
+    one = one_launch_experts(wl)
+    if one:
+        kinds = ["experts"]
+    else:
+        kinds = ["gate_up", "down"]
+
+    def launch(kind, w, dl):
+        if kind == "experts":
             moe.moe_experts_forward(cfg, w, dl.x, base + L["topk_ids"], base + L["topk_w"], base + L["offsets"],
                                     base + L["sorted_ids"], base + L["inv_perm"], out, ws, stream)
-        else:
-            a = dl.x if not fp8 else base + a_off
+        elif kind == "gate_up":
+            a = dl.x if not fp8 else base + L["xq"]
             a_sc = None if not fp8 else base + L["x_scales"]
             hs = None if not fp8 else base + L["h_scales"]
             moe.moe_grouped_gemm(cfg, moe.MOE_STAGE_GATE_UP, moe.MOE_GROUP_ROUTED, w, a, a_sc,
                                  base + L["sorted_ids"], base + L["offsets"], base + L["h"], hs, ws, stream)
-        if i >= args.warmup:
-            ev[i - args.warmup][1].record(stream)
-    torch.cuda.synchronize()
-    k_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        else:
+            hs = None if not fp8 else base + L["h_scales"]
+            moe.moe_grouped_gemm(cfg, moe.MOE_STAGE_DOWN, moe.MOE_GROUP_ROUTED, w, base + L["h"], hs,
+                                 base + L["sorted_ids"], base + L["offsets"], base + L["y"], None, ws, stream)
 
-    if one_launch:
-        # touched experts' gate, up and down weights, x read, out written (h and y are intermediates)
-        k_bytes = e_t * 3 * I * H * wbytes + 2 * N * H * 2
-        k_flops = 6.0 * p_r * H * I
-        k_name = "routed gate/up + SwiGLU, down, unpermute-reduce (one launch)"
-    else:
-        # touched experts' gate and up weights (+ block scales), x read, h written
-        k_bytes = (e_t * 2 * I * H * wbytes + (e_t * 2 * (I // 128) * (H // 128) * 4 if wl.weight_dtype == "fp8" else 0)
-                   + N * H * abytes + p_r * I * abytes)
-        k_flops = 4.0 * p_r * H * I
-        k_name = "grouped gate/up + SwiGLU (routed)"
-    # whole layer
-    layer_flops = 2.0 * N * H * R + 6.0 * p_r * H * I + 6.0 * N * H * Is
-    layer_bytes_alg = (e_t * 3 * I * H * wbytes + R * H * 2 + 2 * N * H * 2 + 3 * Is * H * wbytes)
-    ai = k_flops / k_bytes
+    k_us = {}
+    for kind in kinds:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for i in range(args.warmup + args.steps):
+            dl, w = layers[i % n_layers]
+            moe.moe_forward(cfg, w, dl.x, out, ws, stream)  # refreshes ids / offsets / quantised x / h
+            if i >= args.warmup:
+                ev[i - args.warmup][0].record(stream)
+            launch(kind, w, dl)
+            if i >= args.warmup:
+                ev[i - args.warmup][1].record(stream)
+        torch.cuda.synchronize()
+        k_us[kind] = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+
+    # ---- algorithmic bytes and flops (touched experts' weights counted once; h, y intermediates not
+    # counted by the one-launch kernel, which never needs them in HBM)
+    w_touched = e_t * I * H * (wbytes + sbytes)  # one of the three matrices, all touched experts
+    sh_w = Is * H * (wbytes + sbytes)  # one shared matrix
+    alg = {
+        "experts": (3 * w_touched + 3 * sh_w + 2 * N * H * 2, 6.0 * p_r * H * I + 6.0 * N * H * Is,
+                    "routed gate/up + SwiGLU, down, unpermute-reduce (one launch)"
+                    + (" after the shared expert's two GEMMs" if Is else "")),
+        "gate_up": (2 * w_touched + N * H * abytes + p_r * I * abytes, 4.0 * p_r * H * I,
+                    "routed grouped gate/up + SwiGLU"),
+        "down": (w_touched + p_r * I * abytes + p_r * H * 2, 2.0 * p_r * H * I, "routed grouped down"),
+    }
     ridge = MFMA_PEAK_TFLOPS[wl.weight_dtype] * 1e12 / (HBM_PEAK_GBS * 1e9)
-    if ai < ridge:
-        roof = {"bound": "hbm", "achieved": k_bytes / (k_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
-    else:
-        roof = {"bound": "mfma", "achieved": k_flops / (k_ms * 1e-3) / 1e12,
-                "peak": MFMA_PEAK_TFLOPS[wl.weight_dtype], "unit": "TFLOP/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(wl.name)  # bytes per launch (HBM, counters), or null
-    roof["alg_bytes"] = k_bytes
-    roof["kernel"] = k_name
-    roof["kernel_us"] = k_ms * 1e3
 
-    result = {
-        "metric": "MoE-layer tokens/sec (prefill) + decode µs/layer; % of MFMA / HBM peak",
-        "value": N / (ms * 1e-3),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms,
+    def roof(kind):
+        b, f, label = alg[kind]
+        t = k_us[kind] * 1e-6
+        hbm = b / t / 1e9
+        mfma = f / t / 1e12
+        if f / b < ridge:
+            r = {"bound": "hbm", "achieved": hbm, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+        else:
+            r = {"bound": "mfma", "achieved": mfma, "peak": MFMA_PEAK_TFLOPS[wl.weight_dtype], "unit": "TFLOP/s"}
+        r["frac"] = r["achieved"] / r["peak"]
+        r["traffic"] = measured_traffic(wl.name, kind)
+        r.update({"kernel": label, "kernel_us": k_us[kind], "alg_bytes": b, "alg_flops": f,
+                  "hbm_frac": hbm / HBM_PEAK_GBS, "mfma_frac": mfma / MFMA_PEAK_TFLOPS[wl.weight_dtype]})
+        return r
+
+    rooflines = {k: roof(k) for k in kinds}
+    dominant = max(kinds, key=lambda k: k_us[k])
+    layer_flops = 2.0 * N * H * R + 6.0 * p_r * H * I + 6.0 * N * H * Is
+    layer_bytes_alg = 3 * w_touched + R * H * 2 + 2 * N * H * 2 + 3 * sh_w
+    t_star = max(layer_flops / (MFMA_PEAK_TFLOPS[wl.weight_dtype] * 1e12), layer_bytes_alg / (HBM_PEAK_GBS * 1e9))
+    entry = {
         "us_per_layer": ms * 1e3,
+        "tokens_per_s": N / (ms * 1e-3),
         "timing": "hip_graph_replay" if use_graph else "eager",
-        "ms_per_step_eager": ms_eager,
-        "ms_per_step_graph": ms_graph,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
+        "us_per_layer_eager": ms_eager * 1e3,
+        "us_per_layer_graph": None if ms_graph is None else ms_graph * 1e3,
         "dtype": wl.weight_dtype,
-        "data": "synthetic (seeded counter-based generator; random-init weights)",
         "config": {"workload": wl.name, "num_tokens": N, "hidden": H, "num_experts": E, "router_width": R,
                    "top_k": K, "inter": I, "shared_inter": Is, "scoring": wl.scoring,
                    "weight_copies_cycled": n_layers, "experts_touched": e_t, "routed_rows": p_r},
-        "layer": {"flops": layer_flops, "alg_bytes": layer_bytes_alg,
+        "layer": {"flops": layer_flops, "alg_bytes": layer_bytes_alg, "t_star_us": t_star * 1e6,
+                  "roofline_frac": t_star / (ms * 1e-3),
                   "hbm_frac": layer_bytes_alg / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
                   "mfma_frac": layer_flops / (ms * 1e-3) / (MFMA_PEAK_TFLOPS[wl.weight_dtype] * 1e12)},
-        "roofline": roof,
+        "roofline": rooflines[dominant],
+        "kernels": rooflines,
     }
+    del layers, ws, out
+    torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
-    print(json.dumps(result))
+        entry["cpu_baseline"] = cpu_baseline(name, wl, args.cpu_seconds)
+    return entry
 
 
-def cpu_baseline(wl, seconds: float):
-    """The oracle as it stands, timed on the host cores on a bounded sample:
-    up to 64 tokens of the same layer shape, over 4 weight copies whose touched
-    experts are generated (and cached) before the timed runs."""
+def cpu_baseline(name: str, wl, seconds: float):
+    """The oracle as it stands, timed on the host cores on a bounded sample: the first few tokens of
+    the same layer shape (one weight copy), whose touched experts are generated (and cached) before
+    the timed runs; runs repeat until about `seconds` of host time are spent."""
     from threadpoolctl import threadpool_info
 
     import moe_inputs as mi
     from oracle import workloads as ow
 
-    n = min(wl.num_tokens, 64)
+    n = min(wl.num_tokens, CPU_SAMPLE_TOKENS.get(name, 4))
     sw = wl.with_tokens(n)
-    copies = []
-    for l in range(4):
-        inp, cache = mi.host_inputs(sw, layer=l), {}
-        ow.run(sw, layer=l, inputs=inp, expert_cache=cache)  # untimed: fills the expert cache
-        copies.append((l, inp, cache))
+    inp, cache = mi.host_inputs(sw), {}
+    ow.run(sw, inputs=inp, expert_cache=cache)  # untimed: fills the expert cache
     done, t_used, runs = 0, 0.0, 0
-    while t_used < seconds and runs < 10000:
-        l, inp, cache = copies[runs % len(copies)]
+    while (t_used < seconds or runs == 0) and runs < 10000:
         t0 = time.perf_counter()
-        ow.run(sw, layer=l, inputs=inp, expert_cache=cache)
+        ow.run(sw, inputs=inp, expert_cache=cache)
         t_used += time.perf_counter() - t0
         done += n
         runs += 1
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": done / t_used, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{runs} oracle runs over {n} tokens of the {wl.name} layer shape (4 weight copies, experts "
-                      f"pre-generated), {t_used:.1f} s of host time"}
+            "sample": f"{runs} oracle runs over the first {n} tokens of the {wl.name} layer (experts touched by "
+                      f"them generated beforehand), {t_used:.1f} s of host time; the BLAS pool's threads are the "
+                      f"cores counted"}
 
 
 if __name__ == "__main__":
