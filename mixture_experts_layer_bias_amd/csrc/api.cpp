@@ -181,9 +181,11 @@ moe::GroupedGemmArgs gemm_args(const moe_config_t* c, int stage, int group, cons
   moe::GroupedGemmArgs g{};
   g.stage = stage;
   g.shared = group == MOE_GROUP_SHARED;
+  g.with_shared = 0;
   g.N = c->num_tokens;
   g.H = c->hidden;
   g.I = g.shared ? c->shared_inter : c->inter;
+  g.Is = c->shared_inter;
   g.K = c->top_k;
   g.E = c->num_experts;
   g.P = g.shared ? c->num_tokens : c->num_tokens * c->top_k;
@@ -205,8 +207,42 @@ moe::GroupedGemmArgs gemm_args(const moe_config_t* c, int stage, int group, cons
   g.sh_down_s = w->sh_down_s;
   g.out = out;
   g.out_scales = out_scales;
+  if (g.shared) {  // the shared group reads and writes through the sh_* operands
+    g.sh_a = a;
+    g.sh_a_scales = a_scales;
+    g.sh_out = out;
+    g.sh_out_scales = out_scales;
+  }
   g.row_invariant = c->row_invariant;
   return g;
+}
+
+// The routed launch `routed` with the shared expert carried as one more group (index E): its A rows
+// are tokens of `sh_a`, its output rows go to `sh_out`.
+moe::GroupedGemmArgs with_shared(moe::GroupedGemmArgs routed, const void* sh_a, const float* sh_a_scales,
+                                 void* sh_out, float* sh_out_scales) {
+  routed.with_shared = 1;
+  routed.sh_a = sh_a;
+  routed.sh_a_scales = sh_a_scales;
+  routed.sh_out = sh_out;
+  routed.sh_out_scales = sh_out_scales;
+  return routed;
+}
+
+// The shared expert rides in the routed launch of a stage as one more group when the tile schedulers'
+// group tables have room for it and that launch takes the kernel that the routed experts and the
+// shared expert would each take in a launch of their own (so every output keeps its bits).
+constexpr int kMaxLaunchGroups = 1024;
+bool same_kernel(const moe_config_t* c, const moe::GroupedGemmArgs& routed, const moe::GroupedGemmArgs& shared) {
+  if (c->weight_dtype == MOE_WEIGHTS_BF16) return moe::decode_gemm_fits(routed) == moe::decode_gemm_fits(shared);
+  if (c->weight_dtype == MOE_WEIGHTS_FP8_E4M3) return moe::fp8_streams(routed) == moe::fp8_streams(shared);
+  return true;  // MXFP4: one kernel pair
+}
+bool fold_shared(const moe_config_t* c, int stage) {
+  if (c->shared_inter <= 0 || c->num_experts + 1 > kMaxLaunchGroups) return false;
+  const moe_weights_t none{};  // the kernel choice is a function of the sizes only
+  return same_kernel(c, gemm_args(c, stage, MOE_GROUP_ROUTED, &none, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr),
+                     gemm_args(c, stage, MOE_GROUP_SHARED, &none, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr));
 }
 
 moe_status_t run_gemm(const moe_config_t* c, const moe::GroupedGemmArgs& g, hipStream_t s) {
@@ -220,15 +256,21 @@ moe_status_t run_gemm(const moe_config_t* c, const moe::GroupedGemmArgs& g, hipS
   return MOE_OK;
 }
 
-// Whether the decode experts path (routed gate/up, down and the reduce in one launch) applies.
+// Whether the decode experts path (routed gate/up, down and the reduce in one launch, with the shared
+// expert as one more group when it folds) applies.
 bool experts_fused(const moe_config_t* c) {
   if (c->weight_dtype != MOE_WEIGHTS_BF16 || c->row_invariant) return false;
-  if (!moe::decode_fused_fits(c->num_experts, c->hidden)) return false;
+  if (c->shared_inter > 0 && !(fold_shared(c, MOE_STAGE_GATE_UP) && fold_shared(c, MOE_STAGE_DOWN))) return false;
+  if (!moe::decode_fused_fits(c->num_experts + (c->shared_inter > 0 ? 1 : 0), c->hidden)) return false;
   const moe_weights_t none{};  // the fit is a function of the sizes only
-  const moe::GroupedGemmArgs gu = gemm_args(c, MOE_STAGE_GATE_UP, MOE_GROUP_ROUTED, &none, nullptr, nullptr,
-                                            nullptr, nullptr, nullptr, nullptr);
-  const moe::GroupedGemmArgs dn = gemm_args(c, MOE_STAGE_DOWN, MOE_GROUP_ROUTED, &none, nullptr, nullptr, nullptr,
-                                            nullptr, nullptr, nullptr);
+  moe::GroupedGemmArgs gu = gemm_args(c, MOE_STAGE_GATE_UP, MOE_GROUP_ROUTED, &none, nullptr, nullptr, nullptr,
+                                      nullptr, nullptr, nullptr);
+  moe::GroupedGemmArgs dn = gemm_args(c, MOE_STAGE_DOWN, MOE_GROUP_ROUTED, &none, nullptr, nullptr, nullptr, nullptr,
+                                      nullptr, nullptr);
+  if (c->shared_inter > 0) {
+    gu = with_shared(gu, nullptr, nullptr, nullptr, nullptr);
+    dn = with_shared(dn, nullptr, nullptr, nullptr, nullptr);
+  }
   return moe::decode_gemm_fits(gu) && moe::decode_gemm_fits(dn);
 }
 
@@ -267,18 +309,22 @@ moe_status_t run_experts(const moe_config_t* cfg, const moe_weights_t* w, const 
                             c.hidden,
                             c.top_k,
                             c.num_experts};
-  if (fused) {
-    if (c.shared_inter > 0) {
-      MOE_RET(run_gemm(cfg, sh_gu, s));
-      MOE_RET(run_gemm(cfg, sh_dn, s));
-    }
-    MOE_HIP(moe::launch_decode_fused(gu, dn, red, static_cast<int32_t*>(at(L.sync)), s));
+  // the shared expert as one more group of the routed launches (same per-row arithmetic as its own
+  // launches), or, when the group tables have no room for it, in launches of its own
+  const bool fold_gu = fold_shared(cfg, MOE_STAGE_GATE_UP), fold_dn = fold_shared(cfg, MOE_STAGE_DOWN);
+  const moe::GroupedGemmArgs gu_all =
+      fold_gu ? with_shared(gu, a, a_scales, at(L.shared_h), static_cast<float*>(at(L.shared_h_scales))) : gu;
+  const moe::GroupedGemmArgs dn_all =
+      fold_dn ? with_shared(dn, at(L.shared_h), static_cast<float*>(at(L.shared_h_scales)), at(L.shared_y), nullptr)
+              : dn;
+  if (fused) {  // implies both folds when there is a shared expert
+    MOE_HIP(moe::launch_decode_fused(gu_all, dn_all, red, static_cast<int32_t*>(at(L.sync)), s));
     return ok();
   }
-  MOE_RET(run_gemm(cfg, gu, s));
-  if (c.shared_inter > 0) MOE_RET(run_gemm(cfg, sh_gu, s));
-  MOE_RET(run_gemm(cfg, dn, s));
-  if (c.shared_inter > 0) MOE_RET(run_gemm(cfg, sh_dn, s));
+  MOE_RET(run_gemm(cfg, gu_all, s));
+  if (c.shared_inter > 0 && !fold_gu) MOE_RET(run_gemm(cfg, sh_gu, s));
+  MOE_RET(run_gemm(cfg, dn_all, s));
+  if (c.shared_inter > 0 && !fold_dn) MOE_RET(run_gemm(cfg, sh_dn, s));
   MOE_HIP(moe::launch_unpermute_reduce(static_cast<const uint16_t*>(at(L.y)), red, s));
   return ok();
 }

@@ -49,12 +49,12 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_bf16(GroupedGemmArgs g)
   __shared__ int s_prefix[kMaxGroups + 1];
   __shared__ int s_wsum[4];
 
-  const int KD = STAGE == 0 ? g.H : g.I;     // reduction length
-  const int NCOLS = STAGE == 0 ? g.I : g.H;  // output columns
-  const int NT = NCOLS / T::COLS;
-  const TileCoord tc =
-      schedule_tile(g.offsets, g.shared ? 1 : g.E, g.shared ? g.N : -1, BM, NT, s_prefix, s_wsum);
+  const Groups G = gemm_groups(g, STAGE, T::COLS);
+  const TileCoord tc = schedule_tile(G, BM, s_prefix, s_wsum);
   if (tc.expert < 0) return;
+  const bool sh = tc.expert == G.nr;  // the shared expert's group
+  const int KD = STAGE == 0 ? g.H : (sh ? g.Is : g.I);     // reduction length
+  const int NCOLS = STAGE == 0 ? (sh ? g.Is : g.I) : g.H;  // output columns
 
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int n0 = tc.n_tile * T::COLS;
@@ -63,12 +63,12 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_bf16(GroupedGemmArgs g)
   const uint16_t* wa;  // gate (stage 0) or down (stage 1) weights
   const uint16_t* wb = nullptr;  // up weights (stage 0)
   if (STAGE == 0) {
-    wa = static_cast<const uint16_t*>(g.shared ? g.sh_gate : g.w_gate[tc.expert]);
-    wb = static_cast<const uint16_t*>(g.shared ? g.sh_up : g.w_up[tc.expert]);
+    wa = static_cast<const uint16_t*>(sh ? g.sh_gate : g.w_gate[tc.expert]);
+    wb = static_cast<const uint16_t*>(sh ? g.sh_up : g.w_up[tc.expert]);
   } else {
-    wa = static_cast<const uint16_t*>(g.shared ? g.sh_down : g.w_down[tc.expert]);
+    wa = static_cast<const uint16_t*>(sh ? g.sh_down : g.w_down[tc.expert]);
   }
-  const uint16_t* a_src = static_cast<const uint16_t*>(g.a);
+  const uint16_t* a_src = static_cast<const uint16_t*>(sh ? g.sh_a : g.a);
 
   const int lrow = tid >> 3;       // 0..31: row within a 32-row slab of the tile
   const int lcol = (tid & 7) * 8;  // bf16 column of this thread's 16-byte chunk
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_bf16(GroupedGemmArgs g)
     int p = tc.row0 + lrow + 32 * i;
     if (p >= tc.row_end) p = tc.row_end - 1;  // clamp: rows past the segment are computed, never stored
     long arow;
-    if (STAGE == 0) arow = g.shared ? p : g.sorted_ids[p] / g.K;
+    if (STAGE == 0) arow = sh ? p : g.sorted_ids[p] / g.K;
     else arow = p;
     a_ptr[i] = a_src + (size_t)arow * KD + lcol;
   }
@@ -157,7 +157,7 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_bf16(GroupedGemmArgs g)
   }
 
   // ---- epilogue.  32x32 MFMA D layout: lane l, item r -> row 8*(r/4) + 4*(l/32) + r%4, column l%32
-  uint16_t* out = static_cast<uint16_t*>(g.out);
+  uint16_t* out = static_cast<uint16_t*>(sh ? g.sh_out : g.out);
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
@@ -178,16 +178,14 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_bf16(GroupedGemmArgs g)
 }  // namespace
 
 hipError_t launch_grouped_gemm_bf16(const GroupedGemmArgs& g, hipStream_t s) {
-  const int groups = g.shared ? 1 : g.E;
-  const int rows = g.shared ? g.N : g.P;
-  if (rows == 0) return hipSuccess;
+  if (g.N == 0) return hipSuccess;
   if (!g.row_invariant && decode_gemm_fits(g)) return launch_grouped_gemm_decode(g, s);
   if (g.stage == 0) {
-    k_grouped_gemm_bf16<0><<<grouped_grid(rows, groups, BM, g.I / BN), 256, 0, s>>>(g);
+    k_grouped_gemm_bf16<0><<<grouped_grid(g, gemm_groups(g, 0, BN), BM), 256, 0, s>>>(g);
   } else if (g.H % (2 * BN) == 0) {
-    k_grouped_gemm_bf16<2><<<grouped_grid(rows, groups, BM, g.H / (2 * BN)), 256, 0, s>>>(g);
+    k_grouped_gemm_bf16<2><<<grouped_grid(g, gemm_groups(g, 1, 2 * BN), BM), 256, 0, s>>>(g);
   } else {
-    k_grouped_gemm_bf16<1><<<grouped_grid(rows, groups, BM, g.H / BN), 256, 0, s>>>(g);
+    k_grouped_gemm_bf16<1><<<grouped_grid(g, gemm_groups(g, 1, BN), BM), 256, 0, s>>>(g);
   }
   return hipGetLastError();
 }

@@ -1,53 +1,85 @@
 // Device-side tile scheduler shared by the grouped expert GEMMs.
 //
-// The rows of each expert are a contiguous segment [offsets[e], offsets[e+1])
+// The rows of each routed expert are a contiguous segment [offsets[e], offsets[e+1])
 // of the sorted rows (forward_prefill.rs page, expert_offsets of
-// moe_sort_by_expert).  Expert e needs ceil(count_e / BM) row tiles times NT
-// column tiles.  The host only knows an upper bound of the tile count, so the
-// grid is sized to that bound (a multiple of 8) and every block recomputes the
-// exact per-expert tile prefix from the device offsets, then either takes a
-// tile or leaves.
+// moe_sort_by_expert).  A launch may also carry the shared expert as one more
+// group after the routed ones, holding all N tokens as rows [0, N) of its own
+// (run_shared_expert_prefill on the same page: a dense MLP over every token).
+// Group e needs ceil(rows_e / BM) row tiles times its column tiles (the shared
+// expert's intermediate size may differ from the routed experts', so a gate/up
+// launch has two column-tile counts).  The host only knows an upper bound of the
+// tile count, so the grid is sized to that bound (a multiple of 8) and every
+// block recomputes the exact per-group tile prefix from the device offsets, then
+// either takes a tile or leaves.
 //
 // Block -> tile map: MI355X hands consecutive workgroups to its 8 XCDs round
 // robin, and each XCD has its own L2.  Block b runs on XCD b % 8, so it takes
 // logical tile (b % 8) * ceil(T/8) + b / 8: each XCD works through one
-// contiguous range of logical tiles.  Within an expert the logical order is
+// contiguous range of logical tiles.  Within a group the logical order is
 // (column tile, row tile) with row tiles fastest, so the blocks that share one
 // weight slab run together on one XCD and read it from HBM once.
 #pragma once
 
 #include "common.h"
+#include "kernels.h"
 
 namespace moe {
 
 constexpr int kMaxGroups = 1024;
 
-struct TileCoord {
-  int expert;   // -1: this block has no tile
-  int m_tile;
-  int n_tile;
-  int row0;     // first sorted row of the tile
-  int row_end;  // end of the tile's rows: the segment's end, or the next tile's first row (even split)
-  int m_tiles;  // row tiles over all groups (the tiles of one column tile)
+// The groups of one launch: routed groups [0, nr) read from offsets, then, if xr > 0, one more group
+// (index nr) of rows [0, xr): the shared expert.
+struct Groups {
+  const int32_t* offsets;
+  int nr;   // routed groups
+  int xr;   // rows of the shared group (0: none)
+  int nt;   // column tiles of a routed group
+  int xnt;  // column tiles of the shared group
 };
 
-// s_prefix must hold kMaxGroups + 1 ints in LDS.  Block of at least 256 threads.  `b` is the
-// block's tile slot (blockIdx.x unless one launch runs several grids of tiles).
+// The groups of a grouped GEMM launch whose tiles cover COLS output columns: gate/up (stage 0) has I
+// output columns per routed expert and Is for the shared one, down has H for both.
+__host__ __device__ inline Groups gemm_groups(const GroupedGemmArgs& g, int stage, int COLS) {
+  Groups G;
+  G.offsets = g.offsets;
+  G.nr = g.shared ? 0 : g.E;
+  G.xr = (g.shared || g.with_shared) ? g.N : 0;
+  G.nt = (stage == 0 ? g.I : g.H) / COLS;
+  G.xnt = (stage == 0 ? g.Is : g.H) / COLS;
+  return G;
+}
+
+struct TileCoord {
+  int expert;   // -1: this block has no tile; the shared group has index Groups::nr
+  int m_tile;
+  int n_tile;
+  int row0;     // first row of the tile (sorted row; a token for the shared group)
+  int row_end;  // end of the tile's rows: the segment's end, or the next tile's first row (even split)
+  int m_tiles;  // row tiles over all groups (the tiles of one column tile) when every group has the same
+                // column-tile count, else -1
+};
+
+// rows of group e (0 past the last group)
+__device__ __forceinline__ int group_rows(const Groups& G, int e) {
+  if (e < G.nr) return G.offsets[e + 1] - G.offsets[e];
+  return e == G.nr ? G.xr : 0;
+}
+
+// s_prefix must hold kMaxGroups + 1 ints in LDS (G.nr + (G.xr > 0) <= kMaxGroups).  Block of at least
+// 256 threads.  `b` is the block's tile slot (blockIdx.x unless one launch runs several grids of tiles).
 // split_align == 0: a segment's tiles start every BM rows, the last one ragged.  split_align > 0 (a
 // divisor of BM): the segment is cut into the same number of tiles, of ceil(rows / tiles) rows
 // rounded up to split_align, so its tiles carry nearly equal work (130 rows: 96 + 34, not 128 + 2).
-__device__ __forceinline__ TileCoord schedule_tile_at(const int32_t* __restrict__ offsets, int num_groups,
-                                                      int shared_rows, int BM, int NT, int* s_prefix, int* s_wsum,
-                                                      int b, int split_align = 0) {
+__device__ __forceinline__ TileCoord schedule_tile_at(const Groups& G, int BM, int* s_prefix, int* s_wsum, int b,
+                                                      int split_align = 0) {
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  // each thread owns 4 consecutive groups
+  const int ngroups = G.nr + (G.xr > 0 ? 1 : 0);
+  // each thread owns 4 consecutive groups; the prefix counts tiles (row tiles x column tiles)
   int cnt[4], local = 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = tid * 4 + j;
-    int c = 0;
-    if (e < num_groups) c = shared_rows >= 0 ? shared_rows : (offsets[e + 1] - offsets[e]);
-    cnt[j] = (c + BM - 1) / BM;
+    cnt[j] = e < ngroups ? (group_rows(G, e) + BM - 1) / BM * (e < G.nr ? G.nt : G.xnt) : 0;
     local += cnt[j];
   }
   // inclusive scan of `local` across the block
@@ -65,34 +97,34 @@ __device__ __forceinline__ TileCoord schedule_tile_at(const int32_t* __restrict_
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = tid * 4 + j;
-    if (e < num_groups) s_prefix[e] = run;
+    if (e < ngroups) s_prefix[e] = run;
     run += cnt[j];
   }
-  if (tid == 0) s_prefix[num_groups] = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
+  if (tid == 0) s_prefix[ngroups] = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
   __syncthreads();
 
-  TileCoord tc{-1, 0, 0, 0, 0, s_prefix[num_groups]};
-  const int T = s_prefix[num_groups] * NT;
+  const int T = s_prefix[ngroups];
+  TileCoord tc{-1, 0, 0, 0, 0, G.nt == G.xnt || G.xr == 0 ? T / G.nt : -1};
   const int chunk = (T + 7) / 8;
   const int local_idx = b / 8;
   if (local_idx >= chunk) return tc;
   const int L = (b % 8) * chunk + local_idx;
   if (L >= T) return tc;
-  // largest e with s_prefix[e] * NT <= L
-  int lo = 0, hi = num_groups - 1;
+  // largest e with s_prefix[e] <= L
+  int lo = 0, hi = ngroups - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) / 2;
-    if (s_prefix[mid] * NT <= L) lo = mid;
+    if (s_prefix[mid] <= L) lo = mid;
     else hi = mid - 1;
   }
   const int e = lo;
-  const int mt_e = s_prefix[e + 1] - s_prefix[e];
-  const int rem = L - s_prefix[e] * NT;
+  const int seg0 = e < G.nr ? G.offsets[e] : 0;
+  const int seg_end = e < G.nr ? G.offsets[e + 1] : G.xr;
+  const int mt_e = (seg_end - seg0 + BM - 1) / BM;
+  const int rem = L - s_prefix[e];
   tc.expert = e;
   tc.n_tile = rem / mt_e;
   tc.m_tile = rem % mt_e;
-  const int seg0 = shared_rows >= 0 ? 0 : offsets[e];
-  const int seg_end = shared_rows >= 0 ? shared_rows : offsets[e + 1];
   // rows per tile: BM, or the even split (never above BM, and mt_e - 1 tiles of it stay below the
   // segment's rows, so every tile is non-empty)
   int rpt = BM;
@@ -105,9 +137,9 @@ __device__ __forceinline__ TileCoord schedule_tile_at(const int32_t* __restrict_
   return tc;
 }
 
-__device__ __forceinline__ TileCoord schedule_tile(const int32_t* __restrict__ offsets, int num_groups, int shared_rows,
-                                                   int BM, int NT, int* s_prefix, int* s_wsum, int split_align = 0) {
-  return schedule_tile_at(offsets, num_groups, shared_rows, BM, NT, s_prefix, s_wsum, blockIdx.x, split_align);
+__device__ __forceinline__ TileCoord schedule_tile(const Groups& G, int BM, int* s_prefix, int* s_wsum,
+                                                   int split_align = 0) {
+  return schedule_tile_at(G, BM, s_prefix, s_wsum, blockIdx.x, split_align);
 }
 
 // Grid size for a grouped GEMM: an upper bound of the tile count, rounded up to 8.
@@ -116,6 +148,13 @@ inline unsigned grouped_grid(int rows_upper, int num_groups, int BM, int NT) {
   long t = mt * NT;
   t = (t + 7) / 8 * 8;
   return (unsigned)t;
+}
+
+// The same bound for a launch's groups (routed rows P = N K at most, plus the shared group's rows).
+inline unsigned grouped_grid(const GroupedGemmArgs& g, const Groups& G, int BM) {
+  const int rows = (G.nr > 0 ? g.P : 0) + G.xr;
+  const int groups = G.nr + (G.xr > 0 ? 1 : 0);
+  return grouped_grid(rows, groups, BM, G.nt > G.xnt ? G.nt : G.xnt);
 }
 
 }  // namespace moe

@@ -142,7 +142,8 @@ __device__ void reduce_columns(const ReduceArgs& r, const uint16_t* y, int c0, i
     }
     const size_t xo = (size_t)t * r.H + c;
     const u32x4 xv = zero != 0.f ? ld16(r.x + xo) : z4;
-    const u32x4 sv = r.shared_y ? ld16(r.shared_y + xo) : z4;
+    // the shared expert's y may come from down tiles of this very launch (other XCDs): device scope
+    const u32x4 sv = r.shared_y ? ld16_device_scope(r.shared_y + xo) : z4;
     st16(r.out + xo, finish_bf16x8(acc, zero, xv, r.shared_y != nullptr, sv, gated ? s_w[t] : 1.0f));
   }
 }
@@ -161,7 +162,7 @@ __device__ void reduce_columns(const ReduceArgs& r, const uint16_t* y, int c0, i
 // No cache-wide write-back or invalidate is needed on either side.
 template <int STAGE, bool FUSED>
 __device__ __forceinline__ void decode_tile(const GroupedGemmArgs& g, uint8_t* smem, int block, int32_t* done,
-                                            int gu_tiles_per_row_tile, const ReduceArgs* ra) {
+                                            int gu_nt, int gu_xnt, const ReduceArgs* ra) {
   using S = DecodeShape<STAGE>;
   constexpr int BM = S::BM, BNB = S::BNB, ROWB = S::ROWB, WK = S::WK, WN = 4 / WK;
   constexpr int NSTAGE = S::NSTAGE, AI = S::AI, BI = S::BI, VM = AI + BI;
@@ -179,12 +180,13 @@ __device__ __forceinline__ void decode_tile(const GroupedGemmArgs& g, uint8_t* s
   int* s_prefix = reinterpret_cast<int*>(smem);     // scheduler scratch, dead before the first load
   int* s_wsum = s_prefix + kMaxGroups + 1;
 
-  const int KD = STAGE == 0 ? g.H : g.I;
-  const int NCOLS = STAGE == 0 ? g.I : g.H;
   const int COLS_PER_TILE = STAGE == 0 ? BNB / 2 : BNB;
-  const int NT = NCOLS / COLS_PER_TILE;
-  const TileCoord tc =
-      schedule_tile_at(g.offsets, g.shared ? 1 : g.E, g.shared ? g.N : -1, BM, NT, s_prefix, s_wsum, block);
+  const Groups G = gemm_groups(g, STAGE, COLS_PER_TILE);
+  const TileCoord tc = schedule_tile_at(G, BM, s_prefix, s_wsum, block);
+  const int NT = G.nt;  // column tiles of a routed group (down: of every group)
+  const bool sh = tc.expert == G.nr;  // the shared expert's group
+  const int KD = STAGE == 0 ? g.H : (sh ? g.Is : g.I);
+  const int NCOLS = STAGE == 0 ? (sh ? g.Is : g.I) : g.H;
   if (tc.expert < 0) {  // the same decision in every thread of the block
     // FUSED with no routed rows at all (every slot took an identity expert): no down tile counts,
     // so the first NT slots reduce one column tile each
@@ -202,10 +204,10 @@ __device__ __forceinline__ void decode_tile(const GroupedGemmArgs& g, uint8_t* s
 
   const uint8_t *wa, *wb = nullptr;
   if (STAGE == 0) {
-    wa = static_cast<const uint8_t*>(g.shared ? g.sh_gate : g.w_gate[tc.expert]);
-    wb = static_cast<const uint8_t*>(g.shared ? g.sh_up : g.w_up[tc.expert]);
+    wa = static_cast<const uint8_t*>(sh ? g.sh_gate : g.w_gate[tc.expert]);
+    wb = static_cast<const uint8_t*>(sh ? g.sh_up : g.w_up[tc.expert]);
   } else {
-    wa = static_cast<const uint8_t*>(g.shared ? g.sh_down : g.w_down[tc.expert]);
+    wa = static_cast<const uint8_t*>(sh ? g.sh_down : g.w_down[tc.expert]);
   }
 
   // Load sources.  One instruction writes RPI rows x ROWB bytes; lane l covers row l / LPR
@@ -220,9 +222,10 @@ __device__ __forceinline__ void decode_tile(const GroupedGemmArgs& g, uint8_t* s
     int p = tc.row0 + trow;
     if (p >= tc.row_end) p = tc.row_end - 1;  // rows past the segment are computed, never stored
     long arow;
-    if (STAGE == 0) arow = g.shared ? p : g.sorted_ids[p] / g.K;
+    if (STAGE == 0) arow = sh ? p : g.sorted_ids[p] / g.K;
     else arow = p;
-    a_ptr[i] = static_cast<const uint8_t*>(g.a) + (size_t)arow * row_bytes + ((pslot ^ (trow % LPR)) << 4);
+    a_ptr[i] = static_cast<const uint8_t*>(sh ? g.sh_a : g.a) + (size_t)arow * row_bytes +
+               ((pslot ^ (trow % LPR)) << 4);
   }
   const uint8_t* b_ptr[BI];
 #pragma unroll
@@ -283,8 +286,10 @@ __device__ __forceinline__ void decode_tile(const GroupedGemmArgs& g, uint8_t* s
     for (int s = 0; s < NSTAGE - 1; ++s)
       if (s < nk) issue_b(s, s);
     if (threadIdx.x == 0) {
-      const int count = g.offsets[tc.expert + 1] - g.offsets[tc.expert];
-      const int need = gu_tiles_per_row_tile * ((count + DecodeShape<0>::BM - 1) / DecodeShape<0>::BM);
+      // the group's gate/up tiles: its row tiles times its gate/up column tiles (the shared expert's
+      // intermediate size may differ from the routed experts')
+      const int count = group_rows(G, tc.expert);
+      const int need = (sh ? gu_xnt : gu_nt) * ((count + DecodeShape<0>::BM - 1) / DecodeShape<0>::BM);
       bool ready = false;
       for (int it = 0; it < kDoneSpinLimit && !ready; ++it) {
         ready = __hip_atomic_load(done + kSyncExperts + tc.expert, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
@@ -332,7 +337,7 @@ __device__ __forceinline__ void decode_tile(const GroupedGemmArgs& g, uint8_t* s
   }
 
   // epilogue.  16x16 D layout: lane l, item r -> row 16 mi + 4 (l / 16) + r, column l % 16 of the block
-  uint16_t* out = static_cast<uint16_t*>(g.out);
+  uint16_t* out = static_cast<uint16_t*>(sh ? g.sh_out : g.out);
   if (WK == 1) {  // every wave holds whole sums for its weight blocks
 #pragma unroll
     for (int mi = 0; mi < MT; ++mi)
@@ -402,7 +407,8 @@ __device__ __forceinline__ void decode_tile(const GroupedGemmArgs& g, uint8_t* s
     }
     __syncthreads();
     if (*s_last) {
-      reduce_columns(*ra, out, n0, BNB, reinterpret_cast<float*>(smem) + 16);
+      // the routed rows of y (g.out), whichever group this tile belongs to
+      reduce_columns(*ra, static_cast<const uint16_t*>(g.out), n0, BNB, reinterpret_cast<float*>(smem) + 16);
       if (threadIdx.x == 0) {
         const int before =
             __hip_atomic_fetch_add(done + kSyncReduced, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -410,7 +416,7 @@ __device__ __forceinline__ void decode_tile(const GroupedGemmArgs& g, uint8_t* s
       }
       __syncthreads();
       if (s_last[1]) {  // every other tile has counted itself: clear what this launch used
-        for (int i = threadIdx.x; i < g.E; i += 256)
+        for (int i = threadIdx.x; i < G.nr + (G.xr > 0 ? 1 : 0); i += 256)  // the groups' counts
           __hip_atomic_store(done + kSyncExperts + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         for (int i = threadIdx.x; i < NT; i += 256)
           __hip_atomic_store(done + kSyncColTiles + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -423,28 +429,29 @@ __device__ __forceinline__ void decode_tile(const GroupedGemmArgs& g, uint8_t* s
 template <int STAGE>
 __global__ __launch_bounds__(256, 2) void k_grouped_gemm_decode(GroupedGemmArgs g) {
   extern __shared__ __align__(16) uint8_t smem[];  // dc_ring_bytes<STAGE>() bytes
-  decode_tile<STAGE, false>(g, smem, blockIdx.x, nullptr, 0, nullptr);
+  decode_tile<STAGE, false>(g, smem, blockIdx.x, nullptr, 0, 0, nullptr);
 }
 
-// gate/up, down and the reduce of the routed experts in one launch: blocks [0, gu_blocks) take
-// gate/up tiles, the rest take down tiles, which wait for their expert's h (gu_blocks is a multiple
-// of 8, so a block keeps its XCD-aware tile order).  Workgroups are dispatched in order on each
-// XCD, so every gate/up tile is running or done before a down tile of the same XCD can occupy a
-// slot, and gate/up tiles never wait: every wait ends.
+// gate/up, down and the reduce of the routed experts (and, with_shared, the shared expert as one more
+// group) in one launch: blocks [0, gu_blocks) take gate/up tiles, the rest take down tiles, which
+// wait for their group's h (gu_blocks is a multiple of 8, so a block keeps its XCD-aware tile order).
+// Workgroups are dispatched in order on each XCD, so every gate/up tile is running or done before a
+// down tile of the same XCD can occupy a slot, and gate/up tiles never wait: every wait ends.
 __global__ __launch_bounds__(256, 2) void k_decode_fused(GroupedGemmArgs gu, GroupedGemmArgs dn, ReduceArgs r,
                                                          int gu_blocks, int32_t* done) {
   extern __shared__ __align__(16) uint8_t smem[];
-  const int gu_nt = gu.I / (DecodeShape<0>::BNB / 2);
-  if ((int)blockIdx.x < gu_blocks) decode_tile<0, true>(gu, smem, blockIdx.x, done, gu_nt, nullptr);
-  else decode_tile<1, true>(dn, smem, blockIdx.x - gu_blocks, done, gu_nt, &r);
+  const int gu_nt = gu.I / (DecodeShape<0>::BNB / 2), gu_xnt = gu.Is / (DecodeShape<0>::BNB / 2);
+  if ((int)blockIdx.x < gu_blocks) decode_tile<0, true>(gu, smem, blockIdx.x, done, gu_nt, gu_xnt, nullptr);
+  else decode_tile<1, true>(dn, smem, blockIdx.x - gu_blocks, done, gu_nt, gu_xnt, &r);
 }
 
 template <int STAGE>
-hipError_t launch_decode(const GroupedGemmArgs& g, int groups, int rows, int nt, hipStream_t s) {
+hipError_t launch_decode(const GroupedGemmArgs& g, hipStream_t s) {
   constexpr int lds = dc_ring_bytes<STAGE>();
   const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&k_grouped_gemm_decode<STAGE>), lds);
   if (e != hipSuccess) return e;
-  k_grouped_gemm_decode<STAGE><<<grouped_grid(rows, groups, DecodeShape<STAGE>::BM, nt), 256, lds, s>>>(g);
+  constexpr int cols = STAGE == 0 ? DecodeShape<0>::BNB / 2 : DecodeShape<1>::BNB;
+  k_grouped_gemm_decode<STAGE><<<grouped_grid(g, gemm_groups(g, STAGE, cols), DecodeShape<STAGE>::BM), 256, lds, s>>>(g);
   return hipGetLastError();
 }
 
@@ -456,32 +463,38 @@ bool decode_fused_fits(int E, int H) {
 
 hipError_t launch_decode_fused(const GroupedGemmArgs& gu, const GroupedGemmArgs& dn, const ReduceArgs& r,
                                int32_t* done, hipStream_t s) {
-  const int rows = gu.P;
-  if (rows == 0) return hipSuccess;
+  if (gu.N == 0) return hipSuccess;
   const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&k_decode_fused), DC_LDS);
   if (e != hipSuccess) return e;
-  const unsigned gu_blocks = grouped_grid(rows, gu.E, DecodeShape<0>::BM, gu.I / (DecodeShape<0>::BNB / 2));
-  const unsigned dn_blocks = grouped_grid(rows, dn.E, DecodeShape<1>::BM, dn.H / DecodeShape<1>::BNB);
+  const unsigned gu_blocks = grouped_grid(gu, gemm_groups(gu, 0, DecodeShape<0>::BNB / 2), DecodeShape<0>::BM);
+  const unsigned dn_blocks = grouped_grid(dn, gemm_groups(dn, 1, DecodeShape<1>::BNB), DecodeShape<1>::BM);
   k_decode_fused<<<gu_blocks + dn_blocks, 256, DC_LDS, s>>>(gu, dn, r, (int)gu_blocks, done);
   return hipGetLastError();
 }
 
+namespace {
+
+// whole K steps (ROWB / 2 elements) and whole column tiles for an expert of intermediate size I
+bool decode_shape_fits(int stage, int H, int I) {
+  return stage == 0 ? (H % (DecodeShape<0>::ROWB / 2) == 0 && I % (DecodeShape<0>::BNB / 2) == 0)
+                    : (I % (DecodeShape<1>::ROWB / 2) == 0 && H % DecodeShape<1>::BNB == 0);
+}
+
+}  // namespace
+
 bool decode_gemm_fits(const GroupedGemmArgs& g) {
-  const int groups = g.shared ? 1 : g.E;
-  const int rows = g.shared ? g.N : g.P;
-  const bool few_rows = rows <= 8L * groups && rows <= 512;  // about one row tile per touched expert
-  if (!few_rows) return false;
-  // whole K steps (ROWB / 2 elements) and whole column tiles
-  return g.stage == 0 ? (g.H % (DecodeShape<0>::ROWB / 2) == 0 && g.I % (DecodeShape<0>::BNB / 2) == 0)
-                      : (g.I % (DecodeShape<1>::ROWB / 2) == 0 && g.H % DecodeShape<1>::BNB == 0);
+  // routed experts: about one row tile per touched expert; the shared expert: a decode-sized batch.
+  // A launch that carries both takes the decode kernels only when each part would on its own, so
+  // every group gets the same kernel, and the same bits, as in a launch of its own.
+  const bool routed = (long)g.P <= 8L * g.E && g.P <= 512 && decode_shape_fits(g.stage, g.H, g.I);
+  const bool shared = g.N <= 64 && decode_shape_fits(g.stage, g.H, g.Is);
+  if (g.shared) return shared;
+  return routed && (!g.with_shared || shared);
 }
 
 hipError_t launch_grouped_gemm_decode(const GroupedGemmArgs& g, hipStream_t s) {
-  const int groups = g.shared ? 1 : g.E;
-  const int rows = g.shared ? g.N : g.P;
-  if (rows == 0) return hipSuccess;
-  return g.stage == 0 ? launch_decode<0>(g, groups, rows, g.I / (DecodeShape<0>::BNB / 2), s)
-                      : launch_decode<1>(g, groups, rows, g.H / DecodeShape<1>::BNB, s);
+  if (g.N == 0) return hipSuccess;
+  return g.stage == 0 ? launch_decode<0>(g, s) : launch_decode<1>(g, s);
 }
 
 }  // namespace moe

@@ -48,13 +48,13 @@ __global__ __launch_bounds__(256, STAGE == 0 ? 1 : 2) void k_grouped_gemm_fp8(Gr
   __shared__ int s_prefix[kMaxGroups + 1];
   __shared__ int s_wsum[4];
 
-  const int KD = STAGE == 0 ? g.H : g.I;
-  const int NCOLS = STAGE == 0 ? g.I : g.H;
-  const int NT = NCOLS / BN;
-  const int KB = KD / 128;  // scale blocks along K
-  const TileCoord tc =
-      schedule_tile(g.offsets, g.shared ? 1 : g.E, g.shared ? g.N : -1, BM, NT, s_prefix, s_wsum, 32);
+  const Groups G = gemm_groups(g, STAGE, BN);
+  const TileCoord tc = schedule_tile(G, BM, s_prefix, s_wsum, 32);
   if (tc.expert < 0) return;
+  const bool sh = tc.expert == G.nr;  // the shared expert's group
+  const int KD = STAGE == 0 ? g.H : (sh ? g.Is : g.I);
+  const int NCOLS = STAGE == 0 ? (sh ? g.Is : g.I) : g.H;
+  const int KB = KD / 128;  // scale blocks along K
 
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int n0 = tc.n_tile * BN;
@@ -62,19 +62,20 @@ __global__ __launch_bounds__(256, STAGE == 0 ? 1 : 2) void k_grouped_gemm_fp8(Gr
   const uint8_t *wa, *wb = nullptr;
   const float *sa_w, *sb_w = nullptr;  // weight block scales
   if (STAGE == 0) {
-    wa = static_cast<const uint8_t*>(g.shared ? g.sh_gate : g.w_gate[tc.expert]);
-    wb = static_cast<const uint8_t*>(g.shared ? g.sh_up : g.w_up[tc.expert]);
-    sa_w = g.shared ? g.sh_gate_s : g.s_gate[tc.expert];
-    sb_w = g.shared ? g.sh_up_s : g.s_up[tc.expert];
+    wa = static_cast<const uint8_t*>(sh ? g.sh_gate : g.w_gate[tc.expert]);
+    wb = static_cast<const uint8_t*>(sh ? g.sh_up : g.w_up[tc.expert]);
+    sa_w = sh ? g.sh_gate_s : g.s_gate[tc.expert];
+    sb_w = sh ? g.sh_up_s : g.s_up[tc.expert];
   } else {
-    wa = static_cast<const uint8_t*>(g.shared ? g.sh_down : g.w_down[tc.expert]);
-    sa_w = g.shared ? g.sh_down_s : g.s_down[tc.expert];
+    wa = static_cast<const uint8_t*>(sh ? g.sh_down : g.w_down[tc.expert]);
+    sa_w = sh ? g.sh_down_s : g.s_down[tc.expert];
   }
   // weight scales of this tile's 128 output columns: row block n0/128 of the [NCOLS/128, KB] scale grid
   const float* swa = sa_w + (size_t)(n0 / 128) * KB;
   const float* swb = STAGE == 0 ? sb_w + (size_t)(n0 / 128) * KB : nullptr;
 
-  const uint8_t* a_src = static_cast<const uint8_t*>(g.a);
+  const uint8_t* a_src = static_cast<const uint8_t*>(sh ? g.sh_a : g.a);
+  const float* a_scales = sh ? g.sh_a_scales : g.a_scales;
   const int lrow = tid >> 3;        // 0..31
   const int lcol = (tid & 7) * 16;  // byte column of this thread's 16-byte chunk
   const uint8_t* a_ptr[T::A_LOADS];
@@ -82,7 +83,7 @@ __global__ __launch_bounds__(256, STAGE == 0 ? 1 : 2) void k_grouped_gemm_fp8(Gr
   for (int i = 0; i < T::A_LOADS; ++i) {
     int p = tc.row0 + lrow + 32 * i;
     if (p >= tc.row_end) p = tc.row_end - 1;
-    long arow = STAGE == 0 ? (g.shared ? p : g.sorted_ids[p] / g.K) : p;
+    long arow = STAGE == 0 ? (sh ? p : g.sorted_ids[p] / g.K) : p;
     a_ptr[i] = a_src + (size_t)arow * KD + lcol;
   }
   // the row-scale row of the A row this thread stages (threads 0..127, one row each)
@@ -90,8 +91,8 @@ __global__ __launch_bounds__(256, STAGE == 0 ? 1 : 2) void k_grouped_gemm_fp8(Gr
   if (tid < BM) {
     int p = tc.row0 + tid;
     if (p >= tc.row_end) p = tc.row_end - 1;
-    long arow = STAGE == 0 ? (g.shared ? p : g.sorted_ids[p] / g.K) : p;
-    asc_ptr = g.a_scales + (size_t)arow * KB;
+    long arow = STAGE == 0 ? (sh ? p : g.sorted_ids[p] / g.K) : p;
+    asc_ptr = a_scales + (size_t)arow * KB;
   }
   const uint8_t* b_ptr[T::B_LOADS];
 #pragma unroll
@@ -188,7 +189,7 @@ __global__ __launch_bounds__(256, STAGE == 0 ? 1 : 2) void k_grouped_gemm_fp8(Gr
   }
 
   if (STAGE == 1) {
-    uint16_t* out = static_cast<uint16_t*>(g.out);
+    uint16_t* out = static_cast<uint16_t*>(sh ? g.sh_out : g.out);
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
@@ -222,7 +223,8 @@ __global__ __launch_bounds__(256, STAGE == 0 ? 1 : 2) void k_grouped_gemm_fp8(Gr
       if ((lane & 31) == 0) s_amax[wn][wm * 64 + mi * 32 + item_row(r)] = m;
     }
   __syncthreads();
-  uint8_t* out = static_cast<uint8_t*>(g.out);
+  uint8_t* out = static_cast<uint8_t*>(sh ? g.sh_out : g.out);
+  float* out_scales = sh ? g.sh_out_scales : g.out_scales;
   const int groups = NCOLS / 128;
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
@@ -239,7 +241,7 @@ __global__ __launch_bounds__(256, STAGE == 0 ? 1 : 2) void k_grouped_gemm_fp8(Gr
           out[(size_t)row * NCOLS + col] = (uint8_t)f32_to_e4m3(h[mi][r][ni] * inv);
         }
         if (wn == 0 && (lane & 31) == 0)
-          g.out_scales[(size_t)row * groups + tc.n_tile] = amax > 0.f ? amax / 448.0f : 1.0f;
+          out_scales[(size_t)row * groups + tc.n_tile] = amax > 0.f ? amax / 448.0f : 1.0f;
       }
     }
 }
@@ -290,14 +292,15 @@ __global__ __launch_bounds__(StreamWaves<STAGE>::WAVES * 64, 1) void k_grouped_g
   int* s_wsum = s_prefix + kMaxGroups + 1;
   float* s_ws = reinterpret_cast<float*>(smem + SNSTAGE * SSTAGE);  // [2][SMAXKB] weight-block scales
 
-  const int KD = STAGE == 0 ? g.H : g.I;
-  const int NCOLS = STAGE == 0 ? g.I : g.H;
   const int COLS = STAGE == 0 ? SBNB / 2 : SBNB;  // output columns per tile
-  const int NT = NCOLS / COLS;
-  const int KB = KD / 128;
-  const TileCoord tc =
-      schedule_tile(g.offsets, g.shared ? 1 : g.E, g.shared ? g.N : -1, SBM, NT, s_prefix, s_wsum, 32);
+  const Groups G = gemm_groups(g, STAGE, COLS);
+  const TileCoord tc = schedule_tile(G, SBM, s_prefix, s_wsum, 32);
   if (tc.expert < 0) return;  // the same decision in every thread
+  const bool sh = tc.expert == G.nr;  // the shared expert's group
+  const int KD = STAGE == 0 ? g.H : (sh ? g.Is : g.I);
+  const int NCOLS = STAGE == 0 ? (sh ? g.Is : g.I) : g.H;
+  const int NT = NCOLS / COLS;  // the group's column tiles
+  const int KB = KD / 128;
 
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -307,13 +310,13 @@ __global__ __launch_bounds__(StreamWaves<STAGE>::WAVES * 64, 1) void k_grouped_g
   const uint8_t *wa, *wb = nullptr;
   const float *sa_w, *sb_w = nullptr;
   if (STAGE == 0) {
-    wa = static_cast<const uint8_t*>(g.shared ? g.sh_gate : g.w_gate[tc.expert]);
-    wb = static_cast<const uint8_t*>(g.shared ? g.sh_up : g.w_up[tc.expert]);
-    sa_w = g.shared ? g.sh_gate_s : g.s_gate[tc.expert];
-    sb_w = g.shared ? g.sh_up_s : g.s_up[tc.expert];
+    wa = static_cast<const uint8_t*>(sh ? g.sh_gate : g.w_gate[tc.expert]);
+    wb = static_cast<const uint8_t*>(sh ? g.sh_up : g.w_up[tc.expert]);
+    sa_w = sh ? g.sh_gate_s : g.s_gate[tc.expert];
+    sb_w = sh ? g.sh_up_s : g.s_up[tc.expert];
   } else {
-    wa = static_cast<const uint8_t*>(g.shared ? g.sh_down : g.w_down[tc.expert]);
-    sa_w = g.shared ? g.sh_down_s : g.s_down[tc.expert];
+    wa = static_cast<const uint8_t*>(sh ? g.sh_down : g.w_down[tc.expert]);
+    sa_w = sh ? g.sh_down_s : g.s_down[tc.expert];
   }
   __syncthreads();  // every wave is done with the scheduler scratch before the loads reuse it
   // weight-block scales ([NCOLS / 128, KB] grid) of the tile into LDS: gate/up: row 0 the gate
@@ -338,13 +341,13 @@ __global__ __launch_bounds__(StreamWaves<STAGE>::WAVES * 64, 1) void k_grouped_g
   auto a_row = [&](int trow) -> long {  // source row of tile row trow (clamped into the segment)
     int p = tc.row0 + trow;
     if (p >= tc.row_end) p = tc.row_end - 1;  // rows past the segment are computed, never stored
-    return STAGE == 0 ? (g.shared ? p : g.sorted_ids[p] / g.K) : p;
+    return STAGE == 0 ? (sh ? p : g.sorted_ids[p] / g.K) : p;
   };
   const uint8_t* a_ptr[SAI];  // A: wave w fills tile rows SAR w .. SAR w + SAR - 1
 #pragma unroll
   for (int i = 0; i < SAI; ++i) {
     const int r = wave * SAR + 8 * i + prow;
-    a_ptr[i] = static_cast<const uint8_t*>(g.a) + (size_t)a_row(r) * KD + (lch(r) << 4);
+    a_ptr[i] = static_cast<const uint8_t*>(sh ? g.sh_a : g.a) + (size_t)a_row(r) * KD + (lch(r) << 4);
   }
   // B: wave w fills weight rows SBR w .. SBR w + SBR - 1 (gate/up: the first 128 gate, the rest up)
   const uint8_t* b_ptr[SBI];
@@ -356,7 +359,7 @@ __global__ __launch_bounds__(StreamWaves<STAGE>::WAVES * 64, 1) void k_grouped_g
     b_ptr[i] = row_base + (lch(r) << 4);
   }
   // row scales: lanes 0 .. SAR - 1 of wave w load the scale of tile row SAR w + lane
-  const float* sc_ptr = g.a_scales + (size_t)a_row(wave * SAR + (lane % SAR)) * KB;
+  const float* sc_ptr = (sh ? g.sh_a_scales : g.a_scales) + (size_t)a_row(wave * SAR + (lane % SAR)) * KB;
 
   auto issue = [&](int buf, int kb) {
     uint8_t* sa = smem + buf * SSTAGE;
@@ -460,7 +463,7 @@ __global__ __launch_bounds__(StreamWaves<STAGE>::WAVES * 64, 1) void k_grouped_g
   }
 
   if (STAGE == 1) {
-    uint16_t* out = static_cast<uint16_t*>(g.out);
+    uint16_t* out = static_cast<uint16_t*>(sh ? g.sh_out : g.out);
 #pragma unroll
     for (int mi = 0; mi < SMI; ++mi)
 #pragma unroll
@@ -489,7 +492,8 @@ __global__ __launch_bounds__(StreamWaves<STAGE>::WAVES * 64, 1) void k_grouped_g
       if (frow == 0) s_amax[wn * SBM + wm * SWR + mi * 32 + item_row(r)] = m;
     }
   __syncthreads();
-  uint8_t* out = static_cast<uint8_t*>(g.out);
+  uint8_t* out = static_cast<uint8_t*>(sh ? g.sh_out : g.out);
+  float* out_scales = sh ? g.sh_out_scales : g.out_scales;
 #pragma unroll
   for (int mi = 0; mi < SMI; ++mi)
 #pragma unroll
@@ -501,39 +505,42 @@ __global__ __launch_bounds__(StreamWaves<STAGE>::WAVES * 64, 1) void k_grouped_g
       const float inv = amax > 0.f ? 448.0f / amax : 1.0f;
       if (row < tc.row_end) {
         out[(size_t)row * NCOLS + n0 + wn * 32 + frow] = (uint8_t)f32_to_e4m3(h[mi][r] * inv);
-        if (wn == 0 && frow == 0) g.out_scales[(size_t)row * NT + tc.n_tile] = amax > 0.f ? amax / 448.0f : 1.0f;
+        if (wn == 0 && frow == 0) out_scales[(size_t)row * NT + tc.n_tile] = amax > 0.f ? amax / 448.0f : 1.0f;
       }
     }
 }
 
 template <int STAGE>
-hipError_t launch_stream(const GroupedGemmArgs& g, int groups, int rows, int nt, hipStream_t s) {
+hipError_t launch_stream(const GroupedGemmArgs& g, hipStream_t s) {
   const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&k_grouped_gemm_fp8_stream<STAGE>), SLDS);
   if (e != hipSuccess) return e;
-  k_grouped_gemm_fp8_stream<STAGE><<<grouped_grid(rows, groups, SBM, nt), StreamWaves<STAGE>::WAVES * 64, SLDS, s>>>(g);
+  const unsigned grid = grouped_grid(g, gemm_groups(g, STAGE, STAGE == 0 ? SBNB / 2 : SBNB), SBM);
+  k_grouped_gemm_fp8_stream<STAGE><<<grid, StreamWaves<STAGE>::WAVES * 64, SLDS, s>>>(g);
   return hipGetLastError();
 }
 
 }  // namespace
 
+bool fp8_streams(const GroupedGemmArgs& g) {
+  // up to ~256 rows per group weight streaming dominates (routed experts); the shared expert's gate/up
+  // (every token, one group) also runs faster on the streaming kernel, its down stage on the
+  // register-staged one once the batch passes 256 tokens.  A launch that carries both streams only
+  // when each part would on its own (every group keeps the kernel, and the bits, of its own launch).
+  if (g.row_invariant || (g.stage == 1 && g.H % SBNB != 0)) return false;
+  auto kd_fits = [&](int I) { return (g.stage == 0 ? g.H : I) <= 128 * SMAXKB; };
+  const bool routed = (long)g.P <= 256L * g.E && kd_fits(g.I);
+  const bool shared = (g.stage == 0 || g.N <= 256) && kd_fits(g.Is);
+  if (g.shared) return shared;
+  return routed && (!g.with_shared || shared);
+}
+
 hipError_t launch_grouped_gemm_fp8(const GroupedGemmArgs& g, hipStream_t s) {
-  const int groups = g.shared ? 1 : g.E;
-  const int rows = g.shared ? g.N : g.P;
-  if (rows == 0) return hipSuccess;
-  // up to ~256 rows per group weight streaming dominates (routed experts); the shared expert's
-  // gate/up (every token, one group) also runs faster on the streaming kernel, its down stage on
-  // the register-staged one
-  const int kd = g.stage == 0 ? g.H : g.I;
-  if (!g.row_invariant && (rows <= 256L * groups || (g.shared && g.stage == 0)) && kd <= 128 * SMAXKB &&
-      (g.stage == 0 || g.H % SBNB == 0))
-    return g.stage == 0 ? launch_stream<0>(g, groups, rows, g.I / (SBNB / 2), s)
-                        : launch_stream<1>(g, groups, rows, g.H / SBNB, s);
+  if (g.N == 0) return hipSuccess;
+  if (fp8_streams(g)) return g.stage == 0 ? launch_stream<0>(g, s) : launch_stream<1>(g, s);
   if (g.stage == 0) {
-    const unsigned grid = grouped_grid(rows, groups, BM, g.I / BN);
-    k_grouped_gemm_fp8<0><<<grid, 256, 0, s>>>(g);
+    k_grouped_gemm_fp8<0><<<grouped_grid(g, gemm_groups(g, 0, BN), BM), 256, 0, s>>>(g);
   } else {
-    const unsigned grid = grouped_grid(rows, groups, BM, g.H / BN);
-    k_grouped_gemm_fp8<1><<<grid, 256, 0, s>>>(g);
+    k_grouped_gemm_fp8<1><<<grouped_grid(g, gemm_groups(g, 1, BN), BM), 256, 0, s>>>(g);
   }
   return hipGetLastError();
 }

@@ -93,13 +93,13 @@ __global__ __launch_bounds__(MxShape<STAGE>::WAVES * 64, STAGE == 0 ? 1 : 2) voi
   int* s_prefix = reinterpret_cast<int*>(smem);     // scheduler scratch, dead before the first load
   int* s_wsum = s_prefix + kMaxGroups + 1;
 
-  const int KD = STAGE == 0 ? g.H : g.I;
-  const int NCOLS = STAGE == 0 ? g.I : g.H;
-  const int NT = NCOLS / BN;
-  const int KB = KD / BK;
-  const TileCoord tc =
-      schedule_tile(g.offsets, g.shared ? 1 : g.E, g.shared ? g.N : -1, BM, NT, s_prefix, s_wsum);
+  const Groups G = gemm_groups(g, STAGE, BN);
+  const TileCoord tc = schedule_tile(G, BM, s_prefix, s_wsum);
   if (tc.expert < 0) return;  // the same decision in every thread
+  const bool sh = tc.expert == G.nr;  // the shared expert's group
+  const int KD = STAGE == 0 ? g.H : (sh ? g.Is : g.I);
+  const int NCOLS = STAGE == 0 ? (sh ? g.Is : g.I) : g.H;
+  const int KB = KD / BK;
   __syncthreads();            // every wave is done with the scheduler scratch before the loads reuse it
 
   const int tid = threadIdx.x, lane = tid % kWave;
@@ -109,13 +109,13 @@ __global__ __launch_bounds__(MxShape<STAGE>::WAVES * 64, STAGE == 0 ? 1 : 2) voi
   const uint8_t *wa, *wb = nullptr;      // packed codes [rows, KD/2]
   const uint8_t *sa_w, *sb_w = nullptr;  // E8M0 codes [rows, KD/32]
   if (STAGE == 0) {
-    wa = static_cast<const uint8_t*>(g.shared ? g.sh_gate : g.w_gate[tc.expert]);
-    wb = static_cast<const uint8_t*>(g.shared ? g.sh_up : g.w_up[tc.expert]);
-    sa_w = reinterpret_cast<const uint8_t*>(g.shared ? g.sh_gate_s : g.s_gate[tc.expert]);
-    sb_w = reinterpret_cast<const uint8_t*>(g.shared ? g.sh_up_s : g.s_up[tc.expert]);
+    wa = static_cast<const uint8_t*>(sh ? g.sh_gate : g.w_gate[tc.expert]);
+    wb = static_cast<const uint8_t*>(sh ? g.sh_up : g.w_up[tc.expert]);
+    sa_w = reinterpret_cast<const uint8_t*>(sh ? g.sh_gate_s : g.s_gate[tc.expert]);
+    sb_w = reinterpret_cast<const uint8_t*>(sh ? g.sh_up_s : g.s_up[tc.expert]);
   } else {
-    wa = static_cast<const uint8_t*>(g.shared ? g.sh_down : g.w_down[tc.expert]);
-    sa_w = reinterpret_cast<const uint8_t*>(g.shared ? g.sh_down_s : g.s_down[tc.expert]);
+    wa = static_cast<const uint8_t*>(sh ? g.sh_down : g.w_down[tc.expert]);
+    sa_w = reinterpret_cast<const uint8_t*>(sh ? g.sh_down_s : g.s_down[tc.expert]);
   }
   auto weight_row = [&](int r, const uint8_t* base_a, const uint8_t* base_b, size_t row_bytes) {
     if (STAGE == 0) return r < BN ? base_a + (size_t)(n0 + r) * row_bytes : base_b + (size_t)(n0 + r - BN) * row_bytes;
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(MxShape<STAGE>::WAVES * 64, STAGE == 0 ? 1 : 2) voi
   auto a_row = [&](int trow) {  // the x / h row behind tile row trow
     int p = tc.row0 + trow;
     if (p >= tc.row_end) p = tc.row_end - 1;  // rows past the segment are computed, never stored
-    return STAGE == 0 ? (g.shared ? (long)p : (long)(g.sorted_ids[p] / g.K)) : (long)p;
+    return STAGE == 0 ? (sh ? (long)p : (long)(g.sorted_ids[p] / g.K)) : (long)p;
   };
 
   // Load sources.  A: instruction i of wave w writes tile rows 8 (4 w + i) .. + 7, lane l row
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(MxShape<STAGE>::WAVES * 64, STAGE == 0 ? 1 : 2) voi
   // chunk (l % 4) ^ ((row / 4) % 4).  A fragment read serves 16 lanes (16 consecutive rows, one
   // chunk) per LDS cycle; these swizzles put them in 16 different 16-byte bank groups.  Scales: 4-byte pieces, the weight rows' E8M0 words (gate/up: 64 rows per
   // wave; down: 32) and the activation rows' fp32 scales (32 rows per wave), row r at 4 r.
-  const uint8_t* a_src = static_cast<const uint8_t*>(g.a);
+  const uint8_t* a_src = static_cast<const uint8_t*>(sh ? g.sh_a : g.a);
   const uint8_t* a_ptr[S::A_DMA];
 #pragma unroll
   for (int i = 0; i < S::A_DMA; ++i) {
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(MxShape<STAGE>::WAVES * 64, STAGE == 0 ? 1 : 2) voi
   const uint8_t* bs_ptr = weight_row(bs_lane ? wave * bs_rows + lane : 0, sa_w, sb_w, (size_t)KD / 32);
   const int as_rows = BM / S::WAVES;  // activation-scale rows per wave
   const bool as_lane = lane < as_rows;
-  const float* as_ptr = g.a_scales + (size_t)a_row(as_lane ? wave * as_rows + lane : 0) * KB;
+  const float* as_ptr = (sh ? g.sh_a_scales : g.a_scales) + (size_t)a_row(as_lane ? wave * as_rows + lane : 0) * KB;
 
   auto issue = [&](int buf, int kb) {
     uint8_t* sa = smem + buf * S::SBYTES;
@@ -255,7 +255,7 @@ __global__ __launch_bounds__(MxShape<STAGE>::WAVES * 64, STAGE == 0 ? 1 : 2) voi
   }
 
   if (STAGE == 1) {
-    uint16_t* out = static_cast<uint16_t*>(g.out);
+    uint16_t* out = static_cast<uint16_t*>(sh ? g.sh_out : g.out);
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -290,7 +290,8 @@ __global__ __launch_bounds__(MxShape<STAGE>::WAVES * 64, STAGE == 0 ? 1 : 2) voi
       if ((lane & 31) == 0) s_amax[wn * BM + wm * WR + mi * 32 + item_row(r)] = m;
     }
   __syncthreads();
-  uint8_t* out = static_cast<uint8_t*>(g.out);
+  uint8_t* out = static_cast<uint8_t*>(sh ? g.sh_out : g.out);
+  float* out_scales = sh ? g.sh_out_scales : g.out_scales;
   const int groups = NCOLS / 128;
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
@@ -308,7 +309,7 @@ __global__ __launch_bounds__(MxShape<STAGE>::WAVES * 64, STAGE == 0 ? 1 : 2) voi
           const int col = n0 + wn * WC + ni * 32 + (lane % 32);
           out[(size_t)row * NCOLS + col] = (uint8_t)f32_to_e4m3(h[mi][r][ni] * inv);
         }
-        if (wn == 0 && (lane & 31) == 0) g.out_scales[(size_t)row * groups + tc.n_tile] = amax > 0.f ? amax / 448.0f : 1.0f;
+        if (wn == 0 && (lane & 31) == 0) out_scales[(size_t)row * groups + tc.n_tile] = amax > 0.f ? amax / 448.0f : 1.0f;
       }
     }
 }
@@ -316,17 +317,15 @@ __global__ __launch_bounds__(MxShape<STAGE>::WAVES * 64, STAGE == 0 ? 1 : 2) voi
 }  // namespace
 
 hipError_t launch_grouped_gemm_mxfp4(const GroupedGemmArgs& g, hipStream_t s) {
-  const int groups = g.shared ? 1 : g.E;
-  const int rows = g.shared ? g.N : g.P;
-  if (rows == 0) return hipSuccess;
+  if (g.N == 0) return hipSuccess;
   if (g.stage == 0) {
     const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&k_grouped_gemm_mxfp4<0>), MxShape<0>::LDS);
     if (e != hipSuccess) return e;
-    k_grouped_gemm_mxfp4<0><<<grouped_grid(rows, groups, BM, g.I / BN), MxShape<0>::WAVES * 64, MxShape<0>::LDS, s>>>(g);
+    k_grouped_gemm_mxfp4<0><<<grouped_grid(g, gemm_groups(g, 0, BN), BM), MxShape<0>::WAVES * 64, MxShape<0>::LDS, s>>>(g);
   } else {
     const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&k_grouped_gemm_mxfp4<1>), MxShape<1>::LDS);
     if (e != hipSuccess) return e;
-    k_grouped_gemm_mxfp4<1><<<grouped_grid(rows, groups, BM, g.H / BN), MxShape<1>::WAVES * 64, MxShape<1>::LDS, s>>>(g);
+    k_grouped_gemm_mxfp4<1><<<grouped_grid(g, gemm_groups(g, 1, BN), BM), MxShape<1>::WAVES * 64, MxShape<1>::LDS, s>>>(g);
   }
   return hipGetLastError();
 }

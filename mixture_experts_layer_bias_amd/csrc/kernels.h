@@ -42,8 +42,10 @@ hipError_t launch_quant_fp8(const uint16_t* x, uint8_t* xq, float* xs, int rows,
 // a5 / a6: grouped expert GEMMs
 struct GroupedGemmArgs {
   int stage;   // 0: gate/up + SwiGLU, 1: down
-  int shared;  // 1: the shared expert over all N rows (identity row map, direct weights)
-  int N, H, I, K, E;  // I is the expert's intermediate size (Is for the shared expert)
+  int shared;  // 1: only the shared expert, over all N rows (identity row map, direct weights)
+  int with_shared;  // 1: the routed experts and, as one more group (index E), the shared expert
+  int N, H, I, K, E;  // I: the routed experts' intermediate size (the shared one's when `shared`)
+  int Is;             // the shared expert's intermediate size (with_shared or shared)
   int P;               // N*K (routed) or N (shared): upper bound of rows
   const void* a;        // gate/up: x [N,H] (bf16 or e4m3); down: h [rows, I]
   const float* a_scales;  // fp8 only
@@ -63,6 +65,12 @@ struct GroupedGemmArgs {
   const float* sh_down_s;
   void* out;           // gate/up: h [rows, I] (bf16 or e4m3); down: y [rows, H] bf16
   float* out_scales;   // fp8 gate/up only: [rows, I/128]
+  // the shared group's operands (shared or with_shared): A rows are tokens (gate/up: x, as `a`; down:
+  // its h [N, Is]), outputs at the token's row (gate/up: h [N, Is]; down: y [N, H])
+  const void* sh_a;
+  const float* sh_a_scales;
+  void* sh_out;
+  float* sh_out_scales;
   int row_invariant;   // 1: only the kernels whose per-row arithmetic is the same at any row count
 };
 hipError_t launch_grouped_gemm_bf16(const GroupedGemmArgs& g, hipStream_t s);
@@ -97,6 +105,8 @@ hipError_t launch_decode_fused(const GroupedGemmArgs& gu, const GroupedGemmArgs&
                                int32_t* sync, hipStream_t s);
 
 hipError_t launch_grouped_gemm_fp8(const GroupedGemmArgs& g, hipStream_t s);
+// whether launch_grouped_gemm_fp8 takes the streaming kernel for g (else the register-staged one)
+bool fp8_streams(const GroupedGemmArgs& g);
 // MXFP4 weights (packed E2M1 [rows, K/2], E8M0 scales [rows, K/32] in the s_* / sh_*_s pointers)
 hipError_t launch_grouped_gemm_mxfp4(const GroupedGemmArgs& g, hipStream_t s);
 
