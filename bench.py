@@ -302,7 +302,7 @@ def measure(name: str, args) -> dict:
     alg = {
         "experts": (3 * w_touched + 3 * sh_w + 2 * N * H * 2, 6.0 * p_r * H * I + 6.0 * N * H * Is,
                     "routed gate/up + SwiGLU, down, unpermute-reduce (one launch)"
-                    + (" after the shared expert's two GEMMs" if Is else "")),
+                    + (", shared expert as one more group" if Is else "")),
         "gate_up": (2 * w_touched + N * H * abytes + p_r * I * abytes, 4.0 * p_r * H * I,
                     "routed grouped gate/up + SwiGLU"),
         "down": (w_touched + p_r * I * abytes + p_r * H * 2, 2.0 * p_r * H * I, "routed grouped down"),
