@@ -4,12 +4,14 @@
 // allocates or synchronises.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
+#include <random>
 #include <set>
 #include <utility>
 
@@ -36,6 +38,16 @@ hipError_t ensure_dynamic_lds(const void* kernel, int bytes) {
 namespace {
 
 thread_local char g_err[512] = "";
+
+// A nonzero value per launch of the one-launch decode prelude, different from the previous launch's
+// (a process-wide counter from a random start, so a workspace's leftover flags are not mistaken for it).
+int next_route_seq() {
+  static std::atomic<uint32_t> ctr{std::random_device{}()};
+  for (;;) {
+    const uint32_t v = ctr.fetch_add(1, std::memory_order_relaxed) + 1u;
+    if (v != 0) return (int)v;
+  }
+}
 
 moe_status_t fail(moe_status_t st, const char* fmt, ...) {
   va_list ap;
@@ -567,18 +579,24 @@ moe_status_t moe_forward(const moe_config_t* cfg, const moe_weights_t* w, const 
   int32_t* hist = static_cast<int32_t*>(at(L.scratch));
   const int P = c.num_tokens * c.top_k;
   int32_t* sync = static_cast<int32_t*>(at(L.sync));
-  // small batch: router GEMM, then top-K and the sort in one block, which also zeroes the counters
-  // and the error word of the one-launch decode experts path
+  // small batch: router GEMM, then top-K and the sort in one block (both in one launch for decode
+  // batches), which also zeroes the counters and the error word of the one-launch decode experts path
   const bool small = moe::topk_sort_small_fits(c.num_tokens, c.top_k);
   const bool fused = small && experts_fused(cfg);
-  if (small) {
+  if (small && c.row_invariant == 0 && moe::route_small_fits(c.num_tokens, c.top_k, c.router_width)) {
+    // decode: router GEMV, top-K and the sort in one launch
+    MOE_HIP(moe::launch_route_small(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w->router_w),
+                                    logits, w->correction_bias, ids, tw, zw, counts, offsets, sorted_ids, inv_perm,
+                                    sync, fused, next_route_seq(), c.num_tokens, c.hidden, c.router_width,
+                                    c.num_experts, c.top_k, c.scoring, c.renormalize, c.routed_scale, s));
+  } else if (small) {
     const bool inv = c.row_invariant != 0;
     const int slices = moe::router_slices(c.num_tokens, c.hidden, c.router_width, inv);
     float* part = slices > 1 ? reinterpret_cast<float*>(hist) : logits;
     MOE_HIP(moe::launch_router_logits(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w->router_w),
                                       part, c.num_tokens, c.hidden, c.router_width, slices, inv, s));
     MOE_HIP(moe::launch_topk_sort_small(part, slices, logits, w->correction_bias, ids, tw, zw, counts, offsets,
-                                        sorted_ids, inv_perm, fused ? sync : nullptr, moe::kSyncInts, c.num_tokens,
+                                        sorted_ids, inv_perm, fused ? sync : nullptr, moe::kSyncRouteFlags, c.num_tokens,
                                         c.router_width, c.num_experts, c.top_k, c.scoring, c.renormalize,
                                         c.routed_scale, s));
   } else {

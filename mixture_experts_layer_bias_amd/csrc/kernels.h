@@ -31,6 +31,18 @@ hipError_t launch_topk_sort_small(const float* part, int slices, float* logits, 
                                   int32_t* inv_perm, int32_t* done, int done_len, int N, int R, int E, int K,
                                   int scoring, int renormalize, float routed_scale, hipStream_t s);
 
+// a1 + a2 + a3 for decode batches (route_small_fits: N <= 8, N*K <= 64, R <= 1024, not row-invariant):
+// router GEMV, top-K and the sort in one launch, with the same results as launch_router_logits (one
+// slice) + launch_topk_sort_small.  sync: the workspace's sync piece (kSyncInts int32; its route flags
+// may hold anything but `seq`); seq: nonzero, different from the last launch's on this sync piece.
+// zero_counters: also zero sync[0, kSyncRouteFlags) for a following one-launch decode.
+bool route_small_fits(int N, int K, int R);
+hipError_t launch_route_small(const uint16_t* x, const uint16_t* router_w, float* logits, const float* bias,
+                              int32_t* ids, float* w, float* zero_w, int32_t* counts, int32_t* offsets,
+                              int32_t* sorted_ids, int32_t* inv_perm, int32_t* sync, bool zero_counters, int seq,
+                              int N, int H, int R, int E, int K, int scoring, int renormalize, float routed_scale,
+                              hipStream_t s);
+
 // a3: stable counting sort by expert; hist is [(permute_chunks(P) + 1) * R] int32 scratch
 int permute_chunks(int P);
 hipError_t launch_permute(const int32_t* ids, int P, int R, int32_t* counts, int32_t* offsets, int32_t* sorted_ids,
@@ -96,7 +108,9 @@ constexpr int kSyncColTiles = 1024;     // [kSyncMaxColTiles]: down tiles finish
 constexpr int kSyncMaxColTiles = 512;   // so the path takes H <= 65536
 constexpr int kSyncReduced = 1536;      // column blocks reduced
 constexpr int kSyncError = 1537;        // set to 1 when a bounded wait expires; the launch never clears it
-constexpr int kSyncInts = 1538;
+constexpr int kSyncRouteFlags = 1538;   // [kSyncRouteMaxFlags]: the one-launch decode prelude's block flags
+constexpr int kSyncRouteMaxFlags = 128;
+constexpr int kSyncInts = kSyncRouteFlags + kSyncRouteMaxFlags;
 // Routed gate/up, down and the unpermute-reduce of a decode layer in one launch (the shared expert,
 // if any, must already be in r.shared_y).  sync: kSyncInts int32 whose counters hold zeros when the
 // launch starts; the launch leaves them zero (and sets sync[kSyncError] if a wait expired).

@@ -8,6 +8,7 @@
 // bias with the zero-expert fold; the DeepSeek-V4 sqrtsoftplus + correction
 // bias arm, weighted like the sigmoid one).
 #include "common.h"
+#include "dma.h"
 #include "kernels.h"
 
 namespace moe {
@@ -110,14 +111,13 @@ __device__ __forceinline__ void bf16x8_to_f32(const u32x4& v, float* f) {
   }
 }
 
+// The calling wave's router column r against the N tokens: acc[t] gets this lane's partial sum of
+// token t (wave_sum of it is the logit).
 template <int NT, int G>  // NT >= N tokens, G chunks per lane in flight
-__global__ __launch_bounds__(256) void k_router_gemv(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
-                                                     float* __restrict__ logits, int N, int H, int R) {
+__device__ __forceinline__ void gemv_column(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int N,
+                                            int H, int r, float* acc) {
   const int lane = threadIdx.x % kWave;
-  const int r = blockIdx.x * 4 + threadIdx.x / kWave;
-  if (r >= R) return;  // the whole wave leaves
   const int nch = H / 8;
-  float acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = 0.f;
   for (int c0 = lane; c0 < nch; c0 += G * kWave) {
@@ -143,6 +143,16 @@ __global__ __launch_bounds__(256) void k_router_gemv(const uint16_t* __restrict_
       }
     }
   }
+}
+
+template <int NT, int G>
+__global__ __launch_bounds__(256) void k_router_gemv(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+                                                     float* __restrict__ logits, int N, int H, int R) {
+  const int lane = threadIdx.x % kWave;
+  const int r = blockIdx.x * 4 + threadIdx.x / kWave;
+  if (r >= R) return;  // the whole wave leaves
+  float acc[NT];
+  gemv_column<NT, G>(x, wr, N, H, r, acc);
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     if (t < N) {  // uniform
@@ -175,8 +185,9 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 
 // Scores and top-K of token t for the calling wave.  p_w is this wave's LDS row
 // of MAXJ*64 floats.  Returns the wave's slot id (lane k holds slot k's column;
-// lanes >= K hold 0) after writing ids / w / zero_w for the token.
-template <int MAXJ>
+// lanes >= K hold 0) after writing ids / w / zero_w for the token.  DEV: whole logits (nslices == 1)
+// written in the same launch by other blocks with device-scope stores, read at device scope.
+template <int MAXJ, bool DEV = false>
 __device__ __forceinline__ int topk_token(const float* __restrict__ part, int nslices, float* __restrict__ logits,
                                           const float* __restrict__ bias, int32_t* __restrict__ ids,
                                           float* __restrict__ w, float* __restrict__ zero_w, float* p_w, int t, int N,
@@ -188,7 +199,8 @@ __device__ __forceinline__ int topk_token(const float* __restrict__ part, int ns
   for (int j = 0; j < MAXJ; ++j) {
     const int r = lane + 64 * j;
     if (r < R && nslices == 1) {  // whole logits (the GEMV router): one load
-      v[j] = part[(size_t)t * R + r];
+      v[j] = DEV ? __hip_atomic_load(part + (size_t)t * R + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                 : part[(size_t)t * R + r];
     } else if (r < R) {
       // all planes are loaded before the (in-order) additions, so the loads overlap
       float pl[16];
@@ -300,6 +312,63 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ part, in
   topk_token<MAXJ>(part, nslices, logits, bias, ids, w, zero_w, p_lds[wave], t, N, R, E, K, scoring, renorm, scale);
 }
 
+// The stable counting sort of up to 64 expanded rows, by one wave: s_ids (LDS) holds the P <= 64 row
+// ids, s_off (LDS) at least R ints, zero on entry.  Lane p holds row p's id v; one ballot per id bit,
+// from the top, splits the rows into those with a smaller id (lt) and those with the same id (eq), so
+// row p lands at |lt| + |{q in eq : q < p}|.
+__device__ __forceinline__ void sort_rows_ballot(const int* s_ids, int* s_off, int P, int R, int32_t* counts,
+                                                 int32_t* offsets, int32_t* sorted_ids, int32_t* inv_perm) {
+  const int lane = threadIdx.x % kWave;
+  const bool valid = lane < P;
+  const int v = valid ? s_ids[lane] : 0;
+  uint64_t eq = __ballot(valid), lt = 0;
+  for (int b = 31 - __builtin_clz((unsigned)R); b >= 0; --b) {  // ids < R fit in these bits
+    const bool bit = (v >> b) & 1;
+    const uint64_t ones = __ballot(valid && bit);
+    if (bit) {
+      lt |= eq & ~ones;
+      eq &= ones;
+    } else {
+      eq &= ~ones;
+    }
+  }
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));  // lanes before this one
+  const int rank = __popcll(eq & below);
+  if (valid) {
+    const int pos = __popcll(lt) + rank;
+    sorted_ids[pos] = lane;
+    inv_perm[lane] = pos;
+    if (rank == 0) s_off[v] = __popcll(eq);  // the expert's first row writes its count
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // exclusive scan of the R counts: lane l owns buckets [l C, l C + C)
+  const int C = (R + kWave - 1) / kWave;
+  int sum = 0;
+  for (int c = 0; c < C; ++c) {
+    const int r = lane * C + c;
+    if (r < R) sum += s_off[r];
+  }
+  int incl = sum;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int xo = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += xo;
+  }
+  int run = incl - sum;
+  for (int c = 0; c < C; ++c) {
+    const int r = lane * C + c;
+    if (r < R) {
+      const int cnt = s_off[r];
+      counts[r] = cnt;
+      offsets[r] = run;
+      run += cnt;
+    }
+  }
+  if (lane == kWave - 1) offsets[R] = incl;  // = P
+}
+
 // Small batches (N <= 64, N*K <= 1024): top-K of every token and the stable
 // counting sort by expert in ONE block of 16 waves, so a decode step spends one
 // launch on both (same results as k_topk followed by the three sort passes).
@@ -331,60 +400,8 @@ __global__ __launch_bounds__(1024) void k_topk_sort_small(const float* __restric
     if (lane < K) s_ids[t * K + lane] = my_id;
   }
   __syncthreads();
-  if (P <= kWave) {
-    // Up to 64 rows (decode): wave 0 sorts them with ballots.  Lane p holds row p's id v; one ballot
-    // per id bit, from the top, splits the rows into those with a smaller id (lt) and those with
-    // the same id (eq), so row p lands at |lt| + |{q in eq : q < p}|: the stable counting sort.
-    if (wave == 0) {
-      const bool valid = lane < P;
-      const int v = valid ? s_ids[lane] : 0;
-      uint64_t eq = __ballot(valid), lt = 0;
-      for (int b = 31 - __builtin_clz((unsigned)R); b >= 0; --b) {  // ids < R fit in these bits
-        const bool bit = (v >> b) & 1;
-        const uint64_t ones = __ballot(valid && bit);
-        if (bit) {
-          lt |= eq & ~ones;
-          eq &= ones;
-        } else {
-          eq &= ~ones;
-        }
-      }
-      const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));  // lanes before this one
-      const int rank = __popcll(eq & below);
-      if (valid) {
-        const int pos = __popcll(lt) + rank;
-        sorted_ids[pos] = lane;
-        inv_perm[lane] = pos;
-        if (rank == 0) s_off[v] = __popcll(eq);  // the expert's first row writes its count
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      // exclusive scan of the R counts: lane l owns buckets [l C, l C + C)
-      const int C = (R + kWave - 1) / kWave;
-      int sum = 0;
-      for (int c = 0; c < C; ++c) {
-        const int r = lane * C + c;
-        if (r < R) sum += s_off[r];
-      }
-      int incl = sum;
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const int xo = __shfl_up(incl, o, kWave);
-        if (lane >= o) incl += xo;
-      }
-      int run = incl - sum;
-      for (int c = 0; c < C; ++c) {
-        const int r = lane * C + c;
-        if (r < R) {
-          const int cnt = s_off[r];
-          counts[r] = cnt;
-          offsets[r] = run;
-          run += cnt;
-        }
-      }
-      if (lane == kWave - 1) offsets[R] = incl;  // = P
-    }
+  if (P <= kWave) {  // up to 64 rows (decode): wave 0 sorts them with ballots
+    if (wave == 0) sort_rows_ballot(s_ids, s_off, P, R, counts, offsets, sorted_ids, inv_perm);
     return;
   }
   // one expanded row per thread, in order
@@ -423,6 +440,109 @@ __global__ __launch_bounds__(1024) void k_topk_sort_small(const float* __restric
     sorted_ids[pos] = tid;
     inv_perm[tid] = pos;
   }
+}
+
+// The decode prelude in one launch (N <= 8 tokens, N K <= 64 rows, R <= 1024): router GEMV, top-K and
+// the sort, with the same results as k_router_gemv followed by k_topk_sort_small.  Every block of 8
+// waves computes 8 router columns (one per wave) and stores their logits at device scope.  Every block
+// but block 0 then waits for its stores and writes `seq` into its flag, sync[kSyncRouteFlags + b - 1];
+// block 0 waits (bounded) until every flag holds seq, puts the flags back to 0, and runs the top-K of
+// each token (one wave per token, logits read at device scope) and the ballot sort.  seq is a nonzero
+// value of this launch that differs from the last launch's on the same flags; flags are taken as set
+// only when they hold exactly seq, so the workspace may start with any contents.  With
+// zero_counters, block 0 also zeroes the counters and the error word of the one-launch decode experts
+// path that follows (sync[0, kSyncRouteFlags)).
+constexpr int kRouteSpinLimit = 1 << 20;
+
+template <int MAXJ, int NT, int G>
+__global__ __launch_bounds__(512) void k_route_small(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, float* __restrict__ logits,
+    const float* __restrict__ bias, int32_t* __restrict__ ids, float* __restrict__ w, float* __restrict__ zero_w,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_ids,
+    int32_t* __restrict__ inv_perm, int32_t* __restrict__ sync, int zero_counters, int seq, int N, int H, int R,
+    int E, int K, int scoring, int renorm, float scale) {
+  __shared__ float p_lds[8][MAXJ * 64];
+  __shared__ int s_ids[64];
+  __shared__ int s_off[1024];
+  __shared__ int s_expired;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int r = blockIdx.x * 8 + wave;
+  if (r < R) {  // wave-uniform
+    float acc[NT];
+    gemv_column<NT, G>(x, wr, N, H, r, acc);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (t < N) {  // uniform
+        const float v = wave_sum(acc[t]);
+        if (lane == 0) __hip_atomic_store(logits + (size_t)t * R + r, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+  dma_wait<0>();  // this wave's logit stores are complete (device scope)
+  if (blockIdx.x != 0) {
+    __syncthreads();  // ... and every other wave's
+    if (tid == 0)
+      __hip_atomic_store(sync + kSyncRouteFlags + blockIdx.x - 1, seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  if (tid == 0) s_expired = 0;
+  for (int i = tid; i < R; i += 512) s_off[i] = 0;
+  __syncthreads();
+  if (tid >= 1 && tid < (int)gridDim.x) {
+    int* flag = sync + kSyncRouteFlags + tid - 1;
+    bool ready = false;
+    for (int it = 0; it < kRouteSpinLimit && !ready; ++it) {
+      ready = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == seq;
+      if (!ready) __builtin_amdgcn_s_sleep(1);
+    }
+    if (!ready) s_expired = 1;
+    __hip_atomic_store(flag, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (zero_counters)
+    for (int i = tid; i < kSyncRouteFlags; i += 512) sync[i] = 0;
+  __syncthreads();
+  if (tid == 0 && s_expired)  // after the zeroing above: this launch's output is undefined
+    __hip_atomic_store(sync + kSyncError, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (wave < N) {
+    const int my_id = topk_token<MAXJ, true>(logits, 1, logits, bias, ids, w, zero_w, p_lds[wave], wave, N, R, E, K,
+                                             scoring, renorm, scale);
+    if (lane < K) s_ids[wave * K + lane] = my_id;
+  }
+  __syncthreads();
+  if (wave == 0) sort_rows_ballot(s_ids, s_off, N * K, R, counts, offsets, sorted_ids, inv_perm);
+}
+
+bool route_small_fits(int N, int K, int R) { return N <= RG_MAXN && N * K <= kWave && R <= 8 * kSyncRouteMaxFlags; }
+
+hipError_t launch_route_small(const uint16_t* x, const uint16_t* router_w, float* logits, const float* bias,
+                              int32_t* ids, float* w, float* zero_w, int32_t* counts, int32_t* offsets,
+                              int32_t* sorted_ids, int32_t* inv_perm, int32_t* sync, bool zero_counters, int seq,
+                              int N, int H, int R, int E, int K, int scoring, int renormalize, float routed_scale,
+                              hipStream_t s) {
+  if (N == 0) return hipSuccess;
+  if (!route_small_fits(N, K, R) || seq == 0) return hipErrorInvalidValue;
+  const unsigned blocks = (unsigned)((R + 7) / 8);
+  const int maxj = (R + 63) / 64;
+#define MOE_ROUTE_CASE(J)                                                                                        \
+  case J:                                                                                                        \
+    if (N <= 4)                                                                                                  \
+      k_route_small<J, 4, 4><<<blocks, 512, 0, s>>>(x, router_w, logits, bias, ids, w, zero_w, counts, offsets,  \
+                                                    sorted_ids, inv_perm, sync, zero_counters, seq, N, H, R, E,   \
+                                                    K, scoring, renormalize, routed_scale);                       \
+    else                                                                                                         \
+      k_route_small<J, 8, 2><<<blocks, 512, 0, s>>>(x, router_w, logits, bias, ids, w, zero_w, counts, offsets,  \
+                                                    sorted_ids, inv_perm, sync, zero_counters, seq, N, H, R, E,   \
+                                                    K, scoring, renormalize, routed_scale);                       \
+    break;
+  switch (maxj <= 2 ? maxj : (maxj <= 4 ? 4 : (maxj <= 6 ? 6 : 16))) {
+    MOE_ROUTE_CASE(1)
+    MOE_ROUTE_CASE(2)
+    MOE_ROUTE_CASE(4)
+    MOE_ROUTE_CASE(6)
+    MOE_ROUTE_CASE(16)
+  }
+#undef MOE_ROUTE_CASE
+  return hipGetLastError();
 }
 
 int router_slices(int N, int H, int R, bool row_invariant) {
