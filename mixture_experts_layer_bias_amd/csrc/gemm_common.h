@@ -65,16 +65,14 @@ __device__ __forceinline__ int group_rows(const Groups& G, int e) {
   return e == G.nr ? G.xr : 0;
 }
 
-// s_prefix must hold kMaxGroups + 1 ints in LDS (G.nr + (G.xr > 0) <= kMaxGroups).  Block of at least
-// 256 threads.  `b` is the block's tile slot (blockIdx.x unless one launch runs several grids of tiles).
-// split_align == 0: a segment's tiles start every BM rows, the last one ragged.  split_align > 0 (a
-// divisor of BM): the segment is cut into the same number of tiles, of ceil(rows / tiles) rows
-// rounded up to split_align, so its tiles carry nearly equal work (130 rows: 96 + 34, not 128 + 2).
-__device__ __forceinline__ TileCoord schedule_tile_at(const Groups& G, int BM, int* s_prefix, int* s_wsum, int b,
-                                                      int split_align = 0) {
+// The tile prefix of a launch's groups: s_prefix[e] = tiles (row tiles x column tiles) of the groups
+// before e, s_prefix[ngroups] = all tiles, which is returned to every thread.  s_prefix holds at least
+// ngroups + 1 ints of LDS (ngroups = G.nr + (G.xr > 0) <= kMaxGroups); block of at least 256 threads,
+// all of which call.
+__device__ __forceinline__ int tile_prefix(const Groups& G, int BM, int* s_prefix, int* s_wsum) {
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int ngroups = G.nr + (G.xr > 0 ? 1 : 0);
-  // each thread owns 4 consecutive groups; the prefix counts tiles (row tiles x column tiles)
+  // each thread owns 4 consecutive groups
   int cnt[4], local = 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -102,14 +100,17 @@ __device__ __forceinline__ TileCoord schedule_tile_at(const Groups& G, int BM, i
   }
   if (tid == 0) s_prefix[ngroups] = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
   __syncthreads();
+  return s_prefix[ngroups];
+}
 
-  const int T = s_prefix[ngroups];
+// The tile at logical index L of a launch whose tile prefix is s_prefix (T tiles in all; L < T).
+// split_align == 0: a segment's tiles start every BM rows, the last one ragged.  split_align > 0 (a
+// divisor of BM): the segment is cut into the same number of tiles, of ceil(rows / tiles) rows
+// rounded up to split_align, so its tiles carry nearly equal work (130 rows: 96 + 34, not 128 + 2).
+__device__ __forceinline__ TileCoord tile_at(const Groups& G, int BM, const int* s_prefix, int T, int L,
+                                             int split_align = 0) {
+  const int ngroups = G.nr + (G.xr > 0 ? 1 : 0);
   TileCoord tc{-1, 0, 0, 0, 0, G.nt == G.xnt || G.xr == 0 ? T / G.nt : -1};
-  const int chunk = (T + 7) / 8;
-  const int local_idx = b / 8;
-  if (local_idx >= chunk) return tc;
-  const int L = (b % 8) * chunk + local_idx;
-  if (L >= T) return tc;
   // largest e with s_prefix[e] <= L
   int lo = 0, hi = ngroups - 1;
   while (lo < hi) {
@@ -135,6 +136,19 @@ __device__ __forceinline__ TileCoord schedule_tile_at(const Groups& G, int BM, i
   tc.row0 = seg0 + tc.m_tile * rpt;
   tc.row_end = min(tc.row0 + rpt, seg_end);
   return tc;
+}
+
+// The tile of block slot `b` (blockIdx.x unless one launch runs several grids of tiles), or expert -1
+// when the slot has none: tile_prefix, then the XCD-aware map of slots to logical tiles.  s_prefix must
+// hold kMaxGroups + 1 ints in LDS.
+__device__ __forceinline__ TileCoord schedule_tile_at(const Groups& G, int BM, int* s_prefix, int* s_wsum, int b,
+                                                      int split_align = 0) {
+  const int T = tile_prefix(G, BM, s_prefix, s_wsum);
+  const int chunk = (T + 7) / 8;
+  const int local_idx = b / 8;
+  const int L = (b % 8) * chunk + local_idx;
+  if (local_idx >= chunk || L >= T) return TileCoord{-1, 0, 0, 0, 0, G.nt == G.xnt || G.xr == 0 ? T / G.nt : -1};
+  return tile_at(G, BM, s_prefix, T, L, split_align);
 }
 
 __device__ __forceinline__ TileCoord schedule_tile(const Groups& G, int BM, int* s_prefix, int* s_wsum,

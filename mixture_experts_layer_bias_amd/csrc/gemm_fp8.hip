@@ -477,37 +477,51 @@ __global__ __launch_bounds__(StreamWaves<STAGE>::WAVES * 64, 1) void k_grouped_g
     return;
   }
 
-  // gate/up epilogue: h = silu(g) * u, quantised per row over the tile's 128 columns
-  __syncthreads();  // the ring is free: s_amax is aliased onto it
-  float* s_amax = reinterpret_cast<float*>(smem);  // [wn][tile row]
-  float h[SMI][16];
+  // gate/up epilogue: h = silu(g) * u, quantised per row over the tile's 128 columns.  The h values
+  // go through LDS (the ring is free) so that each row is finished by the 8 threads that hold it:
+  // an amax over 8 lanes, and the codes leave as 4-byte stores.
+  __syncthreads();
+  constexpr int HSTRIDE = SBNB / 2 + 4;  // floats per LDS row (4 floats of padding: the two halves of a
+                                         // wave write rows 4 apart, which then fall on other banks)
+  float* h_lds = reinterpret_cast<float*>(smem);  // [SBM][HSTRIDE]
 #pragma unroll
   for (int mi = 0; mi < SMI; ++mi)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      h[mi][r] = silu(acc[mi][0][r]) * acc[mi][1][r];
-      float m = fabsf(h[mi][r]);
-#pragma unroll
-      for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));  // the 32 lanes of this row
-      if (frow == 0) s_amax[wn * SBM + wm * SWR + mi * 32 + item_row(r)] = m;
-    }
+    for (int r = 0; r < 16; ++r)
+      h_lds[(wm * SWR + mi * 32 + item_row(r)) * HSTRIDE + wn * 32 + frow] = silu(acc[mi][0][r]) * acc[mi][1][r];
   __syncthreads();
   uint8_t* out = static_cast<uint8_t*>(sh ? g.sh_out : g.out);
   float* out_scales = sh ? g.sh_out_scales : g.out_scales;
+  constexpr int TPR = W::WAVES * 64 / SBM;  // threads per row (8 for 16 waves)
+  constexpr int VPT = SBNB / 2 / TPR;        // values per thread
+  static_assert(TPR * VPT == SBNB / 2 && VPT % 4 == 0 && (TPR & (TPR - 1)) == 0, "row split");
+  const int trow = tid / TPR, seg = tid % TPR;
+  // thread seg of a row holds the float4 groups at columns 4 seg + 4 TPR i: the TPR threads of a row
+  // read one contiguous span per instruction
+  float v[VPT];
 #pragma unroll
-  for (int mi = 0; mi < SMI; ++mi)
+  for (int i = 0; i < VPT / 4; ++i) {
+    const f32x4 q = *reinterpret_cast<const f32x4*>(h_lds + trow * HSTRIDE + 4 * seg + 4 * TPR * i);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int trow = wm * SWR + mi * 32 + item_row(r);
-      const int row = tc.row0 + trow;
-      const float amax =
-          fmaxf(fmaxf(s_amax[trow], s_amax[SBM + trow]), fmaxf(s_amax[2 * SBM + trow], s_amax[3 * SBM + trow]));
-      const float inv = amax > 0.f ? 448.0f / amax : 1.0f;
-      if (row < tc.row_end) {
-        out[(size_t)row * NCOLS + n0 + wn * 32 + frow] = (uint8_t)f32_to_e4m3(h[mi][r] * inv);
-        if (wn == 0 && frow == 0) out_scales[(size_t)row * NT + tc.n_tile] = amax > 0.f ? amax / 448.0f : 1.0f;
-      }
+    for (int j = 0; j < 4; ++j) v[4 * i + j] = q[j];
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) amax = fmaxf(amax, fabsf(v[i]));
+#pragma unroll
+  for (int o = 1; o < TPR; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
+  const int row = tc.row0 + trow;
+  if (row < tc.row_end) {
+    const float inv = amax > 0.f ? 448.0f / amax : 1.0f;
+#pragma unroll
+    for (int i = 0; i < VPT / 4; ++i) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) word |= f32_to_e4m3(v[4 * i + j] * inv) << (8 * j);
+      *reinterpret_cast<uint32_t*>(out + (size_t)row * NCOLS + n0 + 4 * seg + 4 * TPR * i) = word;
     }
+    if (seg == 0) out_scales[(size_t)row * NT + tc.n_tile] = amax > 0.f ? amax / 448.0f : 1.0f;
+  }
 }
 
 template <int STAGE>

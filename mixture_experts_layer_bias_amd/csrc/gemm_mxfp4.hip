@@ -271,47 +271,55 @@ __global__ __launch_bounds__(MxShape<STAGE>::WAVES * 64, STAGE == 0 ? 1 : 2) voi
     return;
   }
 
-  // ---- gate/up epilogue: h = silu(g) * u, quantised per row over this tile's 128 columns
-  __syncthreads();  // every wave is past its last ring read: the per-row maxima reuse the ring
-  float* s_amax = reinterpret_cast<float*>(smem);  // [WN][BM]
-  float h[MI][16][NI];
+  // ---- gate/up epilogue: h = silu(g) * u, quantised per row over this tile's 128 columns.  The h
+  // values go through LDS (the ring is free) so that each row is finished by the threads that hold
+  // it: an amax over a few lanes, and the codes leave as 4-byte stores.
+  __syncthreads();  // every wave is past its last ring read
+  constexpr int HSTRIDE = BN + 4;  // floats per LDS row (4 of padding: rows 4 apart fall on other banks)
+  float* h_lds = reinterpret_cast<float*>(smem);  // [BM][HSTRIDE]
+  static_assert(BM * HSTRIDE * 4 <= S::LDS, "h fits in the ring");
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float m = 0.f;
+    for (int r = 0; r < 16; ++r)
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
-        h[mi][r][ni] = silu(acc[mi][ni][r]) * acc[mi][ni + NI][r];
-        m = fmaxf(m, fabsf(h[mi][r][ni]));
-      }
-#pragma unroll
-      for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));  // the row's 32 lanes
-      if ((lane & 31) == 0) s_amax[wn * BM + wm * WR + mi * 32 + item_row(r)] = m;
-    }
+      for (int ni = 0; ni < NI; ++ni)
+        h_lds[(wm * WR + mi * 32 + item_row(r)) * HSTRIDE + wn * WC + ni * 32 + (lane % 32)] =
+            silu(acc[mi][ni][r]) * acc[mi][ni + NI][r];
   __syncthreads();
   uint8_t* out = static_cast<uint8_t*>(sh ? g.sh_out : g.out);
   float* out_scales = sh ? g.sh_out_scales : g.out_scales;
   const int groups = NCOLS / 128;
+  constexpr int TPR = S::WAVES * 64 / BM;  // threads per row
+  constexpr int VPT = BN / TPR;            // values per thread
+  static_assert(TPR * VPT == BN && VPT % 4 == 0 && (TPR & (TPR - 1)) == 0 && TPR <= kWave, "row split");
+  const int trow = threadIdx.x / TPR, seg = threadIdx.x % TPR;
+  // thread seg of a row holds the float4 groups at columns 4 seg + 4 TPR i: the row's threads read one
+  // contiguous span per instruction
+  float v[VPT];
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi)
+  for (int i = 0; i < VPT / 4; ++i) {
+    const f32x4 q = *reinterpret_cast<const f32x4*>(h_lds + trow * HSTRIDE + 4 * seg + 4 * TPR * i);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int trow = wm * WR + mi * 32 + item_row(r);
-      const int row = tc.row0 + trow;
-      float amax = s_amax[trow];
+    for (int j = 0; j < 4; ++j) v[4 * i + j] = q[j];
+  }
+  float amax = 0.f;
 #pragma unroll
-      for (int w = 1; w < S::WN; ++w) amax = fmaxf(amax, s_amax[w * BM + trow]);
-      const float inv = amax > 0.f ? 448.0f / amax : 1.0f;
-      if (row < tc.row_end) {
+  for (int i = 0; i < VPT; ++i) amax = fmaxf(amax, fabsf(v[i]));
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni) {
-          const int col = n0 + wn * WC + ni * 32 + (lane % 32);
-          out[(size_t)row * NCOLS + col] = (uint8_t)f32_to_e4m3(h[mi][r][ni] * inv);
-        }
-        if (wn == 0 && (lane & 31) == 0) out_scales[(size_t)row * groups + tc.n_tile] = amax > 0.f ? amax / 448.0f : 1.0f;
-      }
+  for (int o = 1; o < TPR; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
+  const int row = tc.row0 + trow;
+  if (row < tc.row_end) {
+    const float inv = amax > 0.f ? 448.0f / amax : 1.0f;
+#pragma unroll
+    for (int i = 0; i < VPT / 4; ++i) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) word |= f32_to_e4m3(v[4 * i + j] * inv) << (8 * j);
+      *reinterpret_cast<uint32_t*>(out + (size_t)row * NCOLS + n0 + 4 * seg + 4 * TPR * i) = word;
     }
+    if (seg == 0) out_scales[(size_t)row * groups + tc.n_tile] = amax > 0.f ? amax / 448.0f : 1.0f;
+  }
 }
 
 }  // namespace

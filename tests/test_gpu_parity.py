@@ -436,9 +436,10 @@ def test_forward_matches_oracle_and_composed_stages(name):
     dl = mi.device.device_layer(wl)
     cfg, w = config_of(wl), weights_of(dl)
     L = moe.moe_workspace_layout(cfg)
-    # a workspace of garbage, except the decode path's counters, which every call leaves at zero
+    # a workspace of garbage, except the decode experts path's counters and error word, which every call
+    # leaves at zero (the decode routing launch's flags after them stay garbage)
     ws = torch.full((moe.moe_workspace_size(cfg),), 0xA5, dtype=torch.uint8, device="cuda")
-    ws[:L["logits"]].zero_()
+    ws[:L["sync_error"] + 4].zero_()
     out = torch.empty_like(dl.x)
     moe.moe_forward(cfg, w, dl.x, out, ws)
     torch.cuda.synchronize()
