@@ -41,14 +41,26 @@ HEADLINE = "prefill_zipf"
 CPU_SAMPLE_TOKENS = {"tiny": 16, "decode": 4, "prefill_zipf": 32, "fp8_sigmoid": 2, "zero_experts": 4,
                      "mxfp4_sigmoid": 2}
 
-# HBM traffic of a kernel per launch, from two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
-# WRITE_SIZE; KiB per dispatch averaged over the kernel's dispatches), each scaled by what the same
-# counter reads for a plain 1 GiB device copy (FETCH_SIZE reads half the bytes moved: x2.0; WRITE_SIZE
-# reads them all: x1.0).  An entry holds only while the kernel's sources hash to the value they had
-# when the counters were taken; otherwise the traffic is reported as null.
-_GEMM_SOURCES = ["mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h",
-                 "mixture_experts_layer_bias_amd/csrc/dma.h"]
-MEASURED_TRAFFIC = {}
+# HBM traffic of a kernel per launch, from two rocprofv3 --pmc runs of this script per workload
+# (`--workload W --steps 5 --warmup 1 --no-cpu-baseline --no-graph` under FETCH_SIZE, then WRITE_SIZE;
+# KiB per dispatch, averaged over the dispatches of the timed launch: the kernel's smallest grid, i.e.
+# the routed-only launch where the layer's own launch also carries the shared expert), each scaled by
+# what the same counter reads for a plain 1 GiB device copy (`--copy-bytes 1073741824 --steps 5`:
+# FETCH_SIZE reads half the bytes moved, so x2.0; WRITE_SIZE reads them all, x1.0).  An entry holds only
+# while its sources hash to the value they had when the counters were taken; otherwise the traffic is
+# reported as null.  The summaries the entries come from are in profiles/.
+MEASURED_TRAFFIC = {
+    ('tiny', 'experts'): {"kernel": "k_decode_fused", "grid": 232, "dispatches": 26, "fetch_kib": 1117.3, "write_kib": 51.2, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_decode.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/unpermute.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "62cca0b82e095fc8ee98f5854c75ceea10963b06234d4137d4b33501b370a08d"},
+    ('decode', 'experts'): {"kernel": "k_decode_fused", "grid": 2224, "dispatches": 25, "fetch_kib": 140210.7, "write_kib": 253.8, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_decode.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/unpermute.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "62cca0b82e095fc8ee98f5854c75ceea10963b06234d4137d4b33501b370a08d"},
+    ('prefill_zipf', 'gate_up'): {"kernel": "k_grouped_gemm_bf16<0>", "grid": 2312, "dispatches": 31, "fetch_kib": 552121.3, "write_kib": 49152.0, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_bf16.hip", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "9c23c898a853f1dff0e60d95719fb8aeaaff5de09eb105415a6340a33a231330"},
+    ('prefill_zipf', 'down'): {"kernel": "k_grouped_gemm_bf16<2>", "grid": 3080, "dispatches": 31, "fetch_kib": 249286.4, "write_kib": 131072.1, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_bf16.hip", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "9c23c898a853f1dff0e60d95719fb8aeaaff5de09eb105415a6340a33a231330"},
+    ('zero_experts', 'gate_up'): {"kernel": "k_grouped_gemm_bf16<0>", "grid": 4880, "dispatches": 26, "fetch_kib": 1581350.4, "write_kib": 19017.0, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_bf16.hip", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "9c23c898a853f1dff0e60d95719fb8aeaaff5de09eb105415a6340a33a231330"},
+    ('zero_experts', 'down'): {"kernel": "k_grouped_gemm_bf16<2>", "grid": 7320, "dispatches": 26, "fetch_kib": 746461.2, "write_kib": 57050.9, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_bf16.hip", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "9c23c898a853f1dff0e60d95719fb8aeaaff5de09eb105415a6340a33a231330"},
+    ('fp8_sigmoid', 'gate_up'): {"kernel": "k_grouped_gemm_fp8_stream<0>", "grid": 6160, "dispatches": 6, "fetch_kib": 2410854.3, "write_kib": 35980.2, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_fp8.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "441f209d22b9527f9913a241f113d376c357a26593d0a6572b634f7ebe74e9a8"},
+    ('fp8_sigmoid', 'down'): {"kernel": "k_grouped_gemm_fp8_stream<1>", "grid": 10784, "dispatches": 26, "fetch_kib": 1077726.2, "write_kib": 229376.0, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_fp8.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "441f209d22b9527f9913a241f113d376c357a26593d0a6572b634f7ebe74e9a8"},
+    ('mxfp4_sigmoid', 'gate_up'): {"kernel": "k_grouped_gemm_mxfp4<0>", "grid": 6160, "dispatches": 6, "fetch_kib": 1352110.7, "write_kib": 35459.7, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_mxfp4.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "34b5f35cf22fd6ade37a650c3477a1adc986e27fdc523c85de2386a82f7a3014"},
+    ('mxfp4_sigmoid', 'down'): {"kernel": "k_grouped_gemm_mxfp4<1>", "grid": 21560, "dispatches": 6, "fetch_kib": 571243.0, "write_kib": 229376.0, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_mxfp4.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "34b5f35cf22fd6ade37a650c3477a1adc986e27fdc523c85de2386a82f7a3014"},
+}
 
 
 def measured_traffic(workload: str, kernel: str):
