@@ -331,7 +331,7 @@ def measure(name: str, args) -> dict:
         else:
             r = {"bound": "mfma", "achieved": mfma, "peak": MFMA_PEAK_TFLOPS[wl.weight_dtype], "unit": "TFLOP/s"}
         r["frac"] = r["achieved"] / r["peak"]
-        r["traffic"] = measured_traffic(wl.name, kind)
+        r["traffic"] = measured_traffic(name, kind)
         r.update({"kernel": label, "kernel_us": k_us[kind], "alg_bytes": b, "alg_flops": f,
                   "hbm_frac": hbm / HBM_PEAK_GBS, "mfma_frac": mfma / MFMA_PEAK_TFLOPS[wl.weight_dtype]})
         return r

@@ -7,13 +7,14 @@
 //
 // With one to a few rows per expert the layer is bound by reading the touched
 // experts' weights from HBM, so the kernel is built to keep many bytes in
-// flight: a 3- or 4-stage LDS ring filled by direct global -> LDS loads
-// (global_load_lds_dwordx4, 16 bytes per lane) of whole row segments, two or
-// three K steps of loads ahead of the MFMAs, and two blocks per CU (the ring is
+// flight: a 4-stage LDS ring filled by direct global -> LDS loads
+// (global_load_lds_dwordx4, 16 bytes per lane) of whole row segments, three K
+// steps of loads ahead of the MFMAs, and two blocks per CU (the ring is
 // the block's only LDS; the tile scheduler's scratch and the epilogue's partial
-// sums are aliased onto it).  Each weight row is read in 512-byte segments
-// where K is long (gate/up), which streams faster than 256- or 128-byte ones.
-// Chunk c of LDS row r is stored at 16-byte slot c ^ (r % (segment / 16)),
+// sums are aliased onto it).  Weight rows are read in 256-byte segments where K
+// is long (gate/up) and 128-byte ones where it is short (down); a probe of this
+// access pattern streams equally fast at 128 to 1024 bytes per segment, so the
+// segment length is chosen for the ring's depth.  Chunk c of LDS row r is stored at 16-byte slot c ^ (r % (segment / 16)),
 // since the loads write rows unpadded in lane order.
 //
 // Waits are explicit (vmcnt of this wave's own loads, then a plain s_barrier):
@@ -30,9 +31,11 @@ namespace {
 
 // Tile shapes.  A stage holds BM x ROWB bytes of A (AI load instructions per wave) and
 // BNB x ROWB bytes of B (BI per wave); NSTAGE stages make the ring.
-//   gate/up (K = H, long): 16 rows x 32 weight rows (16 gate, 16 up) x 512-byte segments,
-//     3 x 24 KB stages; wave w computes 32-wide k slices 2w and 2w+1 of every step for the whole
-//     tile (partial sums added in the epilogue).
+//   gate/up (K = H, long): 16 rows x 64 weight rows (32 gate, 32 up) x 256-byte segments,
+//     4 x 20 KB stages (three K steps of loads ahead: the stream needs about 64 KB in flight per
+//     CU, and a tile spends a few microseconds in its scheduler and epilogue with none); wave w
+//     computes 32-wide k slice w of every step for the whole tile (partial sums added in the
+//     epilogue).
 //   down (K = I, short):   32 rows x 128 weight rows x 128-byte segments, 4 x 20 KB stages (half
 //     as many tiles, so a decode layer's down tiles are all resident at once); wave w owns weight
 //     rows 32w .. 32w+31.
@@ -41,7 +44,7 @@ template <int STAGE>
 struct DecodeShape;
 template <>
 struct DecodeShape<0> {
-  static constexpr int BM = 16, BNB = 32, ROWB = 512, WK = 4, NSTAGE = 3, AI = 2, BI = 4;
+  static constexpr int BM = 16, BNB = 64, ROWB = 256, WK = 4, NSTAGE = 4, AI = 1, BI = 4;
 };
 template <>
 struct DecodeShape<1> {
