@@ -72,12 +72,28 @@ __device__ __forceinline__ int group_rows(const Groups& G, int e) {
 __device__ __forceinline__ int tile_prefix(const Groups& G, int BM, int* s_prefix, int* s_wsum) {
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int ngroups = G.nr + (G.xr > 0 ? 1 : 0);
-  // each thread owns 4 consecutive groups
+  // each thread owns 4 consecutive groups.  Their row counts come from offsets[4 tid .. 4 tid + 4]
+  // (clamped to the table), all five loads issued before the first is used: one memory round trip
+  // rather than one per group.
+  int rows[4];
+  if (G.nr > 0) {  // (a launch of the shared expert alone has no offsets table)
+    int off[5];
+#pragma unroll
+    for (int k = 0; k < 5; ++k) off[k] = G.offsets[min(tid * 4 + k, G.nr)];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = tid * 4 + j;
+      rows[j] = e < G.nr ? off[j + 1] - off[j] : (e == G.nr ? G.xr : 0);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) rows[j] = tid * 4 + j == 0 ? G.xr : 0;
+  }
   int cnt[4], local = 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = tid * 4 + j;
-    cnt[j] = e < ngroups ? (group_rows(G, e) + BM - 1) / BM * (e < G.nr ? G.nt : G.xnt) : 0;
+    cnt[j] = e < ngroups ? (rows[j] + BM - 1) / BM * (e < G.nr ? G.nt : G.xnt) : 0;
     local += cnt[j];
   }
   // inclusive scan of `local` across the block
