@@ -135,8 +135,11 @@ __device__ __forceinline__ TileCoord tile_at(const Groups& G, int BM, const int*
     else hi = mid - 1;
   }
   const int e = lo;
-  const int seg0 = e < G.nr ? G.offsets[e] : 0;
-  const int seg_end = e < G.nr ? G.offsets[e + 1] : G.xr;
+  int seg0 = 0, seg_end = G.xr;  // the shared group: rows [0, xr)
+  if (e < G.nr) {  // both offsets under one test, so that the two loads share one round trip
+    seg0 = G.offsets[e];
+    seg_end = G.offsets[e + 1];
+  }
   const int mt_e = (seg_end - seg0 + BM - 1) / BM;
   const int rem = L - s_prefix[e];
   tc.expert = e;
