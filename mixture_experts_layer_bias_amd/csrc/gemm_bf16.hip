@@ -40,7 +40,29 @@ struct Bf16Tile {
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
-template <int STAGE>
+// 16-byte global load from a base that is the same in every lane plus a per-lane byte offset: with a
+// 32-bit offset the base stays in scalar registers and the address costs one VGPR.  (The empty asm keeps
+// the compiler from hoisting a 64-bit form of the offset out of the K loop, which would cost two VGPRs
+// and a 64-bit add per load.)
+__device__ __forceinline__ u32x4 ldg16_off(const void* base, uint32_t off) {
+  asm volatile("" : "+v"(off));
+  return *(global_u32x4*)(reinterpret_cast<const char*>(base) + off);
+}
+// the same for operands of 4 GiB or more
+__device__ __forceinline__ u32x4 ldg16_off(const void* base, uint64_t off) {
+  return *(global_u32x4*)(reinterpret_cast<const char*>(base) + off);
+}
+// A pointer that is the same in every lane, moved to scalar registers.
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
+
+// OffT: the type of the A rows' byte offsets (uint32_t while the A operand is below 4 GiB)
+template <int STAGE, typename OffT>
 __global__ __launch_bounds__(256, 2) void k_grouped_gemm_bf16(GroupedGemmArgs g) {
   using T = Bf16Tile<STAGE>;
   __shared__ __align__(16) uint16_t lds[T::LDS_BYTES / 2];
@@ -68,37 +90,42 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_bf16(GroupedGemmArgs g)
   } else {
     wa = static_cast<const uint16_t*>(sh ? g.sh_down : g.w_down[tc.expert]);
   }
-  const uint16_t* a_src = static_cast<const uint16_t*>(sh ? g.sh_a : g.a);
+  const uint16_t* a_src = uniform_ptr(static_cast<const uint16_t*>(sh ? g.sh_a : g.a));
+  wa = uniform_ptr(wa);
+  if (STAGE == 0) wb = uniform_ptr(wb);
+  const int n0u = __builtin_amdgcn_readfirstlane(n0);
 
   const int lrow = tid >> 3;       // 0..31: row within a 32-row slab of the tile
   const int lcol = (tid & 7) * 8;  // bf16 column of this thread's 16-byte chunk
-  const uint16_t* a_ptr[T::A_LOADS];
+  // A rows: byte offsets from a_src
+  OffT a_off[T::A_LOADS];
 #pragma unroll
   for (int i = 0; i < T::A_LOADS; ++i) {
     int p = tc.row0 + lrow + 32 * i;
     if (p >= tc.row_end) p = tc.row_end - 1;  // clamp: rows past the segment are computed, never stored
-    long arow;
+    int arow;
     if (STAGE == 0) arow = sh ? p : g.sorted_ids[p] / g.K;
     else arow = p;
-    a_ptr[i] = a_src + (size_t)arow * KD + lcol;
+    a_off[i] = ((OffT)arow * (OffT)KD + (OffT)lcol) * 2u;
   }
-  const uint16_t* b_ptr[T::B_LOADS];
+  // B rows: slab i of 32 weight rows starts at a uniform address; every slab has the same per-lane offset
+  const uint16_t* b_slab[T::B_LOADS];
 #pragma unroll
   for (int i = 0; i < T::B_LOADS; ++i) {
-    const int r = lrow + 32 * i;  // 0..BROWS-1
     if (STAGE == 0) {
-      b_ptr[i] = (r < BN ? wa + (size_t)(n0 + r) * KD : wb + (size_t)(n0 + r - BN) * KD) + lcol;
+      b_slab[i] = i < T::B_LOADS / 2 ? wa + (size_t)(n0u + 32 * i) * KD : wb + (size_t)(n0u + 32 * i - BN) * KD;
     } else {
-      b_ptr[i] = wa + (size_t)(n0 + r) * KD + lcol;
+      b_slab[i] = wa + (size_t)(n0u + 32 * i) * KD;
     }
   }
+  const uint32_t b_off = ((uint32_t)lrow * (uint32_t)KD + lcol) * 2u;
 
   u32x4 ra[T::A_LOADS], rb[T::B_LOADS];
   auto load_tile = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < T::A_LOADS; ++i) ra[i] = ldg16(a_ptr[i] + k0);
+    for (int i = 0; i < T::A_LOADS; ++i) ra[i] = ldg16_off(a_src + k0, a_off[i]);
 #pragma unroll
-    for (int i = 0; i < T::B_LOADS; ++i) rb[i] = ldg16(b_ptr[i] + k0);
+    for (int i = 0; i < T::B_LOADS; ++i) rb[i] = ldg16_off(b_slab[i] + k0, b_off);
   };
   auto store_tile = [&]() {
 #pragma unroll
@@ -177,16 +204,29 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_bf16(GroupedGemmArgs g)
 
 }  // namespace
 
+// Whether some A operand of the launch (x or h, and the shared group's) reaches 4 GiB, so that its row
+// offsets need 64 bits.
+static bool a_is_wide(const GroupedGemmArgs& g) {
+  const uint64_t lim = (uint64_t)1 << 32;
+  if (g.stage == 0) return (uint64_t)g.N * g.H * 2 >= lim;
+  const uint64_t routed = g.shared ? 0 : (uint64_t)g.P * g.I * 2;
+  const uint64_t sh = (g.shared || g.with_shared) ? (uint64_t)g.N * g.Is * 2 : 0;
+  return routed >= lim || sh >= lim;
+}
+
+template <int STAGE>
+static void launch_stage(const GroupedGemmArgs& g, int cols, hipStream_t s) {
+  const dim3 grid(grouped_grid(g, gemm_groups(g, STAGE == 0 ? 0 : 1, cols), BM));
+  if (a_is_wide(g)) k_grouped_gemm_bf16<STAGE, uint64_t><<<grid, 256, 0, s>>>(g);
+  else k_grouped_gemm_bf16<STAGE, uint32_t><<<grid, 256, 0, s>>>(g);
+}
+
 hipError_t launch_grouped_gemm_bf16(const GroupedGemmArgs& g, hipStream_t s) {
   if (g.N == 0) return hipSuccess;
   if (!g.row_invariant && decode_gemm_fits(g)) return launch_grouped_gemm_decode(g, s);
-  if (g.stage == 0) {
-    k_grouped_gemm_bf16<0><<<grouped_grid(g, gemm_groups(g, 0, BN), BM), 256, 0, s>>>(g);
-  } else if (g.H % (2 * BN) == 0) {
-    k_grouped_gemm_bf16<2><<<grouped_grid(g, gemm_groups(g, 1, 2 * BN), BM), 256, 0, s>>>(g);
-  } else {
-    k_grouped_gemm_bf16<1><<<grouped_grid(g, gemm_groups(g, 1, BN), BM), 256, 0, s>>>(g);
-  }
+  if (g.stage == 0) launch_stage<0>(g, BN, s);
+  else if (g.H % (2 * BN) == 0) launch_stage<2>(g, 2 * BN, s);
+  else launch_stage<1>(g, BN, s);
   return hipGetLastError();
 }
 

@@ -427,6 +427,71 @@ def test_bf16_segment_edges_match_oracle(name, H):
     assert (bits(h)[Pr:] == 0).all() and (bits(y)[Pr:] == 0).all()
 
 
+@pytest.mark.parametrize("stage,H", [(0, 2048), (1, 256), (1, 384)])
+def test_bf16_operands_past_4gib_match_oracle(stage, H):
+    """The A operand (x for gate/up, h for down) is 4 GiB or more, so its row offsets need 64 bits; the
+    rows checked lie past the 4 GiB mark (and at the start and at segment edges)."""
+    E, I, seed = 4, 128, 33
+    if stage == 0:
+        K, N = 1, (1 << 20) + 256  # x: N x 2048 bf16 = 4 GiB + 1 MiB
+    else:
+        K, N = 4, (1 << 22) + 64  # h: N*K x 128 bf16 = 4 GiB + 64 KiB
+    P = N * K
+    print(f"\n[case] bf16 stage {stage} with a 4 GiB+ operand: N {N} K {K} H {H}", flush=True)
+    wl = W(f"wide{stage}", 8, H, E, E, K, I, 0, "softmax", True, 1.0, "bf16", False, seed=seed)
+    dl = mi.device.device_layer(wl)
+    cfg = moe.make_config(N, H, E, E, K, I, 0, "softmax", True, 1.0, "bf16")
+    w = weights_of(dl)
+    rng = np.random.default_rng(seed)
+    experts = [mi.host_expert(wl, e) for e in range(E)]
+    if stage == 0:
+        counts = [130, 1, 0, 125]  # 256 routed rows, half of them tokens past the 4 GiB mark
+        Pr = sum(counts)
+        toks = np.concatenate([np.arange(N - Pr // 2, N), rng.choice(N - Pr, Pr - Pr // 2, replace=False)])
+        sid = np.zeros(P, np.int32)
+        sid[:Pr] = rng.permutation(toks)
+        offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+        x = torch.empty((N, H), dtype=torch.bfloat16, device="cuda")
+        mi.dev_bf16(x, seed, mi.TAG_X, 0, mi.SIGMA_X)
+        out = torch.zeros((P, I), dtype=torch.bfloat16, device="cuda")
+        moe.moe_grouped_gemm(cfg, 0, 0, w, x, None, torch.from_numpy(sid).cuda(), torch.from_numpy(offsets).cuda(),
+                             out, None)
+        torch.cuda.synchronize()
+        check = np.arange(Pr)
+        ref = np.zeros((Pr, I), np.uint16)
+        for e in range(E):
+            rows = np.arange(offsets[e], offsets[e + 1])
+            if len(rows):
+                xr = np.stack([mi.host_bf16((H,), seed, mi.TAG_X, 0, mi.SIGMA_X, first=int(t) * H) for t in sid[rows]])
+                ref[rows] = om.gate_up_bf16(om.bf16_to_f64(xr), experts[e][0], experts[e][1])
+        got = bits(out[:Pr])
+        assert_close(om.bf16_to_f64(got), om.bf16_to_f64(ref), BF16_TOL, "gate/up h past 4 GiB of x")
+        assert (bits(out[Pr:Pr + 4096]) == 0).all()
+    else:
+        cuts = [P // 4 - 77, P // 2 + 5, 3 * P // 4 + 130]  # ragged segments; every row routed
+        offsets = np.array([0, *cuts, P], np.int32)
+        h = torch.empty((P, I), dtype=torch.bfloat16, device="cuda")
+        mi.dev_bf16(h, seed, mi.TAG_X, 1, mi.SIGMA_X)
+        out = torch.zeros((P, H), dtype=torch.bfloat16, device="cuda")
+        moe.moe_grouped_gemm(cfg, 1, 0, w, h, None, None, torch.from_numpy(offsets).cuda(), out, None)
+        torch.cuda.synchronize()
+        check = np.unique(np.concatenate([np.arange(64), np.arange(P - 300, P),
+                                          *[np.arange(c - 40, c + 40) for c in cuts],
+                                          rng.integers(0, P, 200)]))
+        hr = np.stack([mi.host_bf16((I,), seed, mi.TAG_X, 1, mi.SIGMA_X, first=int(p) * I) for p in check])
+        e_of = np.searchsorted(offsets, check, side="right") - 1
+        ref = np.zeros((len(check), H))
+        for e in range(E):
+            m = e_of == e
+            if m.any():
+                ref[m] = om.down_bf16(hr[m], experts[e][2])
+        got = f64(out[torch.from_numpy(check).cuda()])
+        assert_close(got, ref, BF16_TOL, "down y past 4 GiB of h")
+        del h
+    del out
+    torch.cuda.empty_cache()
+
+
 # ============================================================================ end to end
 
 @pytest.mark.parametrize("name", list(SMALL) + list(FP8_SMALL))
