@@ -52,10 +52,10 @@ CPU_SAMPLE_TOKENS = {"tiny": 16, "decode": 4, "prefill_zipf": 32, "fp8_sigmoid":
 MEASURED_TRAFFIC = {
     ('tiny', 'experts'): {"kernel": "k_decode_fused", "grid": 128, "dispatches": 26, "fetch_kib": 1106.8, "write_kib": 50.0, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_decode.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/unpermute.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "49483644c2b21ad2f481df1186fc98c618f643a1b1499bdf0e6ad465e6fd58c4"},
     ('decode', 'experts'): {"kernel": "k_decode_fused", "grid": 1384, "dispatches": 25, "fetch_kib": 140211.7, "write_kib": 231.0, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_decode.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/unpermute.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "49483644c2b21ad2f481df1186fc98c618f643a1b1499bdf0e6ad465e6fd58c4"},
-    ('prefill_zipf', 'gate_up'): {"kernel": "k_grouped_gemm_bf16<0>", "grid": 2312, "dispatches": 31, "fetch_kib": 539719.5, "write_kib": 49152.0, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_bf16.hip", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "7514674468fb8d65f80419c562525ebcb9bb30bc377062eeeade553eaa9f9867"},
-    ('prefill_zipf', 'down'): {"kernel": "k_grouped_gemm_bf16<2>", "grid": 3080, "dispatches": 31, "fetch_kib": 249048.8, "write_kib": 131072.1, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_bf16.hip", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "7514674468fb8d65f80419c562525ebcb9bb30bc377062eeeade553eaa9f9867"},
-    ('zero_experts', 'gate_up'): {"kernel": "k_grouped_gemm_bf16<0>", "grid": 4880, "dispatches": 26, "fetch_kib": 1571112.4, "write_kib": 19017.1, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_bf16.hip", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "7514674468fb8d65f80419c562525ebcb9bb30bc377062eeeade553eaa9f9867"},
-    ('zero_experts', 'down'): {"kernel": "k_grouped_gemm_bf16<2>", "grid": 7320, "dispatches": 26, "fetch_kib": 744673.5, "write_kib": 57050.8, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_bf16.hip", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "7514674468fb8d65f80419c562525ebcb9bb30bc377062eeeade553eaa9f9867"},
+    ('prefill_zipf', 'gate_up'): {"kernel": "k_grouped_gemm_bf16<0, unsigned int>", "grid": 2312, "dispatches": 31, "fetch_kib": 616369.8, "write_kib": 49152.2, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_bf16.hip", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "0610c5a617257ada877715647db03d4bf573e618b7a51bafafbbae062ffa39f2"},
+    ('prefill_zipf', 'down'): {"kernel": "k_grouped_gemm_bf16<2, unsigned int>", "grid": 3080, "dispatches": 31, "fetch_kib": 258171.6, "write_kib": 131072.1, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_bf16.hip", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "0610c5a617257ada877715647db03d4bf573e618b7a51bafafbbae062ffa39f2"},
+    ('zero_experts', 'gate_up'): {"kernel": "k_grouped_gemm_bf16<0, unsigned int>", "grid": 4880, "dispatches": 26, "fetch_kib": 1767952.1, "write_kib": 19017.4, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_bf16.hip", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "0610c5a617257ada877715647db03d4bf573e618b7a51bafafbbae062ffa39f2"},
+    ('zero_experts', 'down'): {"kernel": "k_grouped_gemm_bf16<2, unsigned int>", "grid": 7320, "dispatches": 26, "fetch_kib": 784803.4, "write_kib": 57051.1, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_bf16.hip", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "0610c5a617257ada877715647db03d4bf573e618b7a51bafafbbae062ffa39f2"},
     ('fp8_sigmoid', 'gate_up'): {"kernel": "k_grouped_gemm_fp8_stream<0>", "grid": 6160, "dispatches": 6, "fetch_kib": 2413650.8, "write_kib": 36014.0, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_fp8.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "4ad41382eebc4983e5a9760f5949428e3030e1b09035d3b8cb994e5e4e0545f5"},
     ('fp8_sigmoid', 'down'): {"kernel": "k_grouped_gemm_fp8_stream<1>", "grid": 10784, "dispatches": 26, "fetch_kib": 1077275.8, "write_kib": 229376.0, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_fp8.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "4ad41382eebc4983e5a9760f5949428e3030e1b09035d3b8cb994e5e4e0545f5"},
     ('mxfp4_sigmoid', 'gate_up'): {"kernel": "k_grouped_gemm_mxfp4<0>", "grid": 6160, "dispatches": 6, "fetch_kib": 1350446.7, "write_kib": 35526.6, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_mxfp4.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "7c17c50429618d5872a86bb6351d7da9d6d2bd3ab658aa051826375c1486faff"},
