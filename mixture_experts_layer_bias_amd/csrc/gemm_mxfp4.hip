@@ -36,7 +36,15 @@ constexpr int E8M0_ONE = 127;  // E8M0 code of 2^0
 // per CU).
 constexpr int MX_GU_WAVES = 16, MX_DN_WAVES = 4;
 
-template <int STAGE>
+// WIN: the scales travel in windows of 4 K steps (WIN_STEPS) instead of with every step: each weight
+// row's 16 E8M0 codes and each activation row's 4 fp32 scales of a window are one contiguous 16-byte
+// piece, so a window costs one L2 request per row where per-step loads cost one per row and step.  A
+// window's pieces are loaded in WIN_STEPS slices, one with each ring stage of the window before it, into
+// one of three window buffers (a buffer is rewritten only after every step of the window it held is
+// done).  Needs whole windows: KD / BK a multiple of WIN_STEPS.
+constexpr int WIN_STEPS = 4, WIN_BUFS = 3;
+
+template <int STAGE, bool WIN = false>
 struct MxShape {
   static constexpr int WAVES = STAGE == 0 ? MX_GU_WAVES : MX_DN_WAVES;
   static constexpr int WN = WAVES == 4 ? 2 : 4;           // waves along the columns
@@ -49,11 +57,19 @@ struct MxShape {
   static constexpr int BBYTES = BROWS * BK / 2;           // packed E2M1 rows
   static constexpr int BSBYTES = BROWS * 4;               // the 4 E8M0 codes of each weight row
   static constexpr int ASBYTES = BM * 4;                  // the fp32 scale of each activation row
-  static constexpr int SBYTES = ABYTES + BBYTES + BSBYTES + ASBYTES;
+  static constexpr int SBYTES = ABYTES + BBYTES + (WIN ? 0 : BSBYTES + ASBYTES);
   static constexpr int A_DMA = ABYTES / 1024 / WAVES;     // 16-byte A loads per wave per step
   static constexpr int B_DMA = BBYTES / 1024 / WAVES;     // 16-byte B loads per wave per step
-  static constexpr int VM = A_DMA + B_DMA + 1 + 1;        // load instructions per wave per step
-  static constexpr int LDS = NSTAGE * SBYTES;
+  static constexpr int VM = A_DMA + B_DMA + (WIN ? 1 : 2);  // load instructions per wave per step
+  // WIN: a window holds one 16-byte piece per weight row and per activation row; slice j of it (loaded
+  // with one ring stage) covers rows SLICE_ROWS j .., PPW rows per wave
+  static constexpr int WIN_ROWS = BROWS + BM;
+  static constexpr int WIN_BYTES = WIN_ROWS * 16;
+  static constexpr int SLICE_ROWS = WIN_ROWS / WIN_STEPS;
+  static constexpr int PPW = SLICE_ROWS / WAVES;
+  static_assert(!WIN || (SLICE_ROWS * WIN_STEPS == WIN_ROWS && PPW * WAVES == SLICE_ROWS && 4 * PPW <= kWave),
+                "window slices");
+  static constexpr int LDS = NSTAGE * SBYTES + (WIN ? WIN_BUFS * WIN_BYTES : 0);
 };
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
@@ -84,9 +100,9 @@ __device__ __forceinline__ f32x16 mfma_e4m3_x_e2m1(i32x8 a, i32x8 b, int b_scale
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 4, 0, E8M0_ONE, 0, b_scale);
 }
 
-template <int STAGE>
+template <int STAGE, bool WIN>
 __global__ __launch_bounds__(MxShape<STAGE>::WAVES * 64, STAGE == 0 ? 1 : 2) void k_grouped_gemm_mxfp4(GroupedGemmArgs g) {
-  using S = MxShape<STAGE>;
+  using S = MxShape<STAGE, WIN>;
   constexpr int NSTAGE = S::NSTAGE, VM = S::VM, BROWS = S::BROWS, MI = S::MI, NI = S::NI;
   constexpr int WR = BM / S::WM, WC = BN / S::WN;  // a wave's tile rows and columns
   extern __shared__ __align__(16) uint8_t smem[];  // S::LDS bytes: the ring
@@ -153,6 +169,27 @@ __global__ __launch_bounds__(MxShape<STAGE>::WAVES * 64, STAGE == 0 ? 1 : 2) voi
   const bool as_lane = lane < as_rows;
   const float* as_ptr = (sh ? g.sh_a_scales : g.a_scales) + (size_t)a_row(as_lane ? wave * as_rows + lane : 0) * KB;
 
+  // WIN: with slice j, lanes 4 i .. 4 i + 3 (i < PPW) of wave w load the window piece of row
+  // rho = SLICE_ROWS j + PPW w + i (weight rows first, then activation rows) as four 4-byte words, which
+  // the address unit joins into one request; win_src[j] is the lane's word of window 0
+  uint8_t* const win_lds = smem + NSTAGE * S::SBYTES;
+  const uint8_t* win_src[WIN ? WIN_STEPS : 1];
+  if constexpr (WIN) {
+#pragma unroll
+    for (int j = 0; j < WIN_STEPS; ++j) {
+      const int rho = min(S::SLICE_ROWS * j + S::PPW * wave + lane / 4, S::WIN_ROWS - 1);
+      win_src[j] = (rho < BROWS ? weight_row(rho, sa_w, sb_w, (size_t)KD / 32)
+                                : reinterpret_cast<const uint8_t*>((sh ? g.sh_a_scales : g.a_scales) +
+                                                                   (size_t)a_row(rho - BROWS) * KB)) +
+                   (lane % 4) * 4;
+    }
+  }
+  auto issue_slice = [&](int v, int j) {  // slice j of window v (v past the last: the last again, unused)
+    const int vs = min(v, KB / WIN_STEPS - 1);
+    if (lane < 4 * S::PPW)
+      dma4(win_src[j] + (size_t)vs * 16, win_lds + (v % WIN_BUFS) * S::WIN_BYTES + (S::SLICE_ROWS * j + S::PPW * wave) * 16);
+  };
+
   auto issue = [&](int buf, int kb) {
     uint8_t* sa = smem + buf * S::SBYTES;
     uint8_t* sb = sa + S::ABYTES;
@@ -162,8 +199,14 @@ __global__ __launch_bounds__(MxShape<STAGE>::WAVES * 64, STAGE == 0 ? 1 : 2) voi
     for (int i = 0; i < S::A_DMA; ++i) dma16(a_ptr[i] + (size_t)kb * BK, sa + (S::A_DMA * wave + i) * 1024);
 #pragma unroll
     for (int i = 0; i < S::B_DMA; ++i) dma16(b_ptr[i] + (size_t)kb * (BK / 2), sb + (S::B_DMA * wave + i) * 1024);
-    if (bs_lane) dma4(bs_ptr + (size_t)kb * 4, sbs + wave * bs_rows * 4);
-    if (as_lane) dma4(as_ptr + kb, sas + wave * as_rows * 4);
+    if constexpr (WIN) {
+      // slice kb % 4 of window kb / 4 + 1: that buffer last held window kb / 4 - 2, whose last step,
+      // 4 (kb / 4) - 5, every wave has finished by the barrier of step kb - 3 that precedes this issue
+      issue_slice(kb / WIN_STEPS + 1, kb % WIN_STEPS);
+    } else {
+      if (bs_lane) dma4(bs_ptr + (size_t)kb * 4, sbs + wave * bs_rows * 4);
+      if (as_lane) dma4(as_ptr + kb, sas + wave * as_rows * 4);
+    }
   };
 
   constexpr int NB = STAGE == 0 ? 2 * NI : NI;
@@ -184,6 +227,10 @@ __global__ __launch_bounds__(MxShape<STAGE>::WAVES * 64, STAGE == 0 ? 1 : 2) voi
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) live_mi += tc.row0 + wm * WR + mi * 32 < tc.row_end;
 
+  if constexpr (WIN) {
+#pragma unroll
+    for (int j = 0; j < WIN_STEPS; ++j) issue_slice(0, j);  // window 0, older than every ring stage
+  }
 #pragma unroll
   for (int s = 0; s < NSTAGE - 1; ++s)
     if (s < KB) issue(s, s);
@@ -197,8 +244,16 @@ __global__ __launch_bounds__(MxShape<STAGE>::WAVES * 64, STAGE == 0 ? 1 : 2) voi
     if (live_mi == 0) continue;
     const uint8_t* sa = smem + (kb % NSTAGE) * S::SBYTES;
     const uint8_t* sb = sa + S::ABYTES;
-    const uint32_t* sbs = reinterpret_cast<const uint32_t*>(sb + S::BBYTES);
-    const float* sas = reinterpret_cast<const float*>(sb + S::BBYTES + S::BSBYTES);
+    // this step's 4 E8M0 codes of weight row r and fp32 scale of activation row r
+    const uint8_t* win = win_lds + ((kb / WIN_STEPS) % WIN_BUFS) * S::WIN_BYTES + (kb % WIN_STEPS) * 4;
+    auto bcodes = [&](int r) {
+      return WIN ? *reinterpret_cast<const uint32_t*>(win + r * 16)
+                 : reinterpret_cast<const uint32_t*>(sb + S::BBYTES)[r];
+    };
+    auto ascale = [&](int r) {
+      return WIN ? *reinterpret_cast<const float*>(win + (BROWS + r) * 16)
+                 : reinterpret_cast<const float*>(sb + S::BBYTES + S::BSBYTES)[r];
+    };
     f32x16 blk[MI][NB];
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
@@ -230,7 +285,7 @@ __global__ __launch_bounds__(MxShape<STAGE>::WAVES * 64, STAGE == 0 ? 1 : 2) voi
         const int c = kk / 32 + half;  // memory block of the lane's 32 codes (16 bytes)
         const u32x4 v = *reinterpret_cast<const u32x4*>(sb + wr * (BK / 2) + ((c ^ ((wr >> 2) & 3)) << 4));
         bfr[nb] = i32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
-        bsc[nb] = (int)((sbs[wr] >> (8 * c)) & 0xFFu);
+        bsc[nb] = (int)((bcodes(wr) >> (8 * c)) & 0xFFu);
       }
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
@@ -246,7 +301,7 @@ __global__ __launch_bounds__(MxShape<STAGE>::WAVES * 64, STAGE == 0 ? 1 : 2) voi
       if (mi >= live_mi) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float rs = sas[wm * WR + mi * 32 + item_row(r)];
+        const float rs = ascale(wm * WR + mi * 32 + item_row(r));
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[mi][nb][r] += blk[mi][nb][r] * rs;
       }
@@ -324,18 +379,23 @@ __global__ __launch_bounds__(MxShape<STAGE>::WAVES * 64, STAGE == 0 ? 1 : 2) voi
 
 }  // namespace
 
+template <int STAGE, bool WIN>
+static hipError_t launch_mx(const GroupedGemmArgs& g, hipStream_t s) {
+  using S = MxShape<STAGE, WIN>;
+  const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&k_grouped_gemm_mxfp4<STAGE, WIN>), S::LDS);
+  if (e != hipSuccess) return e;
+  k_grouped_gemm_mxfp4<STAGE, WIN><<<grouped_grid(g, gemm_groups(g, STAGE, BN), BM), S::WAVES * 64, S::LDS, s>>>(g);
+  return hipGetLastError();
+}
+
 hipError_t launch_grouped_gemm_mxfp4(const GroupedGemmArgs& g, hipStream_t s) {
   if (g.N == 0) return hipSuccess;
   if (g.stage == 0) {
-    const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&k_grouped_gemm_mxfp4<0>), MxShape<0>::LDS);
-    if (e != hipSuccess) return e;
-    k_grouped_gemm_mxfp4<0><<<grouped_grid(g, gemm_groups(g, 0, BN), BM), MxShape<0>::WAVES * 64, MxShape<0>::LDS, s>>>(g);
-  } else {
-    const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&k_grouped_gemm_mxfp4<1>), MxShape<1>::LDS);
-    if (e != hipSuccess) return e;
-    k_grouped_gemm_mxfp4<1><<<grouped_grid(g, gemm_groups(g, 1, BN), BM), MxShape<1>::WAVES * 64, MxShape<1>::LDS, s>>>(g);
+    // scale windows when every group's K steps come in whole windows (K = H for all of them)
+    if ((g.H / BK) % WIN_STEPS == 0) return launch_mx<0, true>(g, s);
+    return launch_mx<0, false>(g, s);
   }
-  return hipGetLastError();
+  return launch_mx<1, false>(g, s);
 }
 
 }  // namespace moe

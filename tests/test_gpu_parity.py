@@ -349,12 +349,13 @@ SEGMENTS = {
 }
 
 
-@pytest.mark.parametrize("dtype", ["fp8", "mxfp4"])
+# MXFP4 at H = 1536: 12 K steps of gate/up, so its scales come in three windows of 4 steps
+@pytest.mark.parametrize("dtype,H", [("fp8", 256), ("mxfp4", 256), ("mxfp4", 1536)])
 @pytest.mark.parametrize("name", list(SEGMENTS))
-def test_quantised_segment_edges_match_oracle(name, dtype):
+def test_quantised_segment_edges_match_oracle(name, dtype, H):
     N, K, counts = SEGMENTS[name]
-    E, H, I = len(counts), 256, 256
-    print(f"\n[case] {dtype} segment edges {name}: counts {counts}", flush=True)
+    E, I = len(counts), 256
+    print(f"\n[case] {dtype} segment edges {name} H{H}: counts {counts}", flush=True)
     wl = W(f"{dtype}seg{E}", N, H, E, E, K, I, 0, "sigmoid", True, 2.5, dtype, True, seed=31)
     P = N * K
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
