@@ -58,8 +58,8 @@ MEASURED_TRAFFIC = {
     ('zero_experts', 'down'): {"kernel": "k_grouped_gemm_bf16<2, unsigned int>", "grid": 7320, "dispatches": 26, "fetch_kib": 784803.4, "write_kib": 57051.1, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_bf16.hip", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "0610c5a617257ada877715647db03d4bf573e618b7a51bafafbbae062ffa39f2"},
     ('fp8_sigmoid', 'gate_up'): {"kernel": "k_grouped_gemm_fp8_stream<0>", "grid": 6160, "dispatches": 6, "fetch_kib": 2413650.8, "write_kib": 36014.0, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_fp8.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "4ad41382eebc4983e5a9760f5949428e3030e1b09035d3b8cb994e5e4e0545f5"},
     ('fp8_sigmoid', 'down'): {"kernel": "k_grouped_gemm_fp8_stream<1>", "grid": 10784, "dispatches": 26, "fetch_kib": 1077275.8, "write_kib": 229376.0, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_fp8.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "4ad41382eebc4983e5a9760f5949428e3030e1b09035d3b8cb994e5e4e0545f5"},
-    ('mxfp4_sigmoid', 'gate_up'): {"kernel": "k_grouped_gemm_mxfp4<0>", "grid": 6160, "dispatches": 6, "fetch_kib": 1350446.7, "write_kib": 35526.6, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_mxfp4.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "7c17c50429618d5872a86bb6351d7da9d6d2bd3ab658aa051826375c1486faff"},
-    ('mxfp4_sigmoid', 'down'): {"kernel": "k_grouped_gemm_mxfp4<1>", "grid": 21560, "dispatches": 6, "fetch_kib": 571130.1, "write_kib": 229376.2, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_mxfp4.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "7c17c50429618d5872a86bb6351d7da9d6d2bd3ab658aa051826375c1486faff"},
+    ('mxfp4_sigmoid', 'gate_up'): {"kernel": "k_grouped_gemm_mxfp4<0, true>", "grid": 6160, "dispatches": 6, "fetch_kib": 1520504.5, "write_kib": 35700.8, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_mxfp4.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "77dc683aacc709f783f875f94fc289b0431236ab065732a57c2cd483a9edb315"},
+    ('mxfp4_sigmoid', 'down'): {"kernel": "k_grouped_gemm_mxfp4<1, false>", "grid": 21560, "dispatches": 6, "fetch_kib": 571149.9, "write_kib": 229376.1, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_mxfp4.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "77dc683aacc709f783f875f94fc289b0431236ab065732a57c2cd483a9edb315"},
 }
 
 
