@@ -173,7 +173,12 @@ moe_status_t moe_quantize_fp8(const moe_config_t* cfg, const void* x, uint8_t* x
  *   moe_quantize_fp8 for GATE_UP, from the GATE_UP output for DOWN); GATE_UP
  *   writes e4m3 codes + out_scales [P or N, I/128] quantised per 128 columns
  *   like moe_quantize_fp8; DOWN writes bf16.
- * ws: at least moe_workspace_size(cfg) bytes (may be NULL for this build). */
+ * ws: NULL, or at least moe_workspace_size(cfg) bytes (256-byte aligned, any contents).  With
+ *   a workspace, a routed bf16 launch makes moe_forward's choices: for layers that have the `split`
+ *   piece (moe_workspace_layout), when the last round of tiles fills at most half of the GPU its tiles
+ *   are split along K into parts whose fp32 sums are added in part order by the last part to arrive.
+ *   Without one it never splits, and a split tile's outputs can then differ from moe_forward's in
+ *   their last bits (a different order of the same sums).  Calls that overlap on one workspace race. */
 moe_status_t moe_grouped_gemm(const moe_config_t* cfg, int32_t stage, int32_t group, const moe_weights_t* w,
                               const void* a, const float* a_scales, const int32_t* sorted_ids,
                               const int32_t* offsets, void* out, float* out_scales, void* ws, size_t ws_bytes,
@@ -218,7 +223,7 @@ moe_status_t moe_forward(const moe_config_t* cfg, const moe_weights_t* w, const 
  * ws: at least moe_workspace_size(cfg) bytes.  With bf16 weights, H <= 65536 and
  * a few rows per touched expert (decode) the routed GEMMs and the reduce run as
  * one launch whose tiles wait on counters in the workspace's `sync` piece.  That
- * piece is the first 6664 bytes of every workspace, whatever the sizes, and its
+ * piece is the first 8712 bytes of every workspace, whatever the sizes, and its
  * counters must hold zeros when the call starts: zero them once (e.g. zero the
  * whole workspace after allocating it); every call of this library leaves them
  * zero, so the workspace can then serve any batch size and layer shape.
@@ -254,10 +259,13 @@ moe_status_t moe_forward_noalloc(const moe_config_t* cfg, const moe_weights_t* w
  * can inspect them after moe_forward (all in bytes from the workspace start;
  * a piece that the config does not use has offset SIZE_MAX).  `sync` (always 0)
  * holds the counters of the one-launch decode experts path and `sync_error` its
- * error word (see moe_experts_forward). */
+ * error word (see moe_experts_forward), and the arrival counters of split tiles.
+ * `split` holds the parts' fp32 partial sums of split tiles: present for bf16
+ * layers of at least 2048 routed rows with H or I of at least 4096, without a
+ * shared expert and not row-invariant (see moe_grouped_gemm). */
 typedef struct {
   size_t logits, topk_ids, topk_w, zero_w, counts, offsets, sorted_ids, inv_perm;
-  size_t xq, x_scales, h, h_scales, y, shared_h, shared_h_scales, shared_y, scratch, sync, sync_error, total;
+  size_t xq, x_scales, h, h_scales, y, shared_h, shared_h_scales, shared_y, scratch, sync, sync_error, split, total;
 } moe_workspace_layout_t;
 moe_status_t moe_workspace_layout(const moe_config_t* cfg, moe_workspace_layout_t* layout);
 

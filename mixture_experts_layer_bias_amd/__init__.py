@@ -56,7 +56,8 @@ class moe_weights_t(ctypes.Structure):
 class moe_workspace_layout_t(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "logits", "topk_ids", "topk_w", "zero_w", "counts", "offsets", "sorted_ids", "inv_perm", "xq", "x_scales",
-        "h", "h_scales", "y", "shared_h", "shared_h_scales", "shared_y", "scratch", "sync", "sync_error", "total")]
+        "h", "h_scales", "y", "shared_h", "shared_h_scales", "shared_y", "scratch", "sync", "sync_error", "split",
+        "total")]
 
 
 _lib = None

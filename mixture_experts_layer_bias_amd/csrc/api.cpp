@@ -12,6 +12,8 @@
 #include <cstring>
 #include <mutex>
 #include <random>
+#include <algorithm>
+#include <map>
 #include <set>
 #include <utility>
 
@@ -47,6 +49,33 @@ int next_route_seq() {
     const uint32_t v = ctr.fetch_add(1, std::memory_order_relaxed) + 1u;
     if (v != 0) return (int)v;
   }
+}
+
+// A nonzero value per launch of the bf16 tile kernel that may split tiles along K, different from the
+// previous launch's (its arrival counters count only words tagged with it).
+uint32_t next_split_seq() {
+  static std::atomic<uint32_t> ctr{std::random_device{}()};
+  for (;;) {
+    const uint32_t v = ctr.fetch_add(1, std::memory_order_relaxed) + 1u;
+    if (v != 0) return v;
+  }
+}
+
+// Blocks of the bf16 tile kernel (two per compute unit) that the current device holds at once, a
+// multiple of 8 and at most kSplitSlots; 0 if the device cannot be queried.
+int split_slots() {
+  static std::mutex mu;
+  static std::map<int, int> per_device;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = per_device.find(dev);
+  if (it != per_device.end()) return it->second;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 0;
+  const int slots = std::min(2 * cus, moe::kSplitSlots) / 8 * 8;
+  per_device[dev] = slots;
+  return slots;
 }
 
 moe_status_t fail(moe_status_t st, const char* fmt, ...) {
@@ -120,6 +149,16 @@ moe_status_t check_config(const moe_config_t* c) {
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// Whether the layer's bf16 tile-kernel launches may split their last round of tiles along K (and so
+// need the `split` piece): bf16 weights, not row-invariant, and launches of at least 2048 routed rows.
+// need the `split` piece): bf16 weights, not row-invariant, no shared expert (whose launches, folded or
+// not, then keep the bits of moe_forward's), launches of at least 2048 routed rows, and a GEMM with K of at
+// least 4096 (H for gate/up, I for down; see with_split).
+bool uses_split(const moe_config_t* c) {
+  return c->weight_dtype == MOE_WEIGHTS_BF16 && c->row_invariant == 0 && c->shared_inter == 0 &&
+         (int64_t)c->num_tokens * c->top_k >= 2048 && (c->hidden >= 4096 || c->inter >= 4096);
+}
+
 void compute_layout(const moe_config_t* c, moe_workspace_layout_t* L) {
   const size_t N = c->num_tokens, H = c->hidden, R = c->router_width, K = c->top_k, I = c->inter,
                Is = c->shared_inter, P = N * K;
@@ -155,6 +194,7 @@ void compute_layout(const moe_config_t* c, moe_workspace_layout_t* L) {
   L->shared_h = Is ? take(N * Is * (fp8 ? 1 : 2)) : none;
   L->shared_h_scales = (Is && fp8) ? take(N * (Is / 128) * 4) : none;
   L->shared_y = Is ? take(N * H * 2) : none;
+  L->split = uses_split(c) ? take((size_t)moe::kSplitSlots * moe::kSplitFloats * 4) : none;
   L->total = off;
 }
 
@@ -257,6 +297,21 @@ bool fold_shared(const moe_config_t* c, int stage) {
                      gemm_args(c, stage, MOE_GROUP_SHARED, &none, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr));
 }
 
+// Let a routed launch split its last round of tiles along K, with the workspace's `split` piece and
+// arrival counters (a no-op for a layer without that piece).  Only launches whose tiles are long (K of at
+// least 4096) split: there the last round, a tile-time long, costs most (measured: zero-computation-
+// expert layer gate/up, K 6144, 666 -> 617 us); shorter tiles gained nothing, and every launch that
+// may split carries `slots` more blocks, which only find that they have nothing to do.
+moe::GroupedGemmArgs with_split(moe::GroupedGemmArgs g, const moe_workspace_layout_t& L, char* base) {
+  if (L.split == SIZE_MAX || g.shared || g.with_shared) return g;
+  if ((g.stage == 0 ? g.H : g.I) < 4096) return g;
+  g.slots = split_slots();
+  g.split_seq = next_split_seq();
+  g.split_part = reinterpret_cast<float*>(base + L.split);
+  g.split_cnt = reinterpret_cast<unsigned long long*>(base + L.sync + (size_t)moe::kSyncSplit * 4);
+  return g;
+}
+
 moe_status_t run_gemm(const moe_config_t* c, const moe::GroupedGemmArgs& g, hipStream_t s) {
   if (c->weight_dtype == MOE_WEIGHTS_BF16) {
     MOE_HIP(moe::launch_grouped_gemm_bf16(g, s));
@@ -333,9 +388,9 @@ moe_status_t run_experts(const moe_config_t* cfg, const moe_weights_t* w, const 
     MOE_HIP(moe::launch_decode_fused(gu_all, dn_all, red, static_cast<int32_t*>(at(L.sync)), s));
     return ok();
   }
-  MOE_RET(run_gemm(cfg, gu_all, s));
+  MOE_RET(run_gemm(cfg, with_split(gu_all, L, base), s));
   if (c.shared_inter > 0 && !fold_gu) MOE_RET(run_gemm(cfg, sh_gu, s));
-  MOE_RET(run_gemm(cfg, dn_all, s));
+  MOE_RET(run_gemm(cfg, with_split(dn_all, L, base), s));
   if (c.shared_inter > 0 && !fold_dn) MOE_RET(run_gemm(cfg, sh_dn, s));
   MOE_HIP(moe::launch_unpermute_reduce(static_cast<const uint16_t*>(at(L.y)), red, s));
   return ok();
@@ -474,8 +529,6 @@ moe_status_t moe_grouped_gemm(const moe_config_t* cfg, int32_t stage, int32_t gr
                               const void* a, const float* a_scales, const int32_t* sorted_ids,
                               const int32_t* offsets, void* out, float* out_scales, void* ws, size_t ws_bytes,
                               void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   MOE_RET(check_config(cfg));
   MOE_CHECK(stage == MOE_STAGE_GATE_UP || stage == MOE_STAGE_DOWN, MOE_ERR_INVALID,
             "stage %d is not a MOE_STAGE_* value", stage);
@@ -519,7 +572,15 @@ moe_status_t moe_grouped_gemm(const moe_config_t* cfg, int32_t stage, int32_t gr
       if (fp8) MOE_RET(check_ptr(w->sh_down_s, 4, "sh_down_s"));
     }
   }
-  const moe::GroupedGemmArgs g = gemm_args(cfg, stage, group, w, a, a_scales, sorted_ids, offsets, out, out_scales);
+  moe::GroupedGemmArgs g = gemm_args(cfg, stage, group, w, a, a_scales, sorted_ids, offsets, out, out_scales);
+  if (ws != nullptr) {  // with a whole workspace: the same launch choices as moe_forward's
+    moe_workspace_layout_t L;
+    compute_layout(cfg, &L);
+    if (ws_bytes >= L.total) {
+      MOE_RET(check_ptr(ws, 256, "ws"));
+      g = with_split(g, L, static_cast<char*>(ws));
+    }
+  }
   MOE_RET(run_gemm(cfg, g, static_cast<hipStream_t>(stream)));
   return ok();
 }

@@ -71,9 +71,41 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_bf16(GroupedGemmArgs g)
   __shared__ int s_prefix[kMaxGroups + 1];
   __shared__ int s_wsum[4];
 
+  __shared__ int s_last;
+
+  // ---- which tile (and which part of its K range) this block computes.  The T tiles fill `slots`
+  // blocks in F = T / slots full rounds and a last round of R tiles; when that round is at most half
+  // full, each of its tiles is split along K into S parts (S = slots / R, at most kSplitParts and the
+  // K steps of a tile), so the last round ends after about 1 / S of a tile.  Blocks 0 .. F slots - 1
+  // take the whole tiles (XCD-aware, as schedule_tile), the next R S blocks the parts.
   const Groups G = gemm_groups(g, STAGE, T::COLS);
-  const TileCoord tc = schedule_tile(G, BM, s_prefix, s_wsum);
-  if (tc.expert < 0) return;
+  const int ntiles = tile_prefix(G, BM, s_prefix, s_wsum);
+  int S = 1, W = 0, R = 0;
+  if (g.slots > 0) {
+    const int F = ntiles / g.slots;
+    W = F * g.slots;
+    R = ntiles - W;
+    // parts: at most the K steps of the shortest group (gate/up: H; down: I, and Is with the shared group)
+    const int kmin = STAGE == 0 ? g.H : (g.shared ? g.Is : ((g.with_shared && g.Is < g.I) ? g.Is : g.I));
+    if (R > 0) S = min(min(g.slots / R, kSplitParts), kmin / BK);
+  }
+  int part = -1, L;
+  const int b = blockIdx.x;
+  if (S >= 2) {
+    if (b < W) {
+      L = (b % 8) * (W / 8) + b / 8;
+    } else {
+      const int u = b - W;
+      if (u >= R * S) return;  // the same decision in every thread
+      L = W + u / S;
+      part = u % S;
+    }
+  } else {
+    const int chunk = (ntiles + 7) / 8;
+    L = (b % 8) * chunk + b / 8;
+    if (b / 8 >= chunk || L >= ntiles) return;
+  }
+  const TileCoord tc = tile_at(G, BM, s_prefix, ntiles, L);
   const bool sh = tc.expert == G.nr;  // the shared expert's group
   const int KD = STAGE == 0 ? g.H : (sh ? g.Is : g.I);     // reduction length
   const int NCOLS = STAGE == 0 ? (sh ? g.Is : g.I) : g.H;  // output columns
@@ -149,11 +181,14 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_bf16(GroupedGemmArgs g)
   // waves skip the fragment reads and products (wave-uniform), which leaves them zero
   const int live_mi = (tc.row0 + wm * 64 < tc.row_end) + (tc.row0 + wm * 64 + 32 < tc.row_end);
 
-  load_tile(0);
+  const int nk_all = KD / BK;
+  // K steps [kt0, nk) of this block: all of them, or part `part` of S
+  const int kt0 = part < 0 ? 0 : part * nk_all / S;
+  const int nk = part < 0 ? nk_all : (part + 1) * nk_all / S;
+  load_tile(kt0 * BK);
   store_tile();
   __syncthreads();
-  const int nk = KD / BK;
-  for (int kt = 0; kt < nk; ++kt) {
+  for (int kt = kt0; kt < nk; ++kt) {
     if (kt + 1 < nk) load_tile((kt + 1) * BK);
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 16) {
@@ -181,6 +216,63 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_bf16(GroupedGemmArgs g)
       store_tile();
       __syncthreads();
     }
+  }
+
+  // ---- a part of a split tile: store its partial sums (at device scope, past the per-XCD L2s), count
+  // itself, and leave unless it is the last part of its tile to arrive; that one adds the S partial
+  // sums in part order, its own read back like the others' (the same sums whichever part arrives
+  // last), and runs the epilogue.
+  if (part >= 0) {
+    const int tile = L - W;  // the split tile's index, 0 .. R - 1
+    float* const mine = g.split_part + (size_t)(tile * S + part) * kSplitFloats;
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          __hip_atomic_store(mine + ((mi * NB + nb) * 16 + r) * 256 + tid, acc[mi][nb][r], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);  // the stores are complete
+    __syncthreads();
+    if (tid == 0) {
+      // count this part: the word is (split_seq, parts arrived), or anything else before the first part
+      unsigned long long* const w = g.split_cnt + tile;
+      const unsigned long long tag = (unsigned long long)g.split_seq << 32;
+      unsigned long long old = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), nw;
+      do {
+        nw = (old & 0xFFFFFFFF00000000ull) == tag ? old + 1 : tag + 1;
+      } while (!__hip_atomic_compare_exchange_strong(w, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT));
+      s_last = (int)(nw & 0xFFFFFFFFu) == S;
+      if (s_last) __hip_atomic_store(w, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    // 16 accumulators at a time: every part's 16 values are loaded before the first add, so a group
+    // costs one memory round trip (parts past S reload part S - 1 and add nothing)
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        float v[kSplitParts][16];
+#pragma unroll
+        for (int q = 0; q < kSplitParts; ++q) {
+          const float* src = g.split_part + (size_t)(tile * S + min(q, S - 1)) * kSplitFloats +
+                             (mi * NB + nb) * 16 * 256 + tid;
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            v[q][r] = __hip_atomic_load(src + r * 256, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float sum = 0.f;
+#pragma unroll
+          for (int q = 0; q < kSplitParts; ++q)
+            if (q < S) sum += v[q][r];
+          acc[mi][nb][r] = sum;
+        }
+      }
   }
 
   // ---- epilogue.  32x32 MFMA D layout: lane l, item r -> row 8*(r/4) + 4*(l/32) + r%4, column l%32
@@ -216,7 +308,8 @@ static bool a_is_wide(const GroupedGemmArgs& g) {
 
 template <int STAGE>
 static void launch_stage(const GroupedGemmArgs& g, int cols, hipStream_t s) {
-  const dim3 grid(grouped_grid(g, gemm_groups(g, STAGE == 0 ? 0 : 1, cols), BM));
+  // a split adds at most `slots` blocks (the parts of the last round's tiles) to the tiles' blocks
+  const dim3 grid(grouped_grid(g, gemm_groups(g, STAGE == 0 ? 0 : 1, cols), BM) + (g.slots > 0 ? g.slots : 0));
   if (a_is_wide(g)) k_grouped_gemm_bf16<STAGE, uint64_t><<<grid, 256, 0, s>>>(g);
   else k_grouped_gemm_bf16<STAGE, uint32_t><<<grid, 256, 0, s>>>(g);
 }

@@ -84,7 +84,19 @@ struct GroupedGemmArgs {
   void* sh_out;
   float* sh_out_scales;
   int row_invariant;   // 1: only the kernels whose per-row arithmetic is the same at any row count
+  // Splitting the last, partial round of tiles along K (bf16 tile kernel): `slots` blocks of the kernel
+  // fit on the GPU at once (0: never split); split_part holds the parts' fp32 partial sums
+  // (kSplitSlots x kSplitFloats) and split_cnt their arrival counters (kSyncSplitMax 64-bit words, any
+  // contents: a word counts only while its high half holds split_seq, a nonzero value of this launch
+  // that differs from the previous launch's; the last part of a tile puts its word back to 0).
+  int slots;
+  uint32_t split_seq;
+  float* split_part;
+  unsigned long long* split_cnt;
 };
+// Limits of the K split: at most kSplitParts parts per tile, kSplitSlots parts per launch, each part's
+// partial tile kSplitFloats fp32 (256 threads x 128 accumulators).
+constexpr int kSplitParts = 4, kSplitSlots = 512, kSplitFloats = 256 * 128;
 hipError_t launch_grouped_gemm_bf16(const GroupedGemmArgs& g, hipStream_t s);
 // bf16 streaming kernel for a few rows per expert (decode)
 bool decode_gemm_fits(const GroupedGemmArgs& g);
@@ -110,7 +122,10 @@ constexpr int kSyncReduced = 1536;      // column blocks reduced
 constexpr int kSyncError = 1537;        // set to 1 when a bounded wait expires; the launch never clears it
 constexpr int kSyncRouteFlags = 1538;   // [kSyncRouteMaxFlags]: the one-launch decode prelude's block flags
 constexpr int kSyncRouteMaxFlags = 128;
-constexpr int kSyncInts = kSyncRouteFlags + kSyncRouteMaxFlags;
+constexpr int kSyncSplit = kSyncRouteFlags + kSyncRouteMaxFlags;  // [kSyncSplitMax] 64-bit: split tiles' arrivals
+constexpr int kSyncSplitMax = kSplitSlots / 2;                     // a split tile has at least two parts
+constexpr int kSyncInts = kSyncSplit + 2 * kSyncSplitMax;
+static_assert(kSyncSplit % 2 == 0, "64-bit counters");
 // Routed gate/up, down and the unpermute-reduce of a decode layer in one launch (the shared expert,
 // if any, must already be in r.shared_y).  sync: kSyncInts int32 whose counters hold zeros when the
 // launch starts; the launch leaves them zero (and sets sync[kSyncError] if a wait expired).

@@ -49,6 +49,14 @@ SMALL = {
                              shared_gated=True),
     # H = 384 (not a multiple of 256): the routed and shared down GEMMs take the 128-column tiles
     "h384_128col_down_200tok": W("h384", 200, 384, 8, 8, 2, 256, 128, "softmax", True, 1.0, "bf16", False, seed=26),
+    # 2048 routed rows, K 4096 in one GEMM: its tiles fill less than half of the GPU, so each is split
+    # along K (gate/up here, down in the next case)
+    "split_gate_up_1024tok": W("splitg", 1024, 4096, 8, 8, 2, 256, 0, "softmax", True, 1.0, "bf16", False, seed=27),
+    "split_down_1024tok": W("splitd", 1024, 256, 8, 8, 2, 4096, 0, "softmax", True, 1.0, "bf16", False, seed=29),
+    # 768 gate/up tiles (256 experts x 3 column tiles): one round of whole tiles, then a last round of 256
+    # tiles split in two along K
+    "split_last_round_2048tok": W("splitm", 2048, 4096, 256, 256, 2, 384, 0, "softmax", True, 1.0, "bf16", False,
+                                  seed=28),
 }
 FP8_SMALL = {
     "fp8_sigmoid_bias_shared": W("fp8s", 33, 512, 8, 8, 2, 256, 128, "sigmoid", True, 2.5, "fp8", True, seed=9),
@@ -538,8 +546,8 @@ def test_forward_matches_oracle_and_composed_stages(name):
     else:
         h = s("h")[:2 * P * wl.inter].view(torch.bfloat16)
     y = s("y")[:2 * P * H].view(torch.bfloat16)
-    moe.moe_grouped_gemm(cfg, 0, 0, w, a, a_sc, sid, offsets, h, hs)
-    moe.moe_grouped_gemm(cfg, 1, 0, w, h, hs, sid, offsets, y)
+    moe.moe_grouped_gemm(cfg, 0, 0, w, a, a_sc, sid, offsets, h, hs, ws=ws2)
+    moe.moe_grouped_gemm(cfg, 1, 0, w, h, hs, sid, offsets, y, ws=ws2)
     shy = None
     if wl.shared_inter:
         Is = wl.shared_inter
