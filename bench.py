@@ -50,16 +50,16 @@ CPU_SAMPLE_TOKENS = {"tiny": 16, "decode": 4, "prefill_zipf": 32, "fp8_sigmoid":
 # while its sources hash to the value they had when the counters were taken; otherwise the traffic is
 # reported as null.  The summaries the entries come from are in profiles/.
 MEASURED_TRAFFIC = {
-    ('tiny', 'experts'): {"kernel": "k_decode_fused", "grid": 128, "dispatches": 26, "fetch_kib": 1106.8, "write_kib": 50.0, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_decode.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/unpermute.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "49483644c2b21ad2f481df1186fc98c618f643a1b1499bdf0e6ad465e6fd58c4"},
-    ('decode', 'experts'): {"kernel": "k_decode_fused", "grid": 1384, "dispatches": 25, "fetch_kib": 140211.7, "write_kib": 231.0, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_decode.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/unpermute.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "49483644c2b21ad2f481df1186fc98c618f643a1b1499bdf0e6ad465e6fd58c4"},
-    ('prefill_zipf', 'gate_up'): {"kernel": "k_grouped_gemm_bf16<0, unsigned int>", "grid": 2312, "dispatches": 31, "fetch_kib": 616369.8, "write_kib": 49152.2, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_bf16.hip", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "0610c5a617257ada877715647db03d4bf573e618b7a51bafafbbae062ffa39f2"},
-    ('prefill_zipf', 'down'): {"kernel": "k_grouped_gemm_bf16<2, unsigned int>", "grid": 3080, "dispatches": 31, "fetch_kib": 258171.6, "write_kib": 131072.1, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_bf16.hip", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "0610c5a617257ada877715647db03d4bf573e618b7a51bafafbbae062ffa39f2"},
-    ('zero_experts', 'gate_up'): {"kernel": "k_grouped_gemm_bf16<0, unsigned int>", "grid": 4880, "dispatches": 26, "fetch_kib": 1767952.1, "write_kib": 19017.4, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_bf16.hip", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "0610c5a617257ada877715647db03d4bf573e618b7a51bafafbbae062ffa39f2"},
-    ('zero_experts', 'down'): {"kernel": "k_grouped_gemm_bf16<2, unsigned int>", "grid": 7320, "dispatches": 26, "fetch_kib": 784803.4, "write_kib": 57051.1, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_bf16.hip", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "0610c5a617257ada877715647db03d4bf573e618b7a51bafafbbae062ffa39f2"},
-    ('fp8_sigmoid', 'gate_up'): {"kernel": "k_grouped_gemm_fp8_stream<0>", "grid": 6160, "dispatches": 6, "fetch_kib": 2413650.8, "write_kib": 36014.0, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_fp8.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "4ad41382eebc4983e5a9760f5949428e3030e1b09035d3b8cb994e5e4e0545f5"},
-    ('fp8_sigmoid', 'down'): {"kernel": "k_grouped_gemm_fp8_stream<1>", "grid": 10784, "dispatches": 26, "fetch_kib": 1077275.8, "write_kib": 229376.0, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_fp8.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "4ad41382eebc4983e5a9760f5949428e3030e1b09035d3b8cb994e5e4e0545f5"},
-    ('mxfp4_sigmoid', 'gate_up'): {"kernel": "k_grouped_gemm_mxfp4<0, true>", "grid": 6160, "dispatches": 6, "fetch_kib": 1520504.5, "write_kib": 35700.8, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_mxfp4.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "77dc683aacc709f783f875f94fc289b0431236ab065732a57c2cd483a9edb315"},
-    ('mxfp4_sigmoid', 'down'): {"kernel": "k_grouped_gemm_mxfp4<1, false>", "grid": 21560, "dispatches": 6, "fetch_kib": 571149.9, "write_kib": 229376.1, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_mxfp4.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "77dc683aacc709f783f875f94fc289b0431236ab065732a57c2cd483a9edb315"},
+    ('tiny', 'experts'): {"kernel": "k_decode_fused", "grid": 128, "dispatches": 26, "fetch_kib": 1107.1, "write_kib": 50.0, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_decode.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/unpermute.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "56c6a079eacfc42d9510005fff76e5808fea9701e0436615071c897f7bb40d0b"},
+    ('decode', 'experts'): {"kernel": "k_decode_fused", "grid": 1384, "dispatches": 25, "fetch_kib": 140212.3, "write_kib": 231.0, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_decode.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/unpermute.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "56c6a079eacfc42d9510005fff76e5808fea9701e0436615071c897f7bb40d0b"},
+    ('prefill_zipf', 'gate_up'): {"kernel": "k_grouped_gemm_bf16<0, unsigned int>", "grid": 2312, "dispatches": 31, "fetch_kib": 621239.9, "write_kib": 49152.1, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_bf16.hip", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "6f3a7635da3c6b8baab975dd4e3d763252c0ae81352586d9fe6a3734f5b18831"},
+    ('prefill_zipf', 'down'): {"kernel": "k_grouped_gemm_bf16<2, unsigned int>", "grid": 3080, "dispatches": 31, "fetch_kib": 259505.6, "write_kib": 131072.1, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_bf16.hip", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "6f3a7635da3c6b8baab975dd4e3d763252c0ae81352586d9fe6a3734f5b18831"},
+    ('zero_experts', 'gate_up'): {"kernel": "k_grouped_gemm_bf16<0, unsigned int>", "grid": 5392, "dispatches": 26, "fetch_kib": 1771487.4, "write_kib": 47390.3, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_bf16.hip", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "6f3a7635da3c6b8baab975dd4e3d763252c0ae81352586d9fe6a3734f5b18831"},
+    ('zero_experts', 'down'): {"kernel": "k_grouped_gemm_bf16<2, unsigned int>", "grid": 7320, "dispatches": 26, "fetch_kib": 785270.3, "write_kib": 57051.1, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_bf16.hip", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "6f3a7635da3c6b8baab975dd4e3d763252c0ae81352586d9fe6a3734f5b18831"},
+    ('fp8_sigmoid', 'gate_up'): {"kernel": "k_grouped_gemm_fp8_stream<0>", "grid": 6160, "dispatches": 6, "fetch_kib": 2413868.5, "write_kib": 36017.9, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_fp8.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "f8166305c76f3cdd3b993edbc15d4d1d36315d5855d781fd29fd6f3544b43b4a"},
+    ('fp8_sigmoid', 'down'): {"kernel": "k_grouped_gemm_fp8_stream<1>", "grid": 10784, "dispatches": 26, "fetch_kib": 1077028.4, "write_kib": 229376.0, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_fp8.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "f8166305c76f3cdd3b993edbc15d4d1d36315d5855d781fd29fd6f3544b43b4a"},
+    ('mxfp4_sigmoid', 'gate_up'): {"kernel": "k_grouped_gemm_mxfp4<0, true>", "grid": 6160, "dispatches": 6, "fetch_kib": 1512008.4, "write_kib": 35711.4, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_mxfp4.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "775827e3a4c54e4e3d3ee7c32bd04568245b1887b27019c8643763a09cd9ca31"},
+    ('mxfp4_sigmoid', 'down'): {"kernel": "k_grouped_gemm_mxfp4<1, false>", "grid": 21560, "dispatches": 6, "fetch_kib": 571076.7, "write_kib": 229376.1, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_mxfp4.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "775827e3a4c54e4e3d3ee7c32bd04568245b1887b27019c8643763a09cd9ca31"},
 }
 
 
