@@ -183,7 +183,8 @@ void compute_layout(const moe_config_t* c, moe_workspace_layout_t* L) {
   L->sorted_ids = take(P * 4);
   L->inv_perm = take(P * 4);
   const int slices = moe::router_slices((int)N, (int)H, (int)R, c->row_invariant != 0);
-  const size_t hist_bytes = ((size_t)moe::permute_chunks((int)P) + 1) * R * 4;  // chunk histograms + bucket totals
+  // chunk histograms (rows padded to 4 ints) + bucket totals
+  const size_t hist_bytes = ((size_t)moe::permute_chunks((int)P) + 1) * ((R + 3) / 4 * 4) * 4;
   const size_t part_bytes = slices > 1 ? (size_t)slices * N * R * 4 : 0;
   L->scratch = take(hist_bytes > part_bytes ? hist_bytes : part_bytes);
   L->xq = fp8 ? take(N * H) : none;

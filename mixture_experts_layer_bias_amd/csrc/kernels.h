@@ -43,8 +43,10 @@ hipError_t launch_route_small(const uint16_t* x, const uint16_t* router_w, float
                               int N, int H, int R, int E, int K, int scoring, int renormalize, float routed_scale,
                               hipStream_t s);
 
-// a3: stable counting sort by expert; hist is [(permute_chunks(P) + 1) * R] int32 scratch
+// a3: stable counting sort by expert; hist is [(permute_chunks(P) + 1) * 4 ceil(R / 4)] int32 scratch.  Two
+// launches when permute_direct(P, R), else three.
 int permute_chunks(int P);
+bool permute_direct(int P, int R);
 hipError_t launch_permute(const int32_t* ids, int P, int R, int32_t* counts, int32_t* offsets, int32_t* sorted_ids,
                           int32_t* inv_perm, int32_t* hist, hipStream_t s);
 

@@ -216,12 +216,17 @@ def test_stages_match_oracle(name):
     assert_close(f64(out), res.out_f64, BF16_TOL, "unpermute-reduce output")
 
 
-@pytest.mark.parametrize("P,R,K", [(100_003, 1024, 1), (65_536, 7, 4), (2_560, 384, 10), (257, 128, 1), (1, 1, 1)])
+@pytest.mark.parametrize("P,R,K", [(100_003, 1024, 1), (65_536, 7, 4), (2_560, 384, 10), (257, 128, 1), (1, 1, 1),
+                                   (32_768, 128, 8), (16_384, 256, 8), (65_536, 128, 8), (65_537, 128, 1)])
 def test_permute_bit_exact_many_chunks(P, R, K):
     """The stable sort by expert, bit for bit against numpy's stable argsort, at
     sizes spanning many 256-row chunks, the widest router (1024 buckets, every id
     bit in use), a ragged last chunk, a single row and a single bucket.  Ids are
-    Zipf-skewed so that some buckets are long and many are empty."""
+    Zipf-skewed so that some buckets are long and many are empty.  Sorts of up
+    to 8192 chunk-quad counts (256-row chunks x ceil(R / 4)) take two launches,
+    the scatter blocks adding up the chunk counts themselves (65536 x 128 sits at
+    that limit); 65537 x 128 and 100003 x 1024 take three.  The workspace starts
+    as all-ones bytes and the sort runs twice on it."""
     print(f"\n[case] permute P={P} R={R} K={K}", flush=True)
     N = (P + K - 1) // K
     rng = np.random.default_rng(1000 + R)
@@ -232,15 +237,18 @@ def test_permute_bit_exact_many_chunks(P, R, K):
     Pn = N * K
     counts, offsets = _alloc((R,), torch.int32), _alloc((R + 1,), torch.int32)
     sorted_ids, inv_perm = _alloc((Pn,), torch.int32), _alloc((Pn,), torch.int32)
-    ws = _alloc(moe.moe_workspace_size(cfg), torch.uint8)
-    moe.moe_permute(cfg, ids, counts, offsets, sorted_ids, inv_perm, ws)
-    torch.cuda.synchronize()
-    c_, o_, s_, i_ = (t.cpu().numpy() for t in (counts, offsets, sorted_ids, inv_perm))
+    ws = torch.full((moe.moe_workspace_size(cfg),), 255, dtype=torch.uint8, device="cuda")
     ref_c = np.bincount(flat, minlength=R)
-    assert np.array_equal(c_, ref_c)
-    assert np.array_equal(o_, np.concatenate([[0], np.cumsum(ref_c)]))
-    assert np.array_equal(s_, np.argsort(flat, kind="stable"))
-    assert np.array_equal(i_[s_], np.arange(Pn))
+    for call in range(2):
+        for t in (counts, offsets, sorted_ids, inv_perm):
+            t.fill_(-1)
+        moe.moe_permute(cfg, ids, counts, offsets, sorted_ids, inv_perm, ws)
+        torch.cuda.synchronize()
+        c_, o_, s_, i_ = (t.cpu().numpy() for t in (counts, offsets, sorted_ids, inv_perm))
+        assert np.array_equal(c_, ref_c), f"call {call}"
+        assert np.array_equal(o_, np.concatenate([[0], np.cumsum(ref_c)])), f"call {call}"
+        assert np.array_equal(s_, np.argsort(flat, kind="stable")), f"call {call}"
+        assert np.array_equal(i_[s_], np.arange(Pn)), f"call {call}"
 
 
 # ============================================================================ fp8 stages
@@ -767,10 +775,14 @@ def test_full_size_matches_oracle(name):
     print(f"max|gpu - oracle| / max|oracle| over all {N} x {wl.hidden} outputs: {err:.3g}", flush=True)
 
 
-def test_forward_replays_from_a_hip_graph():
+@pytest.mark.parametrize("name", ["decode", "many_tiles_300tok", "split_last_round_2048tok"])
+def test_forward_replays_from_a_hip_graph(name):
     """moe_forward captured into a graph: every replay equals the eager result,
-    with eager work and synchronisations between replays."""
-    wl = SMALL["decode"]
+    with eager work and synchronisations between replays.  The cases take the
+    one-launch decode path, the sort's one-launch count + scan, and a K split of
+    the last round of tiles: the replays repeat their launches' tags."""
+    print(f"\n[case] graph replay {name}", flush=True)
+    wl = SMALL[name]
     dl = mi.device.device_layer(wl)
     cfg, w = config_of(wl), weights_of(dl)
     ref, ws = run_forward(cfg, w, dl.x)
