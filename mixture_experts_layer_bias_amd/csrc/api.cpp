@@ -22,6 +22,21 @@
 
 namespace moe {
 
+// Compute units of the current device (looked up once per device); 0 if it cannot be queried.
+int device_cus() {
+  static std::mutex mu;
+  static std::map<int, int> per_device;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = per_device.find(dev);
+  if (it != per_device.end()) return it->second;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 0;
+  per_device[dev] = cus;
+  return cus;
+}
+
 hipError_t ensure_dynamic_lds(const void* kernel, int bytes) {
   static std::mutex mu;
   static std::set<std::pair<const void*, int>> done;  // (kernel, device)
@@ -61,22 +76,10 @@ uint32_t next_split_seq() {
   }
 }
 
+
 // Blocks of the bf16 tile kernel (two per compute unit) that the current device holds at once, a
 // multiple of 8 and at most kSplitSlots; 0 if the device cannot be queried.
-int split_slots() {
-  static std::mutex mu;
-  static std::map<int, int> per_device;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  std::lock_guard<std::mutex> lock(mu);
-  auto it = per_device.find(dev);
-  if (it != per_device.end()) return it->second;
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 0;
-  const int slots = std::min(2 * cus, moe::kSplitSlots) / 8 * 8;
-  per_device[dev] = slots;
-  return slots;
-}
+int split_slots() { return std::min(2 * ::moe::device_cus(), moe::kSplitSlots) / 8 * 8; }
 
 moe_status_t fail(moe_status_t st, const char* fmt, ...) {
   va_list ap;

@@ -524,11 +524,258 @@ __global__ __launch_bounds__(StreamWaves<STAGE>::WAVES * 64, 1) void k_grouped_g
   }
 }
 
+// ---- the streaming down stage with persistent blocks, one per CU
+//
+// The same tiles, ring, MFMAs and promotions as k_grouped_gemm_fp8_stream<1> (so the same bits), but
+// block b of XCD x = b % 8 walks the tiles b / 8, b / 8 + S, ... (S blocks per XCD) of that XCD's
+// contiguous range of logical tiles, and the ring does not drain between them: at the first K step
+// of a tile the block finds its next tile and starts loading that tile's weight-block scales (into
+// the other of two LDS buffers), and the last two K steps issue the next tile's first two stages.
+// The tile prefix is built once per block.  A down tile streams 16 K steps in ~10 us, so the
+// per-tile scheduler, first-stage latency and epilogue of the one-tile-per-block kernel cost a
+// large share of its time.
+constexpr int P_WS_OFF = SNSTAGE * SSTAGE;                   // [2 buffers][2 column blocks][SMAXKB]
+constexpr int P_PREFIX_OFF = P_WS_OFF + 2 * 2 * SMAXKB * 4;  // tile prefix + 4 words of scan scratch
+constexpr int PLDS = P_PREFIX_OFF + (kMaxGroups + 1 + 4) * 4;
+static_assert(PLDS <= 160 * 1024, "one block per CU");
+
+// One tile of the persistent down kernel: wave-uniform place and this lane's operand addresses.
+struct DownTile {
+  int expert, n_tile, row0, row_end, KB, live_mi, sh;
+  const uint8_t* a_ptr[StreamWaves<1>::AI];  // this lane's A chunks
+  const uint8_t* b_ptr[StreamWaves<1>::BI];  // this lane's B chunks
+  const float* sc_ptr;                       // this lane's row scales
+};
+
+__global__ __launch_bounds__(StreamWaves<1>::WAVES * 64, 1) void k_grouped_gemm_fp8_down_persistent(GroupedGemmArgs g) {
+  using W = StreamWaves<1>;
+  constexpr int SWR = W::WR, SMI = W::MI, SAR = W::AR, SAI = W::AI, SBR = W::BR, SBI = W::BI, SVM = W::VM;
+  extern __shared__ __align__(16) uint8_t smem[];
+  float* s_ws = reinterpret_cast<float*>(smem + P_WS_OFF);  // [buffer][column block][SMAXKB]
+  int* s_prefix = reinterpret_cast<int*>(smem + P_PREFIX_OFF);
+  int* s_wsum = s_prefix + kMaxGroups + 1;
+
+  const Groups G = gemm_groups(g, 1, SBNB);
+  const int T = tile_prefix(G, SBM, s_prefix, s_wsum);
+  // this block's tiles: XCD x's range [x chunk, min((x + 1) chunk, T)), every S-th from b / 8
+  const int S = (int)gridDim.x / 8, x = blockIdx.x % 8;
+  const int chunk = (T + 7) / 8;
+  const int t_end = min((x + 1) * chunk, T);
+  int L = x * chunk + (int)blockIdx.x / 8;
+  if (L >= t_end) return;  // the same decision in every thread
+
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int prow = lane >> 3;
+  auto lch = [&](int lds_row) { return (lane & 7) ^ ((lds_row >> 1) & 7); };
+
+  // the place of tile Lt, and direct-to-LDS loads of its weight-block scales (the tile's two column
+  // blocks: waves 2 and 3, one lane per K block) into buffer buf; a later ring wait covers the loads
+  auto prepare = [&](int Lt, DownTile& t, int buf) {
+    const TileCoord tc = tile_at(G, SBM, s_prefix, T, Lt, 32);
+    t.expert = __builtin_amdgcn_readfirstlane(tc.expert);
+    t.n_tile = __builtin_amdgcn_readfirstlane(tc.n_tile);
+    t.row0 = __builtin_amdgcn_readfirstlane(tc.row0);
+    t.row_end = __builtin_amdgcn_readfirstlane(tc.row_end);
+    t.sh = t.expert == G.nr;
+    t.KB = (t.sh ? g.Is : g.I) / 128;
+    t.live_mi = 0;
+#pragma unroll
+    for (int mi = 0; mi < SMI; ++mi) t.live_mi += t.row0 + wm * SWR + mi * 32 < t.row_end;
+    if (wave == 2 || wave == 3) {
+      const int which = wave - 2, kb = lane;
+      if (kb < t.KB) {
+        const float* src = (t.sh ? g.sh_down_s : g.s_down[t.expert]) + (size_t)(2 * t.n_tile + which) * t.KB;
+        __builtin_amdgcn_global_load_lds((dma_gptr_t)(src + kb), (dma_lptr_t)(s_ws + (buf * 2 + which) * SMAXKB), 4,
+                                         0, 0);
+      }
+    }
+  };
+  // this lane's operand addresses for tile t (the same as the one-tile kernel's)
+  auto addresses = [&](DownTile& t) {
+    const int KD = t.sh ? g.Is : g.I;
+    auto a_row = [&](int trow) -> long {
+      int p = t.row0 + trow;
+      if (p >= t.row_end) p = t.row_end - 1;  // rows past the segment are computed, never stored
+      return p;
+    };
+#pragma unroll
+    for (int i = 0; i < SAI; ++i) {
+      const int r = wave * SAR + 8 * i + prow;
+      t.a_ptr[i] = static_cast<const uint8_t*>(t.sh ? g.sh_a : g.a) + (size_t)a_row(r) * KD + (lch(r) << 4);
+    }
+    const uint8_t* wd = static_cast<const uint8_t*>(t.sh ? g.sh_down : g.w_down[t.expert]);
+#pragma unroll
+    for (int i = 0; i < SBI; ++i) {
+      const int r = wave * SBR + 8 * i + prow;
+      t.b_ptr[i] = wd + (size_t)(t.n_tile * SBNB + r) * KD + (lch(r) << 4);
+    }
+    t.sc_ptr = (t.sh ? g.sh_a_scales : g.a_scales) + (size_t)a_row(wave * SAR + (lane % SAR)) * t.KB;
+  };
+  auto issue = [&](const DownTile& t, int slot, int kb) {
+    uint8_t* sa = smem + slot * SSTAGE;
+    uint8_t* sb = sa + SABYTES;
+    uint8_t* ss = sb + SBBYTES;
+    const size_t koff = (size_t)kb * SROWB;
+#pragma unroll
+    for (int i = 0; i < SAI; ++i) dma16(t.a_ptr[i] + koff, sa + (wave * SAI + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < SBI; ++i) dma16(t.b_ptr[i] + koff, sb + (wave * SBI + i) * 1024);
+    if (lane < SAR)
+      __builtin_amdgcn_global_load_lds((dma_gptr_t)(t.sc_ptr + kb), (dma_lptr_t)(ss + wave * SAR * 4), 4, 0, 0);
+  };
+  auto lds16 = [&](const uint8_t* base, int row, int chunk) {
+    return *reinterpret_cast<const u32x4*>(base + row * SROWB + ((chunk ^ ((row >> 1) & 7)) << 4));
+  };
+  const int frow = lane & 31, fh = lane >> 5;
+  auto item_row = [&](int r) { return 8 * (r / 4) + 4 * fh + (r % 4); };
+  auto brow = [&](int nb) { return wn * 64 + nb * 32 + frow; };
+  const int ws_row0 = (wn * 64) / 128, ws_row1 = (wn * 64 + 32) / 128;
+
+  // the first tile: found, its scales loaded and its first two stages issued
+  DownTile cur, nxt;
+  int buf = 0;
+  prepare(L, cur, buf);
+  addresses(cur);
+  int gs = 0;  // ring stage of the current tile's K step 0
+#pragma unroll
+  for (int s = 0; s < SNSTAGE - 1; ++s)
+    if (s < cur.KB) issue(cur, s, s);
+
+  for (;;) {
+    const int Lnext = L + S;
+    const bool has_next = Lnext < t_end;
+    bool cross = false;  // the next tile's first stages come from this tile's last two steps
+    f32x16 acc[SMI][2], blk[SMI][2];
+#pragma unroll
+    for (int mi = 0; mi < SMI; ++mi)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mi][nb][r] = 0.f;
+
+    for (int kb = 0; kb < cur.KB; ++kb) {
+      const bool later = cross || kb + 1 < cur.KB;  // a stage was issued after this one
+      if (later) dma_wait<SVM>();  // step kb has landed (the one stage after it may still be in flight)
+      else dma_wait<0>();
+      __builtin_amdgcn_s_barrier();  // ... in every wave; every wave is done with step kb - 1
+      __builtin_amdgcn_sched_barrier(0);
+      if (kb + SNSTAGE - 1 < cur.KB) {
+        issue(cur, (gs + kb + SNSTAGE - 1) % SNSTAGE, kb + SNSTAGE - 1);
+      } else if (cross) {
+        // the next tile's K step kb + 2 - KB (its addresses taken here, not kept live through the loop)
+        DownTile t = nxt;
+        addresses(t);
+        issue(t, (gs + kb + SNSTAGE - 1) % SNSTAGE, kb + SNSTAGE - 1 - cur.KB);
+      }
+      if (kb == 0 && has_next && cur.KB >= 4) {
+        // after this step's issue; its scale loads are older than step 3's stage, so they have landed
+        // by the wait of step 2 of ... this tile (KB >= 4), long before the next tile reads them
+        prepare(Lnext, nxt, buf ^ 1);
+        cross = nxt.KB >= 2;
+      }
+      if (cur.live_mi == 0) continue;
+      const uint8_t* sa = smem + ((gs + kb) % SNSTAGE) * SSTAGE;
+      const uint8_t* sb = sa + SABYTES;
+      const float* ss = reinterpret_cast<const float*>(sb + SBBYTES);
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int c0 = 4 * ks + 2 * fh;
+        i32x8 af[SMI], bf[2];
+#pragma unroll
+        for (int mi = 0; mi < SMI; ++mi) {
+          if (mi >= cur.live_mi) continue;
+          const int row = wm * SWR + mi * 32 + frow;
+          const u32x4 lo = lds16(sa, row, c0), hi = lds16(sa, row, c0 + 1);
+          af[mi] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        }
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const u32x4 lo = lds16(sb, brow(nb), c0), hi = lds16(sb, brow(nb), c0 + 1);
+          bf[nb] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        }
+#pragma unroll
+        for (int mi = 0; mi < SMI; ++mi)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            if (mi >= cur.live_mi) continue;
+            if (ks == 0) blk[mi][nb] = mfma_32x32x64_fp8(af[mi], bf[nb], f32x16{});
+            else blk[mi][nb] = mfma_32x32x64_fp8(af[mi], bf[nb], blk[mi][nb]);
+          }
+      }
+      __builtin_amdgcn_s_setprio(0);
+      const float ws0 = s_ws[(buf * 2 + ws_row0) * SMAXKB + kb], ws1 = s_ws[(buf * 2 + ws_row1) * SMAXKB + kb];
+#pragma unroll
+      for (int mi = 0; mi < SMI; ++mi) {
+        if (mi >= cur.live_mi) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 rs = *reinterpret_cast<const f32x4*>(ss + wm * SWR + mi * 32 + 8 * q + 4 * fh);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            acc[mi][0][4 * q + j] += blk[mi][0][4 * q + j] * (rs[j] * ws0);
+            acc[mi][1][4 * q + j] += blk[mi][1][4 * q + j] * (rs[j] * ws1);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    {
+      uint16_t* out = static_cast<uint16_t*>(cur.sh ? g.sh_out : g.out);
+      const int n0 = cur.n_tile * SBNB;
+#pragma unroll
+      for (int mi = 0; mi < SMI; ++mi)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = cur.row0 + wm * SWR + mi * 32 + item_row(r);
+          if (row >= cur.row_end) continue;
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+            out[(size_t)row * g.H + n0 + wn * 64 + nb * 32 + frow] = (uint16_t)f32_to_bf16(acc[mi][nb][r]);
+        }
+    }
+
+    if (!has_next) break;
+    gs += cur.KB;
+    L = Lnext;
+    buf ^= 1;
+    if (cross) {
+      cur = nxt;
+      addresses(cur);
+    } else {
+      // not started ahead (a short tile): find it now and issue its first stages.  Every wave is past
+      // the last step's barrier, so no wave still reads the ring stages these loads overwrite... the
+      // ones of steps KB - 1 and KB - 2 may be read by a slower wave: wait for all before reusing them.
+      __syncthreads();
+      prepare(L, cur, buf);
+      addresses(cur);
+#pragma unroll
+      for (int s = 0; s < SNSTAGE - 1; ++s)
+        if (s < cur.KB) issue(cur, (gs + s) % SNSTAGE, s);
+    }
+  }
+}
+
 template <int STAGE>
 hipError_t launch_stream(const GroupedGemmArgs& g, hipStream_t s) {
+  const unsigned grid = grouped_grid(g, gemm_groups(g, STAGE, STAGE == 0 ? SBNB / 2 : SBNB), SBM);
+  if (STAGE == 1) {
+    // one block per CU, a multiple of 8 (the XCDs), and no more than the tiles can use
+    const int cus = device_cus();
+    if (cus >= 8) {
+      const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&k_grouped_gemm_fp8_down_persistent), PLDS);
+      if (e != hipSuccess) return e;
+      unsigned pgrid = (unsigned)(cus / 8 * 8);
+      if (grid < pgrid) pgrid = grid;  // grouped_grid is a multiple of 8
+      k_grouped_gemm_fp8_down_persistent<<<pgrid, StreamWaves<1>::WAVES * 64, PLDS, s>>>(g);
+      return hipGetLastError();
+    }
+  }
   const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&k_grouped_gemm_fp8_stream<STAGE>), SLDS);
   if (e != hipSuccess) return e;
-  const unsigned grid = grouped_grid(g, gemm_groups(g, STAGE, STAGE == 0 ? SBNB / 2 : SBNB), SBM);
   k_grouped_gemm_fp8_stream<STAGE><<<grid, StreamWaves<STAGE>::WAVES * 64, SLDS, s>>>(g);
   return hipGetLastError();
 }

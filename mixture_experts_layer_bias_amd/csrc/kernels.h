@@ -10,6 +10,8 @@ namespace moe {
 // Raise a kernel's dynamic LDS limit to `bytes` on the current device, once per (kernel, device);
 // thread-safe.  Kernels that use more than the default dynamic LDS call this before each launch.
 hipError_t ensure_dynamic_lds(const void* kernel, int bytes);
+// compute units of the current device, looked up once per device (0 if it cannot be queried)
+int device_cus();
 
 // a1 + a2: router logits (split over `slices` parts of H, each writing an [N, R]
 // partial plane) and top-K selection (adds the planes in order; when slices > 1
