@@ -157,6 +157,49 @@ __device__ __forceinline__ TileCoord tile_at(const Groups& G, int BM, const int*
   return tc;
 }
 
+// tile_at for a wave-uniform L, with the segment bounds read by scalar loads: a kernel that keeps direct
+// global -> LDS loads in flight while it finds its next tile then waits only on those two words, not on
+// every vector load issued before them.  The same result as tile_at.
+__device__ __forceinline__ TileCoord tile_at_uniform(const Groups& G, int BM, const int* s_prefix, int T, int L,
+                                                     int split_align = 0) {
+  const int ngroups = G.nr + (G.xr > 0 ? 1 : 0);
+  TileCoord tc{-1, 0, 0, 0, 0, G.nt == G.xnt || G.xr == 0 ? T / G.nt : -1};
+  int lo = 0, hi = ngroups - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (s_prefix[mid] <= L) lo = mid;
+    else hi = mid - 1;
+  }
+  const int e = __builtin_amdgcn_readfirstlane(lo);
+  int seg0 = 0, seg_end = G.xr;
+  if (e < G.nr) {
+    typedef const int __attribute__((address_space(4)))* const_int_ptr;
+    const_int_ptr off = (const_int_ptr)(G.offsets);
+    seg0 = off[e];
+    seg_end = off[e + 1];
+  }
+  const int mt_e = (seg_end - seg0 + BM - 1) / BM;
+  const int rem = L - __builtin_amdgcn_readfirstlane(s_prefix[e]);
+  tc.expert = e;
+  tc.n_tile = rem / mt_e;
+  tc.m_tile = rem % mt_e;
+  int rpt = BM;
+  if (split_align > 0 && mt_e > 1) {
+    const int even = (seg_end - seg0 + mt_e - 1) / mt_e;
+    rpt = (even + split_align - 1) / split_align * split_align;
+  }
+  tc.row0 = seg0 + tc.m_tile * rpt;
+  tc.row_end = min(tc.row0 + rpt, seg_end);
+  return tc;
+}
+
+// Entry e (wave-uniform) of a device table of pointers, by a scalar load (see tile_at_uniform).
+template <typename T>
+__device__ __forceinline__ T* table_entry_uniform(T* const* table, int e) {
+  typedef T* const __attribute__((address_space(4)))* const_table;
+  return ((const_table)table)[e];
+}
+
 // The tile of block slot `b` (blockIdx.x unless one launch runs several grids of tiles), or expert -1
 // when the slot has none: tile_prefix, then the XCD-aware map of slots to logical tiles.  s_prefix must
 // hold kMaxGroups + 1 ints in LDS.

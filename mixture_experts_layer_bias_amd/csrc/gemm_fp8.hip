@@ -573,7 +573,7 @@ __global__ __launch_bounds__(StreamWaves<1>::WAVES * 64, 1) void k_grouped_gemm_
   // the place of tile Lt, and direct-to-LDS loads of its weight-block scales (the tile's two column
   // blocks: waves 2 and 3, one lane per K block) into buffer buf; a later ring wait covers the loads
   auto prepare = [&](int Lt, DownTile& t, int buf) {
-    const TileCoord tc = tile_at(G, SBM, s_prefix, T, Lt, 32);
+    const TileCoord tc = tile_at_uniform(G, SBM, s_prefix, T, Lt, 32);
     t.expert = __builtin_amdgcn_readfirstlane(tc.expert);
     t.n_tile = __builtin_amdgcn_readfirstlane(tc.n_tile);
     t.row0 = __builtin_amdgcn_readfirstlane(tc.row0);
@@ -586,7 +586,8 @@ __global__ __launch_bounds__(StreamWaves<1>::WAVES * 64, 1) void k_grouped_gemm_
     if (wave == 2 || wave == 3) {
       const int which = wave - 2, kb = lane;
       if (kb < t.KB) {
-        const float* src = (t.sh ? g.sh_down_s : g.s_down[t.expert]) + (size_t)(2 * t.n_tile + which) * t.KB;
+        const float* src =
+            (t.sh ? g.sh_down_s : table_entry_uniform(g.s_down, t.expert)) + (size_t)(2 * t.n_tile + which) * t.KB;
         __builtin_amdgcn_global_load_lds((dma_gptr_t)(src + kb), (dma_lptr_t)(s_ws + (buf * 2 + which) * SMAXKB), 4,
                                          0, 0);
       }
@@ -605,7 +606,7 @@ __global__ __launch_bounds__(StreamWaves<1>::WAVES * 64, 1) void k_grouped_gemm_
       const int r = wave * SAR + 8 * i + prow;
       t.a_ptr[i] = static_cast<const uint8_t*>(t.sh ? g.sh_a : g.a) + (size_t)a_row(r) * KD + (lch(r) << 4);
     }
-    const uint8_t* wd = static_cast<const uint8_t*>(t.sh ? g.sh_down : g.w_down[t.expert]);
+    const uint8_t* wd = static_cast<const uint8_t*>(t.sh ? g.sh_down : table_entry_uniform(g.w_down, t.expert));
 #pragma unroll
     for (int i = 0; i < SBI; ++i) {
       const int r = wave * SBR + 8 * i + prow;

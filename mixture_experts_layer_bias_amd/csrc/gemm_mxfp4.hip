@@ -377,6 +377,220 @@ __global__ __launch_bounds__(MxShape<STAGE>::WAVES * 64, STAGE == 0 ? 1 : 2) voi
   }
 }
 
+// ---- the down stage with persistent blocks, two per CU
+//
+// The same tiles, ring (three stages, the E8M0 codes and activation scales of each step riding in it),
+// MFMAs and promotions as k_grouped_gemm_mxfp4<1, false>, so the same bits; but block b of XCD x =
+// b % 8 walks the tiles b / 8, b / 8 + S, ... (S blocks per XCD) of that XCD's contiguous range of
+// logical tiles, and the ring does not drain between them: the last two K steps of a tile issue the next
+// tile's first two stages.  The tile prefix is built once per block (it stays in LDS after the ring).
+// A down tile streams 16 K steps in ~13 us, so the one-tile-per-block kernel's scheduler, first-stage
+// latency and epilogue are a large share of its time.
+using MxDn = MxShape<1, false>;
+constexpr int MXP_PREFIX_OFF = MxDn::NSTAGE * MxDn::SBYTES;
+constexpr int MXP_LDS = MXP_PREFIX_OFF + (kMaxGroups + 1 + 4) * 4;
+static_assert(2 * MXP_LDS <= 160 * 1024, "two blocks per CU");
+
+struct MxDownTile {
+  int expert, n_tile, row0, row_end, KB, live_mi, sh;
+  const uint8_t* a_ptr[MxDn::A_DMA];
+  const uint8_t* b_ptr[MxDn::B_DMA];
+  const uint8_t* bs_ptr;
+  const float* as_ptr;
+};
+
+__global__ __launch_bounds__(MX_DN_WAVES * 64, 2) void k_grouped_gemm_mxfp4_down_persistent(GroupedGemmArgs g) {
+  using S = MxDn;
+  constexpr int NSTAGE = S::NSTAGE, VM = S::VM, MI = S::MI, NI = S::NI;
+  constexpr int WR = BM / S::WM, WC = BN / S::WN;
+  extern __shared__ __align__(16) uint8_t smem[];
+  int* s_prefix = reinterpret_cast<int*>(smem + MXP_PREFIX_OFF);
+  int* s_wsum = s_prefix + kMaxGroups + 1;
+
+  const Groups G = gemm_groups(g, 1, BN);
+  const int T = tile_prefix(G, BM, s_prefix, s_wsum);
+  const int SB = (int)gridDim.x / 8, x = blockIdx.x % 8;  // blocks per XCD; this block's XCD
+  const int chunk = (T + 7) / 8;
+  const int t_end = min((x + 1) * chunk, T);
+  int L = x * chunk + (int)blockIdx.x / 8;
+  if (L >= t_end) return;  // the same decision in every thread
+
+  const int lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int wm = wave / S::WN, wn = wave % S::WN;
+  const int frow = lane & 31, half = lane >> 5;
+  auto item_row = [&](int r) { return 8 * (r / 4) + 4 * half + (r % 4); };
+  const int bs_rows = S::BROWS / S::WAVES;  // E8M0 rows per wave
+  const bool bs_lane = lane < bs_rows;
+  const int as_rows = BM / S::WAVES;        // activation-scale rows per wave
+  const bool as_lane = lane < as_rows;
+
+  // tile Lt: its place and this lane's load sources (as the one-tile kernel computes them)
+  auto prepare = [&](int Lt, MxDownTile& t) {
+    const TileCoord tc = tile_at_uniform(G, BM, s_prefix, T, Lt);
+    t.expert = __builtin_amdgcn_readfirstlane(tc.expert);
+    t.n_tile = __builtin_amdgcn_readfirstlane(tc.n_tile);
+    t.row0 = __builtin_amdgcn_readfirstlane(tc.row0);
+    t.row_end = __builtin_amdgcn_readfirstlane(tc.row_end);
+    t.sh = t.expert == G.nr;
+    const int KD = t.sh ? g.Is : g.I;
+    t.KB = KD / BK;
+    t.live_mi = 0;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) t.live_mi += t.row0 + wm * WR + mi * 32 < t.row_end;
+    auto a_row = [&](int trow) -> long {
+      int p = t.row0 + trow;
+      if (p >= t.row_end) p = t.row_end - 1;  // rows past the segment are computed, never stored
+      return p;
+    };
+    const uint8_t* a_src = static_cast<const uint8_t*>(t.sh ? g.sh_a : g.a);
+#pragma unroll
+    for (int i = 0; i < S::A_DMA; ++i) {
+      const int trow = (S::A_DMA * wave + i) * 8 + lane / 8;
+      t.a_ptr[i] = a_src + (size_t)a_row(trow) * KD + (((lane % 8) ^ ((trow >> 1) & 7)) << 4);
+    }
+    const uint8_t* wd = static_cast<const uint8_t*>(t.sh ? g.sh_down : table_entry_uniform(g.w_down, t.expert));
+    const uint8_t* sd =
+        reinterpret_cast<const uint8_t*>(t.sh ? g.sh_down_s : table_entry_uniform(g.s_down, t.expert));
+    const int n0 = t.n_tile * BN;
+#pragma unroll
+    for (int i = 0; i < S::B_DMA; ++i) {
+      const int wr = (S::B_DMA * wave + i) * 16 + lane / 4;
+      t.b_ptr[i] = wd + (size_t)(n0 + wr) * (KD / 2) + (((lane % 4) ^ ((wr >> 2) & 3)) << 4);
+    }
+    t.bs_ptr = sd + (size_t)(n0 + (bs_lane ? wave * bs_rows + lane : 0)) * (KD / 32);
+    t.as_ptr = (t.sh ? g.sh_a_scales : g.a_scales) + (size_t)a_row(as_lane ? wave * as_rows + lane : 0) * t.KB;
+  };
+  auto issue = [&](const MxDownTile& t, int slot, int kb) {
+    uint8_t* sa = smem + slot * S::SBYTES;
+    uint8_t* sb = sa + S::ABYTES;
+    uint8_t* sbs = sb + S::BBYTES;
+    uint8_t* sas = sbs + S::BSBYTES;
+#pragma unroll
+    for (int i = 0; i < S::A_DMA; ++i) dma16(t.a_ptr[i] + (size_t)kb * BK, sa + (S::A_DMA * wave + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < S::B_DMA; ++i) dma16(t.b_ptr[i] + (size_t)kb * (BK / 2), sb + (S::B_DMA * wave + i) * 1024);
+    if (bs_lane) dma4(t.bs_ptr + (size_t)kb * 4, sbs + wave * bs_rows * 4);
+    if (as_lane) dma4(t.as_ptr + kb, sas + wave * as_rows * 4);
+  };
+
+  MxDownTile cur, nxt;
+  prepare(L, cur);
+  int gs = 0;  // ring stage of the current tile's K step 0
+#pragma unroll
+  for (int s = 0; s < NSTAGE - 1; ++s)
+    if (s < cur.KB) issue(cur, s, s);
+
+  for (;;) {
+    const int Lnext = L + SB;
+    const bool has_next = Lnext < t_end;
+    bool cross = false;  // the next tile's first stages come from this tile's last two steps
+    if (has_next) {
+      prepare(Lnext, nxt);
+      cross = cur.KB >= NSTAGE - 1 && nxt.KB >= NSTAGE - 1;
+    }
+    f32x16 acc[MI][NI];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int nb = 0; nb < NI; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mi][nb][r] = 0.f;
+
+    for (int kb = 0; kb < cur.KB; ++kb) {
+      const int later = cross ? 1 : (kb + 1 < cur.KB ? 1 : 0);  // a stage was issued after step kb
+      wait_steps<NSTAGE, VM>(later);
+      __builtin_amdgcn_s_barrier();  // step kb has landed in every wave; every wave is done with kb - 1
+      __builtin_amdgcn_sched_barrier(0);
+      if (kb + NSTAGE - 1 < cur.KB) issue(cur, (gs + kb + NSTAGE - 1) % NSTAGE, kb + NSTAGE - 1);
+      else if (cross) issue(nxt, (gs + kb + NSTAGE - 1) % NSTAGE, kb + NSTAGE - 1 - cur.KB);
+      if (cur.live_mi == 0) continue;
+      const uint8_t* sa = smem + ((gs + kb) % NSTAGE) * S::SBYTES;
+      const uint8_t* sb = sa + S::ABYTES;
+      const uint32_t* bcodes = reinterpret_cast<const uint32_t*>(sb + S::BBYTES);
+      const float* ascale = reinterpret_cast<const float*>(sb + S::BBYTES + S::BSBYTES);
+      f32x16 blk[MI][NI];
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int nb = 0; nb < NI; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) blk[mi][nb][r] = 0.f;
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int kk = 0; kk < BK; kk += 64) {
+        i32x8 af[MI], bfr[NI];
+        int bsc[NI];
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) {
+          if (mi >= cur.live_mi) continue;
+          const int ar = wm * WR + mi * 32 + frow;
+          const uint8_t* rowp = sa + ar * BK;
+          const int c1 = kk / 16 + half, c2 = kk / 16 + 2 + half;
+          const u32x4 lo = *reinterpret_cast<const u32x4*>(rowp + ((c1 ^ ((ar >> 1) & 7)) << 4));
+          const u32x4 hi = *reinterpret_cast<const u32x4*>(rowp + ((c2 ^ ((ar >> 1) & 7)) << 4));
+          af[mi] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        }
+#pragma unroll
+        for (int nb = 0; nb < NI; ++nb) {
+          const int wr = wn * WC + nb * 32 + frow;
+          const int c = kk / 32 + half;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(sb + wr * (BK / 2) + ((c ^ ((wr >> 2) & 3)) << 4));
+          bfr[nb] = i32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+          bsc[nb] = (int)((bcodes[wr] >> (8 * c)) & 0xFFu);
+        }
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) {
+          if (mi >= cur.live_mi) continue;
+#pragma unroll
+          for (int nb = 0; nb < NI; ++nb) blk[mi][nb] = mfma_e4m3_x_e2m1(af[mi], bfr[nb], bsc[nb], blk[mi][nb]);
+        }
+      }
+      __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        if (mi >= cur.live_mi) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float rs = ascale[wm * WR + mi * 32 + item_row(r)];
+#pragma unroll
+          for (int nb = 0; nb < NI; ++nb) acc[mi][nb][r] += blk[mi][nb][r] * rs;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    {
+      uint16_t* out = static_cast<uint16_t*>(cur.sh ? g.sh_out : g.out);
+      const int n0 = cur.n_tile * BN;
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = cur.row0 + wm * WR + mi * 32 + item_row(r);
+          if (row >= cur.row_end) continue;
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni)
+            out[(size_t)row * g.H + n0 + wn * WC + ni * 32 + (lane % 32)] = (uint16_t)f32_to_bf16(acc[mi][ni][r]);
+        }
+    }
+
+    if (!has_next) break;
+    gs += cur.KB;
+    L = Lnext;
+    const bool was_cross = cross;
+    cur = nxt;
+    if (!was_cross) {
+      // a short tile on either side: the ring drained (the last step waited for everything); every wave
+      // must be past its last ring read before the next tile's first stages overwrite the ring
+      __syncthreads();
+#pragma unroll
+      for (int s = 0; s < NSTAGE - 1; ++s)
+        if (s < cur.KB) issue(cur, (gs + s) % NSTAGE, s);
+    }
+  }
+}
+
 }  // namespace
 
 template <int STAGE, bool WIN>
@@ -394,6 +608,17 @@ hipError_t launch_grouped_gemm_mxfp4(const GroupedGemmArgs& g, hipStream_t s) {
     // scale windows when every group's K steps come in whole windows (K = H for all of them)
     if ((g.H / BK) % WIN_STEPS == 0) return launch_mx<0, true>(g, s);
     return launch_mx<0, false>(g, s);
+  }
+  // down: persistent blocks, two per CU, a multiple of 8 (the XCDs) and no more than the tiles can use
+  const int cus = device_cus();
+  if (cus >= 8) {
+    const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&k_grouped_gemm_mxfp4_down_persistent), MXP_LDS);
+    if (e != hipSuccess) return e;
+    unsigned grid = (unsigned)(2 * cus / 8 * 8);
+    const unsigned tiles = grouped_grid(g, gemm_groups(g, 1, BN), BM);  // a multiple of 8
+    if (tiles < grid) grid = tiles;
+    k_grouped_gemm_mxfp4_down_persistent<<<grid, MX_DN_WAVES * 64, MXP_LDS, s>>>(g);
+    return hipGetLastError();
   }
   return launch_mx<1, false>(g, s);
 }
