@@ -26,6 +26,7 @@
 namespace moe {
 
 constexpr int kMaxGroups = 1024;
+constexpr int kMaxSchedWaves = 16;  // tile_prefix's s_wsum: one int per wave of the block, at most this many
 
 // The groups of one launch: routed groups [0, nr) read from offsets, then, if xr > 0, one more group
 // (index nr) of rows [0, xr): the shared expert.
@@ -67,8 +68,9 @@ __device__ __forceinline__ int group_rows(const Groups& G, int e) {
 
 // The tile prefix of a launch's groups: s_prefix[e] = tiles (row tiles x column tiles) of the groups
 // before e, s_prefix[ngroups] = all tiles, which is returned to every thread.  s_prefix holds at least
-// ngroups + 1 ints of LDS (ngroups = G.nr + (G.xr > 0) <= kMaxGroups); block of at least 256 threads,
-// all of which call.
+// ngroups + 1 ints of LDS (ngroups = G.nr + (G.xr > 0) <= kMaxGroups), s_wsum one int per wave (every
+// wave writes its sum, the groups' sums being in the first four); block of 256 to 64 kMaxSchedWaves
+// threads, all of which call.
 __device__ __forceinline__ int tile_prefix(const Groups& G, int BM, int* s_prefix, int* s_wsum) {
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int ngroups = G.nr + (G.xr > 0 ? 1 : 0);

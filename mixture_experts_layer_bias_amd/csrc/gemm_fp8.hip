@@ -535,8 +535,8 @@ __global__ __launch_bounds__(StreamWaves<STAGE>::WAVES * 64, 1) void k_grouped_g
 // per-tile scheduler, first-stage latency and epilogue of the one-tile-per-block kernel cost a
 // large share of its time.
 constexpr int P_WS_OFF = SNSTAGE * SSTAGE;                   // [2 buffers][2 column blocks][SMAXKB]
-constexpr int P_PREFIX_OFF = P_WS_OFF + 2 * 2 * SMAXKB * 4;  // tile prefix + 4 words of scan scratch
-constexpr int PLDS = P_PREFIX_OFF + (kMaxGroups + 1 + 4) * 4;
+constexpr int P_PREFIX_OFF = P_WS_OFF + 2 * 2 * SMAXKB * 4;  // tile prefix + the scan's wave sums
+constexpr int PLDS = P_PREFIX_OFF + (kMaxGroups + 1 + kMaxSchedWaves) * 4;
 static_assert(PLDS <= 160 * 1024, "one block per CU");
 
 // One tile of the persistent down kernel: wave-uniform place and this lane's operand addresses.

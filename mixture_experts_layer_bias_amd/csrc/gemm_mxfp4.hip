@@ -388,7 +388,7 @@ __global__ __launch_bounds__(MxShape<STAGE>::WAVES * 64, STAGE == 0 ? 1 : 2) voi
 // latency and epilogue are a large share of its time.
 using MxDn = MxShape<1, false>;
 constexpr int MXP_PREFIX_OFF = MxDn::NSTAGE * MxDn::SBYTES;
-constexpr int MXP_LDS = MXP_PREFIX_OFF + (kMaxGroups + 1 + 4) * 4;
+constexpr int MXP_LDS = MXP_PREFIX_OFF + (kMaxGroups + 1 + kMaxSchedWaves) * 4;
 static_assert(2 * MXP_LDS <= 160 * 1024, "two blocks per CU");
 
 struct MxDownTile {
