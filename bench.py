@@ -50,16 +50,16 @@ CPU_SAMPLE_TOKENS = {"tiny": 16, "decode": 4, "prefill_zipf": 32, "fp8_sigmoid":
 # while its sources hash to the value they had when the counters were taken; otherwise the traffic is
 # reported as null.  The summaries the entries come from are in profiles/.
 MEASURED_TRAFFIC = {
-    ('tiny', 'experts'): {"kernel": "k_decode_fused", "grid": 128, "dispatches": 26, "fetch_kib": 1107.1, "write_kib": 50.0, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_decode.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/unpermute.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "9e0de5bbb122db7dd5a36a65931a12d86345c18cd32d7a1c469a4dc61bef54b7"},
-    ('decode', 'experts'): {"kernel": "k_decode_fused", "grid": 1384, "dispatches": 25, "fetch_kib": 140210.6, "write_kib": 231.0, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_decode.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/unpermute.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "9e0de5bbb122db7dd5a36a65931a12d86345c18cd32d7a1c469a4dc61bef54b7"},
-    ('prefill_zipf', 'gate_up'): {"kernel": "k_grouped_gemm_bf16<0, unsigned int>", "grid": 2312, "dispatches": 31, "fetch_kib": 620045.3, "write_kib": 49152.1, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_bf16.hip", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "543c15792fcc53321ca6c4c11ca0af13c58ef838f5b6ef72cd03989def466726"},
-    ('prefill_zipf', 'down'): {"kernel": "k_grouped_gemm_bf16<2, unsigned int>", "grid": 3080, "dispatches": 31, "fetch_kib": 260042.2, "write_kib": 131072.1, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_bf16.hip", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "543c15792fcc53321ca6c4c11ca0af13c58ef838f5b6ef72cd03989def466726"},
-    ('zero_experts', 'gate_up'): {"kernel": "k_grouped_gemm_bf16<0, unsigned int>", "grid": 5392, "dispatches": 26, "fetch_kib": 1771915.2, "write_kib": 47390.1, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_bf16.hip", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "543c15792fcc53321ca6c4c11ca0af13c58ef838f5b6ef72cd03989def466726"},
-    ('zero_experts', 'down'): {"kernel": "k_grouped_gemm_bf16<2, unsigned int>", "grid": 7320, "dispatches": 26, "fetch_kib": 788496.8, "write_kib": 57051.1, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_bf16.hip", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "543c15792fcc53321ca6c4c11ca0af13c58ef838f5b6ef72cd03989def466726"},
-    ('fp8_sigmoid', 'gate_up'): {"kernel": "k_grouped_gemm_fp8_stream<0>", "grid": 6160, "dispatches": 6, "fetch_kib": 2427423.9, "write_kib": 36006.0, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_fp8.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "9b0b13e078c545f94282585ec473f4958d6850ff815db69ffdc69adf9a52cf20"},
-    ('fp8_sigmoid', 'down'): {"kernel": "k_grouped_gemm_fp8_down_persistent", "grid": 256, "dispatches": 26, "fetch_kib": 1199572.3, "write_kib": 229376.0, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_fp8.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "9b0b13e078c545f94282585ec473f4958d6850ff815db69ffdc69adf9a52cf20"},
-    ('mxfp4_sigmoid', 'gate_up'): {"kernel": "k_grouped_gemm_mxfp4<0, true>", "grid": 6160, "dispatches": 6, "fetch_kib": 1517131.1, "write_kib": 35763.9, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_mxfp4.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "c21a92978effe3fcafedb0c7a70448effb8bb2ac73a56abdbd4d05a10207a415"},
-    ('mxfp4_sigmoid', 'down'): {"kernel": "k_grouped_gemm_mxfp4<1, false>", "grid": 21560, "dispatches": 6, "fetch_kib": 571144.4, "write_kib": 229376.1, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_mxfp4.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "c21a92978effe3fcafedb0c7a70448effb8bb2ac73a56abdbd4d05a10207a415"},
+    ('tiny', 'experts'): {"kernel": "k_decode_fused", "grid": 128, "dispatches": 26, "fetch_kib": 1108.0, "write_kib": 50.0, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_decode.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/unpermute.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "bfcaab30e94a51951a61db94ca84a4c2989b9e8e0674a7dfc4e6a847f8075c5d"},
+    ('decode', 'experts'): {"kernel": "k_decode_fused", "grid": 1384, "dispatches": 25, "fetch_kib": 140213.5, "write_kib": 231.0, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_decode.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/unpermute.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "bfcaab30e94a51951a61db94ca84a4c2989b9e8e0674a7dfc4e6a847f8075c5d"},
+    ('prefill_zipf', 'gate_up'): {"kernel": "k_grouped_gemm_bf16<0, unsigned int>", "grid": 2312, "dispatches": 31, "fetch_kib": 618522.0, "write_kib": 49152.1, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_bf16.hip", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "c6a4a91e37207fdb955d062d3e8676620fcabfc1599ef61585ad857f4a08e920"},
+    ('prefill_zipf', 'down'): {"kernel": "k_grouped_gemm_bf16_persistent<2, unsigned int>", "grid": 512, "dispatches": 31, "fetch_kib": 282790.1, "write_kib": 131074.5, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_bf16.hip", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "c6a4a91e37207fdb955d062d3e8676620fcabfc1599ef61585ad857f4a08e920"},
+    ('zero_experts', 'gate_up'): {"kernel": "k_grouped_gemm_bf16<0, unsigned int>", "grid": 5392, "dispatches": 26, "fetch_kib": 1776311.5, "write_kib": 47390.3, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_bf16.hip", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "c6a4a91e37207fdb955d062d3e8676620fcabfc1599ef61585ad857f4a08e920"},
+    ('zero_experts', 'down'): {"kernel": "k_grouped_gemm_bf16<2, unsigned int>", "grid": 7320, "dispatches": 26, "fetch_kib": 788662.5, "write_kib": 57051.1, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_bf16.hip", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "c6a4a91e37207fdb955d062d3e8676620fcabfc1599ef61585ad857f4a08e920"},
+    ('fp8_sigmoid', 'gate_up'): {"kernel": "k_grouped_gemm_fp8_stream<0>", "grid": 6160, "dispatches": 6, "fetch_kib": 2410407.6, "write_kib": 36015.2, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_fp8.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "c74c56ff66e2ccc280f08d9bf9f2081efce90fccc8a599b32c281a334d657cd9"},
+    ('fp8_sigmoid', 'down'): {"kernel": "k_grouped_gemm_fp8_down_persistent", "grid": 256, "dispatches": 26, "fetch_kib": 1236569.0, "write_kib": 229376.0, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_fp8.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "c74c56ff66e2ccc280f08d9bf9f2081efce90fccc8a599b32c281a334d657cd9"},
+    ('mxfp4_sigmoid', 'gate_up'): {"kernel": "k_grouped_gemm_mxfp4<0, true>", "grid": 6160, "dispatches": 6, "fetch_kib": 1519055.9, "write_kib": 35711.6, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_mxfp4.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "4d95e39c4d66bfa85e6242a067aef70055e13e5d421ba044c990c39cdd1b881c"},
+    ('mxfp4_sigmoid', 'down'): {"kernel": "k_grouped_gemm_mxfp4_down_persistent", "grid": 512, "dispatches": 26, "fetch_kib": 734735.5, "write_kib": 251432.3, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_mxfp4.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "4d95e39c4d66bfa85e6242a067aef70055e13e5d421ba044c990c39cdd1b881c"},
 }
 
 
