@@ -206,9 +206,10 @@ moe_status_t moe_unpermute_reduce(const moe_config_t* cfg, const void* y_sorted,
  * MoeLayer::forward_prefill (the grouped data flow); forward.rs page,
  * MoeLayer::forward and apply_zero_expert.
  * x [N, H] bf16 -> out [N, H] bf16; ws: at least moe_workspace_size(cfg) bytes,
- * with any contents (a decode batch's routing launch keeps per-block flags in
- * the `sync` piece, which count as set only when they hold a value of that very
- * launch).  Calls that overlap on one workspace race. */
+ * with any contents (a decode batch's routing launch hands its logits over in
+ * the `scratch` piece as words tagged with a value of that very launch, and
+ * counts a word only when it carries that value).  Calls that overlap on one
+ * workspace race. */
 moe_status_t moe_forward(const moe_config_t* cfg, const moe_weights_t* w, const void* x, void* out, void* ws,
                          size_t ws_bytes, void* stream);
 
@@ -223,7 +224,7 @@ moe_status_t moe_forward(const moe_config_t* cfg, const moe_weights_t* w, const 
  * ws: at least moe_workspace_size(cfg) bytes.  With bf16 weights, H <= 65536 and
  * a few rows per touched expert (decode) the routed GEMMs and the reduce run as
  * one launch whose tiles wait on counters in the workspace's `sync` piece.  That
- * piece is the first 8712 bytes of every workspace, whatever the sizes, and its
+ * piece is the first 8200 bytes of every workspace, whatever the sizes, and its
  * counters must hold zeros when the call starts: zero them once (e.g. zero the
  * whole workspace after allocating it); every call of this library leaves them
  * zero, so the workspace can then serve any batch size and layer shape.

@@ -189,7 +189,9 @@ void compute_layout(const moe_config_t* c, moe_workspace_layout_t* L) {
   // chunk histograms (rows padded to 4 ints) + bucket totals
   const size_t hist_bytes = ((size_t)moe::permute_chunks((int)P) + 1) * ((R + 3) / 4 * 4) * 4;
   const size_t part_bytes = slices > 1 ? (size_t)slices * N * R * 4 : 0;
-  L->scratch = take(hist_bytes > part_bytes ? hist_bytes : part_bytes);
+  // a decode batch's one-launch routing hands the logits over as 64-bit tagged words
+  const size_t tag_bytes = moe::route_small_fits((int)N, (int)K, (int)R) ? N * R * 8 : 0;
+  L->scratch = take(std::max(hist_bytes, std::max(part_bytes, tag_bytes)));
   L->xq = fp8 ? take(N * H) : none;
   L->x_scales = fp8 ? take(N * (H / 128) * 4) : none;
   L->h = take(P * I * (fp8 ? 1 : 2));
@@ -652,7 +654,8 @@ moe_status_t moe_forward(const moe_config_t* cfg, const moe_weights_t* w, const 
     // decode: router GEMV, top-K and the sort in one launch
     MOE_HIP(moe::launch_route_small(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w->router_w),
                                     logits, w->correction_bias, ids, tw, zw, counts, offsets, sorted_ids, inv_perm,
-                                    sync, fused, next_route_seq(), c.num_tokens, c.hidden, c.router_width,
+                                    sync, reinterpret_cast<unsigned long long*>(hist), fused, next_route_seq(),
+                                    c.num_tokens, c.hidden, c.router_width,
                                     c.num_experts, c.top_k, c.scoring, c.renormalize, c.routed_scale, s));
   } else if (small) {
     const bool inv = c.row_invariant != 0;
@@ -661,7 +664,7 @@ moe_status_t moe_forward(const moe_config_t* cfg, const moe_weights_t* w, const 
     MOE_HIP(moe::launch_router_logits(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w->router_w),
                                       part, c.num_tokens, c.hidden, c.router_width, slices, inv, s));
     MOE_HIP(moe::launch_topk_sort_small(part, slices, logits, w->correction_bias, ids, tw, zw, counts, offsets,
-                                        sorted_ids, inv_perm, fused ? sync : nullptr, moe::kSyncRouteFlags, c.num_tokens,
+                                        sorted_ids, inv_perm, fused ? sync : nullptr, moe::kSyncCounters, c.num_tokens,
                                         c.router_width, c.num_experts, c.top_k, c.scoring, c.renormalize,
                                         c.routed_scale, s));
   } else {

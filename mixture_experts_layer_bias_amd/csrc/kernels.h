@@ -35,15 +35,17 @@ hipError_t launch_topk_sort_small(const float* part, int slices, float* logits, 
 
 // a1 + a2 + a3 for decode batches (route_small_fits: N <= 8, N*K <= 64, R <= 1024, not row-invariant):
 // router GEMV, top-K and the sort in one launch, with the same results as launch_router_logits (one
-// slice) + launch_topk_sort_small.  sync: the workspace's sync piece (kSyncInts int32; its route flags
-// may hold anything but `seq`); seq: nonzero, different from the last launch's on this sync piece.
-// zero_counters: also zero sync[0, kSyncRouteFlags) for a following one-launch decode.
+// slice) + launch_topk_sort_small.  tagged: N R 64-bit words of scratch (any contents but `seq` in a
+// high half) through which the GEMV blocks hand the logits to the top-K block; the launch leaves them
+// zero.  seq: nonzero, different from the last launch's on these words.  sync: the workspace's sync
+// piece (kSyncInts int32), whose error word is set if the top-K block's bounded wait expires.
+// zero_counters: also zero sync[0, kSyncCounters) for a following one-launch decode.
 bool route_small_fits(int N, int K, int R);
 hipError_t launch_route_small(const uint16_t* x, const uint16_t* router_w, float* logits, const float* bias,
                               int32_t* ids, float* w, float* zero_w, int32_t* counts, int32_t* offsets,
-                              int32_t* sorted_ids, int32_t* inv_perm, int32_t* sync, bool zero_counters, int seq,
-                              int N, int H, int R, int E, int K, int scoring, int renormalize, float routed_scale,
-                              hipStream_t s);
+                              int32_t* sorted_ids, int32_t* inv_perm, int32_t* sync, unsigned long long* tagged,
+                              bool zero_counters, int seq, int N, int H, int R, int E, int K, int scoring,
+                              int renormalize, float routed_scale, hipStream_t s);
 
 // a3: stable counting sort by expert; hist is [(permute_chunks(P) + 1) * 4 ceil(R / 4)] int32 scratch.  Two
 // launches when permute_direct(P, R), else three.
@@ -124,9 +126,8 @@ constexpr int kSyncColTiles = 1024;     // [kSyncMaxColTiles]: down tiles finish
 constexpr int kSyncMaxColTiles = 512;   // so the path takes H <= 65536
 constexpr int kSyncReduced = 1536;      // column blocks reduced
 constexpr int kSyncError = 1537;        // set to 1 when a bounded wait expires; the launch never clears it
-constexpr int kSyncRouteFlags = 1538;   // [kSyncRouteMaxFlags]: the one-launch decode prelude's block flags
-constexpr int kSyncRouteMaxFlags = 128;
-constexpr int kSyncSplit = kSyncRouteFlags + kSyncRouteMaxFlags;  // [kSyncSplitMax] 64-bit: split tiles' arrivals
+constexpr int kSyncCounters = 1538;     // sync[0, kSyncCounters): the counters above and the error word
+constexpr int kSyncSplit = kSyncCounters;  // [kSyncSplitMax] 64-bit: split tiles' arrivals
 constexpr int kSyncSplitMax = kSplitSlots / 2;                     // a split tile has at least two parts
 constexpr int kSyncInts = kSyncSplit + 2 * kSyncSplitMax;
 static_assert(kSyncSplit % 2 == 0, "64-bit counters");

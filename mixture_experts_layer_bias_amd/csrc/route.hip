@@ -185,22 +185,61 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 
 // Scores and top-K of token t for the calling wave.  p_w is this wave's LDS row
 // of MAXJ*64 floats.  Returns the wave's slot id (lane k holds slot k's column;
-// lanes >= K hold 0) after writing ids / w / zero_w for the token.  DEV: whole logits (nslices == 1)
-// written in the same launch by other blocks with device-scope stores, read at device scope.
-template <int MAXJ, bool DEV = false>
+// lanes >= K hold 0) after writing ids / w / zero_w for the token.  TAGGED: `part` holds, for every
+// (token, column), a 64-bit word (seq << 32 | logit bits) that other blocks of this launch store at
+// device scope; the wave reads them at device scope until every word carries `seq` (at most
+// kRouteSpinLimit rounds; past it *expired is set and the values are undefined), writes the logits out and
+// puts the words back to zero, so that the next launch, which may repeat `seq` (a graph replay), waits
+// for its own.
+constexpr int kRouteSpinLimit = 1 << 20;
+
+template <int MAXJ, bool TAGGED = false>
 __device__ __forceinline__ int topk_token(const float* __restrict__ part, int nslices, float* __restrict__ logits,
                                           const float* __restrict__ bias, int32_t* __restrict__ ids,
                                           float* __restrict__ w, float* __restrict__ zero_w, float* p_w, int t, int N,
-                                          int R, int E, int K, int scoring, int renorm, float scale) {
+                                          int R, int E, int K, int scoring, int renorm, float scale,
+                                          uint32_t seq = 0, int* expired = nullptr) {
   const int lane = threadIdx.x % kWave;
   // logits of this token: the split-K partial planes added in slice order
   float v[MAXJ];
+  if (TAGGED) {
+    unsigned long long* tw =
+        reinterpret_cast<unsigned long long*>(const_cast<float*>(part)) + (size_t)t * R;
+    unsigned long long word[MAXJ];
+    bool ready = false;
+    for (int it = 0; it < kRouteSpinLimit && !ready; ++it) {
+      ready = true;
+#pragma unroll
+      for (int j = 0; j < MAXJ; ++j) {
+        const int r = lane + 64 * j;
+        if (r < R && (it == 0 || (uint32_t)(word[j] >> 32) != seq))
+          word[j] = __hip_atomic_load(tw + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+#pragma unroll
+      for (int j = 0; j < MAXJ; ++j)
+        if (lane + 64 * j < R && (uint32_t)(word[j] >> 32) != seq) ready = false;
+      ready = __all(ready);
+      if (!ready) __builtin_amdgcn_s_sleep(1);
+    }
+    if (!ready && lane == 0) *expired = 1;
+#pragma unroll
+    for (int j = 0; j < MAXJ; ++j) {
+      const int r = lane + 64 * j;
+      if (r < R) {
+        v[j] = __uint_as_float((uint32_t)word[j]);
+        logits[(size_t)t * R + r] = v[j];
+        __hip_atomic_store(tw + r, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        v[j] = -INFINITY;
+      }
+    }
+  }
 #pragma unroll
   for (int j = 0; j < MAXJ; ++j) {
+    if (TAGGED) break;
     const int r = lane + 64 * j;
     if (r < R && nslices == 1) {  // whole logits (the GEMV router): one load
-      v[j] = DEV ? __hip_atomic_load(part + (size_t)t * R + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                 : part[(size_t)t * R + r];
+      v[j] = part[(size_t)t * R + r];
     } else if (r < R) {
       // all planes are loaded before the (in-order) additions, so the loads overlap
       float pl[16];
@@ -444,23 +483,21 @@ __global__ __launch_bounds__(1024) void k_topk_sort_small(const float* __restric
 
 // The decode prelude in one launch (N <= 8 tokens, N K <= 64 rows, R <= 1024): router GEMV, top-K and
 // the sort, with the same results as k_router_gemv followed by k_topk_sort_small.  Every block of 8
-// waves computes 8 router columns (one per wave) and stores their logits at device scope.  Every block
-// but block 0 then waits for its stores and writes `seq` into its flag, sync[kSyncRouteFlags + b - 1];
-// block 0 waits (bounded) until every flag holds seq, puts the flags back to 0, and runs the top-K of
-// each token (one wave per token, logits read at device scope) and the ballot sort.  seq is a nonzero
-// value of this launch that differs from the last launch's on the same flags; flags are taken as set
-// only when they hold exactly seq, so the workspace may start with any contents.  With
-// zero_counters, block 0 also zeroes the counters and the error word of the one-launch decode experts
-// path that follows (sync[0, kSyncRouteFlags)).
-constexpr int kRouteSpinLimit = 1 << 20;
-
+// waves computes 8 router columns (one per wave) and stores each logit at device scope as one 64-bit
+// word tagged with `seq` (a nonzero value of this launch that differs from the last launch's on the same
+// words).  Block 0 then runs the top-K of each token (one wave per token), reading its logits at device
+// scope until every word carries seq (a bounded wait), puts the words back to 0, and runs the ballot
+// sort.  A word counts only when it carries exactly seq, so the workspace may start with any contents,
+// and a graph replay (which repeats seq) finds the words zeroed.  With zero_counters, block 0 also
+// zeroes the counters and the error word of the one-launch decode experts path that follows
+// (sync[0, kSyncCounters)).
 template <int MAXJ, int NT, int G>
 __global__ __launch_bounds__(512) void k_route_small(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, float* __restrict__ logits,
     const float* __restrict__ bias, int32_t* __restrict__ ids, float* __restrict__ w, float* __restrict__ zero_w,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_ids,
-    int32_t* __restrict__ inv_perm, int32_t* __restrict__ sync, int zero_counters, int seq, int N, int H, int R,
-    int E, int K, int scoring, int renorm, float scale) {
+    int32_t* __restrict__ inv_perm, int32_t* __restrict__ sync, unsigned long long* __restrict__ tagged,
+    int zero_counters, int seq, int N, int H, int R, int E, int K, int scoring, int renorm, float scale) {
   __shared__ float p_lds[8][MAXJ * 64];
   __shared__ int s_ids[64];
   __shared__ int s_off[1024];
@@ -474,51 +511,38 @@ __global__ __launch_bounds__(512) void k_route_small(
     for (int t = 0; t < NT; ++t) {
       if (t < N) {  // uniform
         const float v = wave_sum(acc[t]);
-        if (lane == 0) __hip_atomic_store(logits + (size_t)t * R + r, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0)
+          __hip_atomic_store(tagged + (size_t)t * R + r, ((unsigned long long)(uint32_t)seq << 32) | __float_as_uint(v),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
-  dma_wait<0>();  // this wave's logit stores are complete (device scope)
-  if (blockIdx.x != 0) {
-    __syncthreads();  // ... and every other wave's
-    if (tid == 0)
-      __hip_atomic_store(sync + kSyncRouteFlags + blockIdx.x - 1, seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return;
-  }
+  if (blockIdx.x != 0) return;  // block 0 waits for the tagged logits themselves
   if (tid == 0) s_expired = 0;
   for (int i = tid; i < R; i += 512) s_off[i] = 0;
-  __syncthreads();
-  if (tid >= 1 && tid < (int)gridDim.x) {
-    int* flag = sync + kSyncRouteFlags + tid - 1;
-    bool ready = false;
-    for (int it = 0; it < kRouteSpinLimit && !ready; ++it) {
-      ready = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == seq;
-      if (!ready) __builtin_amdgcn_s_sleep(1);
-    }
-    if (!ready) s_expired = 1;
-    __hip_atomic_store(flag, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
   if (zero_counters)
-    for (int i = tid; i < kSyncRouteFlags; i += 512) sync[i] = 0;
+    for (int i = tid; i < kSyncCounters; i += 512) sync[i] = 0;
+  __syncthreads();
+  if (wave < N) {
+    const int my_id = topk_token<MAXJ, true>(reinterpret_cast<const float*>(tagged), 1, logits, bias, ids, w, zero_w,
+                                             p_lds[wave], wave, N, R, E, K, scoring, renorm, scale, (uint32_t)seq,
+                                             &s_expired);
+    if (lane < K) s_ids[wave * K + lane] = my_id;
+  }
   __syncthreads();
   if (tid == 0 && s_expired)  // after the zeroing above: this launch's output is undefined
     __hip_atomic_store(sync + kSyncError, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (wave < N) {
-    const int my_id = topk_token<MAXJ, true>(logits, 1, logits, bias, ids, w, zero_w, p_lds[wave], wave, N, R, E, K,
-                                             scoring, renorm, scale);
-    if (lane < K) s_ids[wave * K + lane] = my_id;
-  }
   __syncthreads();
   if (wave == 0) sort_rows_ballot(s_ids, s_off, N * K, R, counts, offsets, sorted_ids, inv_perm);
 }
 
-bool route_small_fits(int N, int K, int R) { return N <= RG_MAXN && N * K <= kWave && R <= 8 * kSyncRouteMaxFlags; }
+bool route_small_fits(int N, int K, int R) { return N <= RG_MAXN && N * K <= kWave && R <= 1024; }
 
 hipError_t launch_route_small(const uint16_t* x, const uint16_t* router_w, float* logits, const float* bias,
                               int32_t* ids, float* w, float* zero_w, int32_t* counts, int32_t* offsets,
-                              int32_t* sorted_ids, int32_t* inv_perm, int32_t* sync, bool zero_counters, int seq,
-                              int N, int H, int R, int E, int K, int scoring, int renormalize, float routed_scale,
-                              hipStream_t s) {
+                              int32_t* sorted_ids, int32_t* inv_perm, int32_t* sync, unsigned long long* tagged,
+                              bool zero_counters, int seq, int N, int H, int R, int E, int K, int scoring,
+                              int renormalize, float routed_scale, hipStream_t s) {
   if (N == 0) return hipSuccess;
   if (!route_small_fits(N, K, R) || seq == 0) return hipErrorInvalidValue;
   const unsigned blocks = (unsigned)((R + 7) / 8);
@@ -527,12 +551,12 @@ hipError_t launch_route_small(const uint16_t* x, const uint16_t* router_w, float
   case J:                                                                                                        \
     if (N <= 4)                                                                                                  \
       k_route_small<J, 4, 4><<<blocks, 512, 0, s>>>(x, router_w, logits, bias, ids, w, zero_w, counts, offsets,  \
-                                                    sorted_ids, inv_perm, sync, zero_counters, seq, N, H, R, E,   \
-                                                    K, scoring, renormalize, routed_scale);                       \
+                                                    sorted_ids, inv_perm, sync, tagged, zero_counters, seq, N, H, \
+                                                    R, E, K, scoring, renormalize, routed_scale);                 \
     else                                                                                                         \
       k_route_small<J, 8, 2><<<blocks, 512, 0, s>>>(x, router_w, logits, bias, ids, w, zero_w, counts, offsets,  \
-                                                    sorted_ids, inv_perm, sync, zero_counters, seq, N, H, R, E,   \
-                                                    K, scoring, renormalize, routed_scale);                       \
+                                                    sorted_ids, inv_perm, sync, tagged, zero_counters, seq, N, H, \
+                                                    R, E, K, scoring, renormalize, routed_scale);                 \
     break;
   switch (maxj <= 2 ? maxj : (maxj <= 4 ? 4 : (maxj <= 6 ? 6 : 16))) {
     MOE_ROUTE_CASE(1)
