@@ -224,7 +224,7 @@ moe_status_t moe_forward(const moe_config_t* cfg, const moe_weights_t* w, const 
  * ws: at least moe_workspace_size(cfg) bytes.  With bf16 weights, H <= 65536 and
  * a few rows per touched expert (decode) the routed GEMMs and the reduce run as
  * one launch whose tiles wait on counters in the workspace's `sync` piece.  That
- * piece is the first 8200 bytes of every workspace, whatever the sizes, and its
+ * piece is the first 8232 bytes of every workspace, whatever the sizes, and its
  * counters must hold zeros when the call starts: zero them once (e.g. zero the
  * whole workspace after allocating it); every call of this library leaves them
  * zero, so the workspace can then serve any batch size and layer shape.
@@ -260,7 +260,8 @@ moe_status_t moe_forward_noalloc(const moe_config_t* cfg, const moe_weights_t* w
  * can inspect them after moe_forward (all in bytes from the workspace start;
  * a piece that the config does not use has offset SIZE_MAX).  `sync` (always 0)
  * holds the counters of the one-launch decode experts path and `sync_error` its
- * error word (see moe_experts_forward), and the arrival counters of split tiles.
+ * error word (see moe_experts_forward), the arrival counters of split tiles, and
+ * the per-XCD tile counters that moe_forward's sort zeroes for the GEMMs after it.
  * `split` holds the parts' fp32 partial sums of split tiles: present for bf16
  * layers of at least 2048 routed rows with H or I of at least 4096, without a
  * shared expert and not row-invariant (see moe_grouped_gemm). */

@@ -351,9 +351,11 @@ bool experts_fused(const moe_config_t* c) {
 // (+ shared) -> unpermute-reduce.  With `fused` (the counters piece of the workspace holds zeros)
 // the routed GEMMs and the reduce run as one launch, after the shared expert, whose output the
 // reduce reads; that launch leaves the counters zero again.
+// queue: the workspace's per-XCD tile counters, zero (or null: the launches walk their tiles in a fixed order)
 moe_status_t run_experts(const moe_config_t* cfg, const moe_weights_t* w, const void* x, const int32_t* ids,
                          const float* tw, const int32_t* offsets, const int32_t* sorted_ids, const int32_t* inv_perm,
-                         void* out, const moe_workspace_layout_t& L, char* base, bool fused, hipStream_t s) {
+                         void* out, const moe_workspace_layout_t& L, char* base, bool fused, int32_t* queue,
+                         hipStream_t s) {
   const moe_config_t& c = *cfg;
   auto at = [&](size_t off) -> void* { return off == SIZE_MAX ? nullptr : base + off; };
   const bool fp8 = c.weight_dtype != MOE_WEIGHTS_BF16;  // e4m3 activations
@@ -394,10 +396,14 @@ moe_status_t run_experts(const moe_config_t* cfg, const moe_weights_t* w, const 
     MOE_HIP(moe::launch_decode_fused(gu_all, dn_all, red, static_cast<int32_t*>(at(L.sync)), s));
     return ok();
   }
-  MOE_RET(run_gemm(cfg, with_split(gu_all, L, base), s));
-  if (c.shared_inter > 0 && !fold_gu) MOE_RET(run_gemm(cfg, sh_gu, s));
-  MOE_RET(run_gemm(cfg, with_split(dn_all, L, base), s));
-  if (c.shared_inter > 0 && !fold_dn) MOE_RET(run_gemm(cfg, sh_dn, s));
+  auto queued = [&](moe::GroupedGemmArgs g) {
+    g.queue = queue;
+    return g;
+  };
+  MOE_RET(run_gemm(cfg, with_split(queued(gu_all), L, base), s));
+  if (c.shared_inter > 0 && !fold_gu) MOE_RET(run_gemm(cfg, queued(sh_gu), s));
+  MOE_RET(run_gemm(cfg, with_split(queued(dn_all), L, base), s));
+  if (c.shared_inter > 0 && !fold_dn) MOE_RET(run_gemm(cfg, queued(sh_dn), s));
   MOE_HIP(moe::launch_unpermute_reduce(static_cast<const uint16_t*>(at(L.y)), red, s));
   return ok();
 }
@@ -515,7 +521,7 @@ moe_status_t moe_permute(const moe_config_t* cfg, const int32_t* topk_ids, int32
   }
   const int P = cfg->num_tokens * cfg->top_k;
   int32_t* hist = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + L.scratch);
-  MOE_HIP(moe::launch_permute(topk_ids, P, cfg->router_width, counts, offsets, sorted_ids, inv_perm, hist,
+  MOE_HIP(moe::launch_permute(topk_ids, P, cfg->router_width, counts, offsets, sorted_ids, inv_perm, hist, nullptr,
                               static_cast<hipStream_t>(stream)));
   return ok();
 }
@@ -646,6 +652,7 @@ moe_status_t moe_forward(const moe_config_t* cfg, const moe_weights_t* w, const 
   int32_t* hist = static_cast<int32_t*>(at(L.scratch));
   const int P = c.num_tokens * c.top_k;
   int32_t* sync = static_cast<int32_t*>(at(L.sync));
+  int32_t* queue = nullptr;  // tile counters of the GEMMs (prefill routing only)
   // small batch: router GEMM, then top-K and the sort in one block (both in one launch for decode
   // batches), which also zeroes the counters and the error word of the one-launch decode experts path
   const bool small = moe::topk_sort_small_fits(c.num_tokens, c.top_k);
@@ -670,9 +677,11 @@ moe_status_t moe_forward(const moe_config_t* cfg, const moe_weights_t* w, const 
   } else {
     MOE_RET(launch_route(cfg, x, w->router_w, w->correction_bias, logits, ids, tw, zw, reinterpret_cast<float*>(hist),
                          s));
-    MOE_HIP(moe::launch_permute(ids, P, c.router_width, counts, offsets, sorted_ids, inv_perm, hist, s));
+    // the sort also zeroes the GEMMs' tile counters, which each launch that takes them leaves zero
+    queue = sync + moe::kSyncQueue;
+    MOE_HIP(moe::launch_permute(ids, P, c.router_width, counts, offsets, sorted_ids, inv_perm, hist, queue, s));
   }
-  return run_experts(cfg, w, x, ids, tw, offsets, sorted_ids, inv_perm, out, L, base, fused, s);
+  return run_experts(cfg, w, x, ids, tw, offsets, sorted_ids, inv_perm, out, L, base, fused, queue, s);
 }
 
 moe_status_t moe_experts_forward(const moe_config_t* cfg, const moe_weights_t* w, const void* x,
@@ -695,7 +704,7 @@ moe_status_t moe_experts_forward(const moe_config_t* cfg, const moe_weights_t* w
   MOE_RET(check_ptr(out, 16, "out"));
   MOE_RET(check_ptr(ws, 256, "ws"));
   return run_experts(cfg, w, x, topk_ids, topk_w, offsets, sorted_ids, inv_perm, out, L, static_cast<char*>(ws),
-                     experts_fused(cfg), static_cast<hipStream_t>(stream));
+                     experts_fused(cfg), nullptr, static_cast<hipStream_t>(stream));
 }
 
 moe_status_t moe_forward_noalloc(const moe_config_t* cfg, const moe_weights_t* w, const void* x, void* out,

@@ -407,13 +407,21 @@ __global__ __launch_bounds__(MX_DN_WAVES * 64, 2) void k_grouped_gemm_mxfp4_down
   int* s_prefix = reinterpret_cast<int*>(smem + MXP_PREFIX_OFF);
   int* s_wsum = s_prefix + kMaxGroups + 1;
 
+  __shared__ int s_next;
+
   const Groups G = gemm_groups(g, 1, BN);
   const int T = tile_prefix(G, BM, s_prefix, s_wsum);
   const int SB = (int)gridDim.x / 8, x = blockIdx.x % 8;  // blocks per XCD; this block's XCD
   const int chunk = (T + 7) / 8;
-  const int t_end = min((x + 1) * chunk, T);
-  int L = x * chunk + (int)blockIdx.x / 8;
+  const int t0 = x * chunk, t_end = min((x + 1) * chunk, T);
+  int L = t0 + (int)blockIdx.x / 8;
   if (L >= t_end) return;  // the same decision in every thread
+  // with the launch's tile counters (g.queue): the XCD's nT tiles, the first nb of them taken by its
+  // blocks' first tiles; the i-th add on the XCD's counter hands out tile t0 + nb + i, and the add that
+  // returns nT - 1 is the XCD's last (each tile a block takes is followed by one add), which puts the
+  // counter back to zero.  A block adds at a tile's first K step and reads the answer half a tile later.
+  const int nT = t_end - t0, nb = min(SB, nT);
+  int32_t* const qw = g.queue != nullptr ? g.queue + x : nullptr;
 
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -482,13 +490,21 @@ __global__ __launch_bounds__(MX_DN_WAVES * 64, 2) void k_grouped_gemm_mxfp4_down
     if (s < cur.KB) issue(cur, s, s);
 
   for (;;) {
-    const int Lnext = L + SB;
-    const bool has_next = Lnext < t_end;
+    int Lnext = -1;
+    bool has_next = false;
     bool cross = false;  // the next tile's first stages come from this tile's last two steps
-    if (has_next) {
-      prepare(Lnext, nxt);
-      cross = cur.KB >= NSTAGE - 1 && nxt.KB >= NSTAGE - 1;
+    // counters: the next tile is known from the barrier of step pub (at most KB - 2, so that its stages
+    // can still be issued from this tile's last two steps), or, for a tile of under 4 steps, after it
+    const int pub = cur.KB >= 4 ? cur.KB / 2 : -1;
+    if (qw == nullptr) {
+      Lnext = L + SB;
+      has_next = Lnext < t_end;
+      if (has_next) {
+        prepare(Lnext, nxt);
+        cross = cur.KB >= NSTAGE - 1 && nxt.KB >= NSTAGE - 1;
+      }
     }
+    int grab = 0;
     f32x16 acc[MI][NI];
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
@@ -502,8 +518,23 @@ __global__ __launch_bounds__(MX_DN_WAVES * 64, 2) void k_grouped_gemm_mxfp4_down
       wait_steps<NSTAGE, VM>(later);
       __builtin_amdgcn_s_barrier();  // step kb has landed in every wave; every wave is done with kb - 1
       __builtin_amdgcn_sched_barrier(0);
+      if (qw != nullptr && kb == pub) {
+        Lnext = s_next;
+        has_next = Lnext >= 0;
+        if (has_next) {
+          prepare(Lnext, nxt);
+          cross = nxt.KB >= NSTAGE - 1;
+        }
+      }
       if (kb + NSTAGE - 1 < cur.KB) issue(cur, (gs + kb + NSTAGE - 1) % NSTAGE, kb + NSTAGE - 1);
       else if (cross) issue(nxt, (gs + kb + NSTAGE - 1) % NSTAGE, kb + NSTAGE - 1 - cur.KB);
+      if (qw != nullptr && threadIdx.x == 0) {
+        if (kb == 0) grab = __hip_atomic_fetch_add(qw, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (kb == (pub >= 0 ? pub - 1 : cur.KB - 1)) {  // read by every thread after the next barrier
+          s_next = nb + grab < nT ? t0 + nb + grab : -1;
+          if (grab == nT - 1) __hip_atomic_store(qw, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
       if (cur.live_mi == 0) continue;
       const uint8_t* sa = smem + ((gs + kb) % NSTAGE) * S::SBYTES;
       const uint8_t* sb = sa + S::ABYTES;
@@ -575,6 +606,12 @@ __global__ __launch_bounds__(MX_DN_WAVES * 64, 2) void k_grouped_gemm_mxfp4_down
         }
     }
 
+    if (qw != nullptr && pub < 0) {  // a short tile: its next is read here
+      __syncthreads();
+      Lnext = s_next;
+      has_next = Lnext >= 0;
+      if (has_next) prepare(Lnext, nxt);
+    }
     if (!has_next) break;
     gs += cur.KB;
     L = Lnext;

@@ -48,11 +48,12 @@ hipError_t launch_route_small(const uint16_t* x, const uint16_t* router_w, float
                               int renormalize, float routed_scale, hipStream_t s);
 
 // a3: stable counting sort by expert; hist is [(permute_chunks(P) + 1) * 4 ceil(R / 4)] int32 scratch.  Two
-// launches when permute_direct(P, R), else three.
+// launches when permute_direct(P, R), else three.  clear8 (or null): 8 ints that the sort sets to zero (the
+// tile counters of the GEMMs after it).
 int permute_chunks(int P);
 bool permute_direct(int P, int R);
 hipError_t launch_permute(const int32_t* ids, int P, int R, int32_t* counts, int32_t* offsets, int32_t* sorted_ids,
-                          int32_t* inv_perm, int32_t* hist, hipStream_t s);
+                          int32_t* inv_perm, int32_t* hist, int32_t* clear8, hipStream_t s);
 
 // a4: per-token, per-128-column e4m3 quantisation of bf16 rows
 hipError_t launch_quant_fp8(const uint16_t* x, uint8_t* xq, float* xs, int rows, int cols, hipStream_t s);
@@ -99,6 +100,10 @@ struct GroupedGemmArgs {
   uint32_t split_seq;
   float* split_part;
   unsigned long long* split_cnt;
+  // Tiles handed out at run time (the MXFP4 persistent down kernel; other kernels ignore it): 8 counters,
+  // one per XCD, holding zero when the launch starts (a launch that takes them leaves them zero), or null
+  // (a fixed walk).
+  int32_t* queue;
 };
 // Limits of the K split: at most kSplitParts parts per tile, kSplitSlots parts per launch, each part's
 // partial tile kSplitFloats fp32 (256 threads x 128 accumulators).
@@ -129,7 +134,8 @@ constexpr int kSyncError = 1537;        // set to 1 when a bounded wait expires;
 constexpr int kSyncCounters = 1538;     // sync[0, kSyncCounters): the counters above and the error word
 constexpr int kSyncSplit = kSyncCounters;  // [kSyncSplitMax] 64-bit: split tiles' arrivals
 constexpr int kSyncSplitMax = kSplitSlots / 2;                     // a split tile has at least two parts
-constexpr int kSyncInts = kSyncSplit + 2 * kSyncSplitMax;
+constexpr int kSyncQueue = kSyncSplit + 2 * kSyncSplitMax;  // [8]: per-XCD tile counters of a launch
+constexpr int kSyncInts = kSyncQueue + 8;
 static_assert(kSyncSplit % 2 == 0, "64-bit counters");
 // Routed gate/up, down and the unpermute-reduce of a decode layer in one launch (the shared expert,
 // if any, must already be in r.shared_y).  sync: kSyncInts int32 whose counters hold zeros when the

@@ -154,10 +154,11 @@ __global__ __launch_bounds__(256) void k_perm_scatter(const int32_t* __restrict_
                                                       const int32_t* __restrict__ totals,
                                                       int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                       int32_t* __restrict__ sorted_ids,
-                                                      int32_t* __restrict__ inv_perm) {
+                                                      int32_t* __restrict__ inv_perm, int32_t* __restrict__ clear8) {
   __shared__ int s_base[kMaxBuckets];  // bucket offsets, then this chunk's cursors
   __shared__ int s_wcnt[4][kMaxBuckets];  // rows per bucket in each wave, then per-wave cursors
   __shared__ int s_wsum[4];
+  if (clear8 != nullptr && blockIdx.x == 0 && threadIdx.x < 8) clear8[threadIdx.x] = 0;
   for (int i = threadIdx.x; i < 4 * kMaxBuckets; i += 256) (&s_wcnt[0][0])[i] = 0;
   bucket_bases(
       R, [&](int r) { return totals[r]; }, [&](int r) { return chunk_prefix[(size_t)blockIdx.x * R + r]; }, s_base,
@@ -177,11 +178,13 @@ __global__ __launch_bounds__(256) void k_perm_scatter_hist(const int32_t* __rest
                                                            int32_t* __restrict__ counts,
                                                            int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ sorted_ids,
-                                                           int32_t* __restrict__ inv_perm) {
+                                                           int32_t* __restrict__ inv_perm,
+                                                           int32_t* __restrict__ clear8) {
   __shared__ int s_base[kMaxBuckets];
   __shared__ int s_wcnt[4][kMaxBuckets];  // the partial sums (before and all), then as k_perm_scatter
   __shared__ int s_wsum[4];
   const int tid = threadIdx.x;
+  if (clear8 != nullptr && blockIdx.x == 0 && tid < 8) clear8[tid] = 0;
   const int R4 = (R + 3) / 4, rs = 4 * R4, G = 256 / R4;
   const int q = tid % R4, g = tid / R4, c_self = blockIdx.x;
   int* s_pre = &s_wcnt[0][0];  // [G][rs], G rs <= 1024
@@ -231,17 +234,18 @@ bool permute_direct(int P, int R) {
 }
 
 hipError_t launch_permute(const int32_t* ids, int P, int R, int32_t* counts, int32_t* offsets, int32_t* sorted_ids,
-                          int32_t* inv_perm, int32_t* hist, hipStream_t s) {
+                          int32_t* inv_perm, int32_t* hist, int32_t* clear8, hipStream_t s) {
   const int C = permute_chunks(P);
   if (permute_direct(P, R)) {
     k_perm_count<<<C, 256, 0, s>>>(ids, P, R, 4 * ((R + 3) / 4), hist);
-    k_perm_scatter_hist<<<C, 256, 0, s>>>(ids, P, R, C, hist, counts, offsets, sorted_ids, inv_perm);
+    k_perm_scatter_hist<<<C, 256, 0, s>>>(ids, P, R, C, hist, counts, offsets, sorted_ids, inv_perm, clear8);
     return hipGetLastError();
   }
   int32_t* totals = hist + (size_t)C * R;  // R more ints after the chunk histograms
   if (C > 0) k_perm_count<<<C, 256, 0, s>>>(ids, P, R, R, hist);
   k_perm_scan<<<(R + 3) / 4, 256, 0, s>>>(hist, C, R, totals);
-  k_perm_scatter<<<C > 0 ? C : 1, 256, 0, s>>>(ids, P, R, hist, totals, counts, offsets, sorted_ids, inv_perm);
+  k_perm_scatter<<<C > 0 ? C : 1, 256, 0, s>>>(ids, P, R, hist, totals, counts, offsets, sorted_ids, inv_perm,
+                                                clear8);
   return hipGetLastError();
 }
 
