@@ -50,16 +50,16 @@ CPU_SAMPLE_TOKENS = {"tiny": 16, "decode": 4, "prefill_zipf": 32, "fp8_sigmoid":
 # while its sources hash to the value they had when the counters were taken; otherwise the traffic is
 # reported as null.  The summaries the entries come from are in profiles/.
 MEASURED_TRAFFIC = {
-    ('tiny', 'experts'): {"kernel": "k_decode_fused", "grid": 128, "dispatches": 26, "fetch_kib": 1107.7, "write_kib": 50.0, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_decode.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/unpermute.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "1736ae0977b8307a50dd73a5b2a7e2051dbc2a25d526f0b3bb5dfc90987d6c6f"},
-    ('decode', 'experts'): {"kernel": "k_decode_fused", "grid": 1384, "dispatches": 25, "fetch_kib": 140216.2, "write_kib": 231.0, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_decode.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/unpermute.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "1736ae0977b8307a50dd73a5b2a7e2051dbc2a25d526f0b3bb5dfc90987d6c6f"},
-    ('prefill_zipf', 'gate_up'): {"kernel": "k_grouped_gemm_bf16<0, unsigned int>", "grid": 2312, "dispatches": 31, "fetch_kib": 620551.1, "write_kib": 49152.2, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_bf16.hip", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "915d5ea6f6d4377ee6631b9438d29021c46342544ccd2cd3982ff77228be32c3"},
-    ('prefill_zipf', 'down'): {"kernel": "k_grouped_gemm_bf16_persistent<2, unsigned int>", "grid": 512, "dispatches": 31, "fetch_kib": 278146.7, "write_kib": 131074.7, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_bf16.hip", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "915d5ea6f6d4377ee6631b9438d29021c46342544ccd2cd3982ff77228be32c3"},
-    ('zero_experts', 'gate_up'): {"kernel": "k_grouped_gemm_bf16<0, unsigned int>", "grid": 5392, "dispatches": 26, "fetch_kib": 1761385.9, "write_kib": 47390.2, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_bf16.hip", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "915d5ea6f6d4377ee6631b9438d29021c46342544ccd2cd3982ff77228be32c3"},
-    ('zero_experts', 'down'): {"kernel": "k_grouped_gemm_bf16<2, unsigned int>", "grid": 7320, "dispatches": 26, "fetch_kib": 784321.5, "write_kib": 57051.1, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_bf16.hip", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "915d5ea6f6d4377ee6631b9438d29021c46342544ccd2cd3982ff77228be32c3"},
-    ('fp8_sigmoid', 'gate_up'): {"kernel": "k_grouped_gemm_fp8_stream<0>", "grid": 6160, "dispatches": 6, "fetch_kib": 2408685.6, "write_kib": 35981.2, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_fp8.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "8ccd77c314f8694f913490725ce2952e770bc24e7295a19eb2d71af3e73ed4f4"},
-    ('fp8_sigmoid', 'down'): {"kernel": "k_grouped_gemm_fp8_down_persistent", "grid": 256, "dispatches": 26, "fetch_kib": 1208927.7, "write_kib": 229376.0, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_fp8.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "8ccd77c314f8694f913490725ce2952e770bc24e7295a19eb2d71af3e73ed4f4"},
-    ('mxfp4_sigmoid', 'gate_up'): {"kernel": "k_grouped_gemm_mxfp4<0, true>", "grid": 6160, "dispatches": 6, "fetch_kib": 1521919.5, "write_kib": 35734.1, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_mxfp4.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "620d0d3381200966bc52a02d43a79adcd59fe2fe0dcad8ec907f7471ea0e5bcd"},
-    ('mxfp4_sigmoid', 'down'): {"kernel": "k_grouped_gemm_mxfp4_down_persistent", "grid": 512, "dispatches": 26, "fetch_kib": 737669.9, "write_kib": 251432.7, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_mxfp4.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "620d0d3381200966bc52a02d43a79adcd59fe2fe0dcad8ec907f7471ea0e5bcd"},
+    ('tiny', 'experts'): {"kernel": "k_decode_fused", "grid": 128, "dispatches": 26, "fetch_kib": 1107.8, "write_kib": 50.0, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_decode.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/unpermute.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "5f0969ff965ac1d5e8a40b7e637adeb726657facc25ead23b2c1b31fe4ee2ab3"},
+    ('decode', 'experts'): {"kernel": "k_decode_fused", "grid": 1384, "dispatches": 25, "fetch_kib": 140213.6, "write_kib": 231.0, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_decode.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/unpermute.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "5f0969ff965ac1d5e8a40b7e637adeb726657facc25ead23b2c1b31fe4ee2ab3"},
+    ('prefill_zipf', 'gate_up'): {"kernel": "k_grouped_gemm_bf16<0, unsigned int>", "grid": 2312, "dispatches": 31, "fetch_kib": 620077.2, "write_kib": 49152.1, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_bf16.hip", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "388072bc0bfe3cf4403ff1fda7838fcc6f7c1628489bfea3c1fdee3664b66d71"},
+    ('prefill_zipf', 'down'): {"kernel": "k_grouped_gemm_bf16_persistent<2, unsigned int>", "grid": 512, "dispatches": 31, "fetch_kib": 282820.8, "write_kib": 131074.3, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_bf16.hip", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "388072bc0bfe3cf4403ff1fda7838fcc6f7c1628489bfea3c1fdee3664b66d71"},
+    ('zero_experts', 'gate_up'): {"kernel": "k_grouped_gemm_bf16<0, unsigned int>", "grid": 5392, "dispatches": 26, "fetch_kib": 1775895.0, "write_kib": 47390.1, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_bf16.hip", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "388072bc0bfe3cf4403ff1fda7838fcc6f7c1628489bfea3c1fdee3664b66d71"},
+    ('zero_experts', 'down'): {"kernel": "k_grouped_gemm_bf16<2, unsigned int>", "grid": 7320, "dispatches": 26, "fetch_kib": 784991.0, "write_kib": 57051.1, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_bf16.hip", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "388072bc0bfe3cf4403ff1fda7838fcc6f7c1628489bfea3c1fdee3664b66d71"},
+    ('fp8_sigmoid', 'gate_up'): {"kernel": "k_grouped_gemm_fp8_stream<0>", "grid": 6160, "dispatches": 6, "fetch_kib": 2417893.0, "write_kib": 36083.3, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_fp8.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "4880c928a54794c85dea8c89df521a19bc135cbc31f9d68406448607fcdce96e"},
+    ('fp8_sigmoid', 'down'): {"kernel": "k_grouped_gemm_fp8_down_persistent", "grid": 256, "dispatches": 26, "fetch_kib": 1211944.4, "write_kib": 229376.0, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_fp8.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "4880c928a54794c85dea8c89df521a19bc135cbc31f9d68406448607fcdce96e"},
+    ('mxfp4_sigmoid', 'gate_up'): {"kernel": "k_grouped_gemm_mxfp4<0, true>", "grid": 6160, "dispatches": 6, "fetch_kib": 1518118.4, "write_kib": 35707.8, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_mxfp4.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "bfd1716498a87e0240a1a00b11aef637c73295b0146ed0916e6684d324128c16"},
+    ('mxfp4_sigmoid', 'down'): {"kernel": "k_grouped_gemm_mxfp4_down_persistent", "grid": 512, "dispatches": 26, "fetch_kib": 648870.7, "write_kib": 251756.3, "fetch_scale": 1.9999, "write_scale": 1.0, "sources": ["mixture_experts_layer_bias_amd/csrc/gemm_mxfp4.hip", "mixture_experts_layer_bias_amd/csrc/dma.h", "mixture_experts_layer_bias_amd/csrc/gemm_common.h", "mixture_experts_layer_bias_amd/csrc/common.h", "mixture_experts_layer_bias_amd/csrc/kernels.h"], "sha256": "bfd1716498a87e0240a1a00b11aef637c73295b0146ed0916e6684d324128c16"},
 }
 
 
