@@ -775,14 +775,17 @@ def test_full_size_matches_oracle(name):
     print(f"max|gpu - oracle| / max|oracle| over all {N} x {wl.hidden} outputs: {err:.3g}", flush=True)
 
 
-@pytest.mark.parametrize("name", ["decode", "many_tiles_300tok", "split_last_round_2048tok"])
+@pytest.mark.parametrize("name", ["decode", "many_tiles_300tok", "split_last_round_2048tok", "fp8_300tok_shared",
+                                  "mxfp4_ragged_sqrtsoftplus_gated"])
 def test_forward_replays_from_a_hip_graph(name):
     """moe_forward captured into a graph: every replay equals the eager result,
     with eager work and synchronisations between replays.  The cases take the
-    one-launch decode path, the sort's one-launch count + scan, and a K split of
-    the last round of tiles: the replays repeat their launches' tags."""
+    one-launch decode path (seq-tagged logits), the two-pass sort, a K split of
+    the last round of tiles (seq-tagged arrival words), the fp8 persistent down
+    kernel and the MXFP4 one with its per-XCD tile counters (which each launch
+    must leave at zero for the next replay)."""
     print(f"\n[case] graph replay {name}", flush=True)
-    wl = SMALL[name]
+    wl = SMALL[name] if name in SMALL else FP8_SMALL[name]
     dl = mi.device.device_layer(wl)
     cfg, w = config_of(wl), weights_of(dl)
     ref, ws = run_forward(cfg, w, dl.x)
