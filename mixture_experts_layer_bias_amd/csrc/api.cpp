@@ -153,7 +153,6 @@ moe_status_t check_config(const moe_config_t* c) {
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // Whether the layer's bf16 tile-kernel launches may split their last round of tiles along K (and so
-// need the `split` piece): bf16 weights, not row-invariant, and launches of at least 2048 routed rows.
 // need the `split` piece): bf16 weights, not row-invariant, no shared expert (whose launches, folded or
 // not, then keep the bits of moe_forward's), launches of at least 2048 routed rows, and a GEMM with K of at
 // least 4096 (H for gate/up, I for down; see with_split).
