@@ -160,6 +160,10 @@ def main():
         "headline": f"{head}: {h['tokens_per_s']:.4g} tokens/s ({h['us_per_layer']:.1f} us/layer)",
         "decode_us_per_layer": entries["decode"]["us_per_layer"] if "decode" in entries else None,
         "roofline": h["roofline"],
+        "after_load": {"us_per_layer": h["us_per_layer_eager_after_load"],
+                       "tokens_per_s": h["config"]["num_tokens"] / (h["us_per_layer_eager_after_load"] * 1e-6),
+                       "note": "the same steps, eager, timed again after the kernel-timing legs (tens of ms of "
+                               "load): outside the clock dip at the onset of sustained load; not the value"},
         "host": host_info(),
         "workloads": entries,
     }
@@ -307,6 +311,17 @@ def measure(name: str, args) -> dict:
         torch.cuda.synchronize()
         k_us[kind] = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
 
+    # ---- the same eager steps timed once more, after the legs above have kept the GPU busy for tens of
+    # milliseconds.  At the onset of sustained load the chip lowers its clocks for some 10-20 ms (every
+    # kernel of the layer, the short latency-bound ones too, runs 10-30% longer), and the first window can
+    # fall inside that dip.  Reported beside `us_per_layer`, never in its place.
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms_after = (time.perf_counter() - t0) * 1e3 / args.steps
+
     # ---- algorithmic bytes and flops (touched experts' weights counted once; h, y intermediates not
     # counted by the one-launch kernel, which never needs them in HBM)
     w_touched = e_t * I * H * (wbytes + sbytes)  # one of the three matrices, all touched experts
@@ -347,6 +362,7 @@ def measure(name: str, args) -> dict:
         "timing": "hip_graph_replay" if use_graph else "eager",
         "us_per_layer_eager": ms_eager * 1e3,
         "us_per_layer_graph": None if ms_graph is None else ms_graph * 1e3,
+        "us_per_layer_eager_after_load": ms_after * 1e3,
         "dtype": wl.weight_dtype,
         "config": {"workload": wl.name, "num_tokens": N, "hidden": H, "num_experts": E, "router_width": R,
                    "top_k": K, "inter": I, "shared_inter": Is, "scoring": wl.scoring,
